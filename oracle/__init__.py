@@ -1,0 +1,176 @@
+"""CPU oracle of the hash-aware top-k decode step (HATA) -- test infrastructure.
+
+Only the tests, the smoke check and the bench's CPU-baseline leg may import
+this package.  It never imports, loads or calls the GPU path, and the GPU
+path never imports it.  The arithmetic lives in plain C (hata_oracle.c,
+double precision, one step per function); this file builds and loads that
+library and composes its steps for one (batch, KV head) unit, following the
+decode workflow of the HATA review ("What carries the argument"): encode the
+query heads, score every cached key by summed Hamming distance, keep the k
+lowest, attend over them.
+
+Threads: large calls are split into row ranges run on a thread pool; ctypes
+releases the GIL, and each range runs the unchanged C step.
+
+Parity status of each function (what pins it) is documented in the tests
+under tests/test_oracle_*.py.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hata_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+D = 128
+R = 128
+
+
+def build(force: bool = True) -> str:
+    """Compile hata_oracle.c with gcc (no FMA contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
+                               "-fno-fast-math", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.oracle_encode.argtypes = [vp, i64, i64, ci, vp, ci, vp]
+        L.oracle_encode.restype = None
+        L.oracle_hamming.argtypes = [vp, ci, vp, i64, ci, vp]
+        L.oracle_hamming.restype = None
+        L.oracle_select.argtypes = [vp, i64, i64, vp]
+        L.oracle_select.restype = i64
+        L.oracle_attend.argtypes = [vp, ci, vp, vp, i64, ci, vp, i64, vp]
+        L.oracle_attend.restype = ci
+        _lib = L
+    return _lib
+
+
+def _nthreads(n_rows: int, per_row_cost: int) -> int:
+    if n_rows * per_row_cost < (1 << 22):
+        return 1
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _ranges(n: int, parts: int):
+    step = (n + parts - 1) // parts
+    return [(s, min(n, s + step)) for s in range(0, n, step)] if n else []
+
+
+def encode(x: np.ndarray, w: np.ndarray, threads: int | None = None) -> np.ndarray:
+    """Sign codes of bf16 rows x [n][d] under W_H w [d][r] (fp32): u32 [n][r/32]."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, d = x.shape
+    assert w.shape[0] == d and w.shape[1] % 32 == 0
+    r = w.shape[1]
+    codes = np.zeros((n, r // 32), dtype=np.uint32)
+    L = lib()
+    nt = threads or _nthreads(n, d * r)
+
+    def run(rng):
+        a, b = rng
+        if b > a:
+            L.oracle_encode(x[a:].ctypes.data, b - a, d, d, w.ctypes.data, r,
+                            codes[a:].ctypes.data)
+
+    parts = _ranges(n, nt * 4) if nt > 1 else [(0, n)]
+    if nt > 1:
+        with ThreadPoolExecutor(nt) as ex:
+            list(ex.map(run, parts))
+    else:
+        for p in parts:
+            run(p)
+    return codes
+
+
+def hamming(qcodes: np.ndarray, kcodes: np.ndarray, threads: int | None = None) -> np.ndarray:
+    """Summed Hamming scores of every key code against the G query codes: int32 [n]."""
+    qcodes = np.ascontiguousarray(qcodes, dtype=np.uint32)
+    kcodes = np.ascontiguousarray(kcodes, dtype=np.uint32)
+    G, words = qcodes.shape
+    n = kcodes.shape[0]
+    assert kcodes.shape[1] == words
+    r = words * 32
+    out = np.zeros(n, dtype=np.int32)
+    L = lib()
+    nt = threads or _nthreads(n, G * r)
+
+    def run(rng):
+        a, b = rng
+        if b > a:
+            L.oracle_hamming(qcodes.ctypes.data, G, kcodes[a:].ctypes.data, b - a, r,
+                             out[a:].ctypes.data)
+
+    parts = _ranges(n, nt * 4) if nt > 1 else [(0, n)]
+    if nt > 1:
+        with ThreadPoolExecutor(nt) as ex:
+            list(ex.map(run, parts))
+    else:
+        for p in parts:
+            run(p)
+    return out
+
+
+def select(scores: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k_eff = min(k, n) lowest (score, index) pairs, ascending index."""
+    scores = np.ascontiguousarray(scores, dtype=np.int32)
+    n = scores.shape[0]
+    idx = np.zeros(max(min(int(k), n), 0), dtype=np.int64)
+    m = lib().oracle_select(scores.ctypes.data, n, int(k), idx.ctypes.data)
+    if m < 0:
+        raise MemoryError("oracle_select")
+    return idx[:m]
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Exact softmax attention of q [G][d] (bf16) over rows idx of K, V [n][d] (bf16):
+    double [G][d]."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    K = np.ascontiguousarray(K, dtype=np.uint16)
+    V = np.ascontiguousarray(V, dtype=np.uint16)
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    G, d = q.shape
+    assert K.shape[1] == d and V.shape == K.shape
+    if idx.size:
+        assert idx.min() >= 0 and idx.max() < K.shape[0]
+    out = np.zeros((G, d), dtype=np.float64)
+    rc = lib().oracle_attend(q.ctypes.data, G, K.ctypes.data, V.ctypes.data, d, d,
+                             idx.ctypes.data, idx.size, out.ctypes.data)
+    if rc != 0:
+        raise MemoryError("oracle_attend")
+    return out
+
+
+def decode_unit(q_group: np.ndarray, w: np.ndarray, K: np.ndarray, V: np.ndarray, k: int,
+                kcodes: np.ndarray | None = None, threads: int | None = None) -> dict:
+    """One decode step of one (batch, KV head) unit.
+
+    q_group: bf16 [G][d], the group's query heads; w: fp32 [d][r], the KV
+    head's W_H; K, V: bf16 [n][d], the whole context (including the token
+    the step appended); k: token budget.  kcodes: the cached key codes if
+    already known (they are a pure function of K and w).
+    """
+    qcodes = encode(q_group, w, threads=1)
+    if kcodes is None:
+        kcodes = encode(K, w, threads=threads)
+    scores = hamming(qcodes, kcodes, threads=threads)
+    idx = select(scores, k)
+    out = attend(q_group, K, V, idx)
+    return {"qcodes": qcodes, "kcodes": kcodes, "scores": scores, "idx": idx, "out": out}
