@@ -1,0 +1,223 @@
+"""Decode-step benchmark of hashed top-k attention on one MI355X.
+
+Workload: the long-context decode configuration -- batch 4, 32 query / 8 KV
+heads (GQA 4:1), head_dim 128, context 131072, top-k 2048 (1.56 %), r = 128
+bits, 0.1 % planted aligned keys, seed 0 (synthetic inputs from synth/).
+
+One step = one attention layer's decode step: hata_append (one new token per
+sequence: K/V row copy + its code) followed by hata_decode_attn (query codes,
+Hamming scan, top-k select, gather + softmax attention).  Steps cycle over
+LAYERS independent layer caches (same contents, distinct memory), as a model
+visits its layers, so the 256 MB last-level cache cannot hold the scanned
+codes between two visits of the same layer.
+
+Prints one JSON line.  value = decode steps per second on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+HBM_PEAK_GBS = 8000.0
+LAYERS = 8
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=2)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(B, Hq, Hkv, n_ctx, k):
+    """Bytes the method must move for one decode step: every cached code
+    (16 B per key per KV head), the selected K and V rows (512 B per
+    selected key per KV head), W_H, q and the output, plus the append (one
+    K and V row and one code per sequence and KV head)."""
+    return (16 * B * Hkv * n_ctx + 512 * B * Hkv * k + 4 * Hkv * 128 * 128 +
+            2 * 2 * B * Hq * 128 + B * Hkv * (512 + 16))
+
+
+def cpu_baseline(spec, reps):
+    """The CPU oracle's decode step (query codes, bit-by-bit Hamming over the
+    cached key codes, sort-based top-k, double-precision attention) on every
+    (batch, KV head) unit of the same workload, units spread over a thread
+    pool.  Key codes come from the oracle's own encoder (untimed prefill)."""
+    import numpy as np
+    import oracle
+    import synth
+    q = synth.gen_q(spec)
+    w = synth.gen_w(spec)
+    new = synth.gen_new_token(spec)
+    cores = max(1, min(16, os.cpu_count() or 1))
+    units = [(b, kv) for b in range(spec.B) for kv in range(spec.Hkv)]
+    ctx = {}
+
+    def prep(u):
+        b, kv = u
+        K, V = synth.unit_context(spec, b, kv, q, new)
+        kc = oracle.encode(K, w[kv], threads=1)
+        ctx[u] = (K, V, kc)
+
+    with ThreadPoolExecutor(cores) as ex:
+        list(ex.map(prep, units))
+    G = spec.G
+
+    def decode(u):
+        b, kv = u
+        K, V, kc = ctx[u]
+        oracle.decode_unit(q[b, kv * G:(kv + 1) * G], w[kv], K, V, spec.topk[b], kcodes=kc,
+                           threads=1)
+
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(cores) as ex:
+            list(ex.map(decode, units))
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": 1.0 / t, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"full decode step (all {len(units)} (batch, KV head) units, context "
+                      f"{spec.lengths[0]}, top-k {spec.topk[0]}), median of {reps} runs; "
+                      f"{cores} threads over units"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path "
+              "has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import hash_top_sparse_encode_amd as hata
+    import synth
+    from workload import GpuWorkload
+
+    dev = torch.device("cuda:0")
+    spec = synth.config(3)
+    B, Hq, Hkv, N, K = spec.B, spec.Hq, spec.Hkv, spec.lengths[0], spec.topk[0]
+    L = max(1, args.layers)
+    per_layer = math.ceil((args.warmup + 2 * args.steps) / L) + 2
+    print(f"[bench] generating {spec.name}", file=sys.stderr, flush=True)
+    base = GpuWorkload(spec, dev, extra_ctx=per_layer)
+    torch.cuda.synchronize()
+    print("[bench] prefill encoded; replicating layers", file=sys.stderr, flush=True)
+
+    class Layer:
+        pass
+
+    layers = []
+    for i in range(L):
+        ly = Layer()
+        if i == 0:
+            ly.cache = base.cache
+            ly.ws = base.ws
+        else:
+            ly.cache = hata.HataCache(B, Hq, Hkv, base.max_ctx, device=dev,
+                                      k=base.cache.k.clone(), v=base.cache.v.clone(),
+                                      codes=base.cache.codes.clone(),
+                                      seq_len=base.cache.seq_len.clone())
+            ly.ws = hata.alloc_workspace(ly.cache, base.k_max)
+        ly.out = torch.empty_like(base.out)
+        layers.append(ly)
+    for ly in layers:
+        ly.cache.seq_len.copy_(base.n_pre)
+    torch.cuda.synchronize()
+
+    def step(s):
+        ly = layers[s % L]
+        hata.hata_append(ly.cache, base.k_new, base.v_new, base.ones, 1, base.w)
+        hata.hata_decode_attn(ly.cache, base.q, base.w, base.topk, base.k_max, ly.out, ly.ws)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ctx0 = int(layers[args.warmup % L].cache.seq_len[0].item()) + 1
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(args.warmup + s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    ms_per_step = wall * 1e3 / args.steps
+    steps_per_s = args.steps / wall
+
+    # Second pass with HIP events around the decode call (same stream) for the
+    # kernel-level roofline figure.
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for s in range(args.steps):
+        ly = layers[(args.warmup + args.steps + s) % L]
+        hata.hata_append(ly.cache, base.k_new, base.v_new, base.ones, 1, base.w)
+        evs[s][0].record(stream)
+        hata.hata_decode_attn(ly.cache, base.q, base.w, base.topk, base.k_max, ly.out, ly.ws)
+        evs[s][1].record(stream)
+    torch.cuda.synchronize()
+    dec_ms = statistics.mean(a.elapsed_time(b) for a, b in evs)
+    status = [ly.cache.status() for ly in layers]
+    if any(status):
+        print(f"[bench] device status flags set: {status}", file=sys.stderr)
+        sys.exit(1)
+
+    n_ctx = ctx0 + (args.steps // L) / 2.0  # mean context over the timed steps
+    step_bytes = algorithmic_bytes(B, Hq, Hkv, n_ctx, K)
+    dec_bytes = step_bytes - B * Hkv * (512 + 16)
+    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "decode steps/sec & HBM GB/s fraction, hashed top-k attn @128K ctx, 1 GPU",
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 K/V/q/out, fp32 W_H and accumulation, u32 codes",
+        "data": "synthetic (seeded SplitMix64/Box-Muller; N(0,1) K/V/q, N(0,1/128) W_H, "
+                "0.1% planted aligned keys)",
+        "config": {
+            "workload": "hashed top-k decode step: B=4, Hq=32, Hkv=8, d=128, r=128, "
+                        f"context {N} (+{args.steps // L} appended), top-k {K}, "
+                        f"{L} layer caches visited in turn",
+            "tokens_per_s": steps_per_s * B,
+            "us_per_step": ms_per_step * 1e3,
+            "step_alg_bytes": step_bytes,
+            "step_hbm_frac": step_bytes * steps_per_s / (HBM_PEAK_GBS * 1e9),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "hata_decode_attn (query encode, Hamming scan, select + gather-attention)",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "launch_us": dec_ms * 1e3,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(spec, args.cpu_reps)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,242 @@
+"""Python binding of libhata.so (include/hata.h): hash-aware top-k decode
+attention on MI355X (gfx950).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and streams.  The
+binding raises if the shared library is missing (build it with
+``python -m hash_top_sparse_encode_amd._build`` or ``__graft_entry__.build()``);
+there is no fallback of any kind.
+
+Names mirror the C ABI:
+  hata_encode_keys, hata_append, hata_decode_workspace_bytes,
+  hata_decode_attn, hata_status_string
+plus ``HataCache``, a holder of the caller-owned cache tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhata.so")
+
+HEAD_DIM = 128
+N_BITS = 128
+CODE_WORDS = 4
+CTRL_WORDS = 64
+
+HATA_OK = 0
+HATA_ERR_INVALID_ARG = 1
+HATA_ERR_UNSUPPORTED = 2
+HATA_ERR_WORKSPACE = 3
+HATA_ERR_HIP = 4
+
+HATA_DEV_APPEND_OVERFLOW = 0x1
+HATA_DEV_BAD_LENGTH = 0x2
+HATA_DEV_TOPK_CLAMPED = 0x4
+HATA_DEV_BAD_NEW = 0x8
+
+EXPORTED_SYMBOLS = ("hata_encode_keys", "hata_append", "hata_decode_workspace_bytes",
+                    "hata_decode_attn", "hata_status_string")
+
+
+class _CCache(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("codes", ctypes.c_void_p),
+        ("seq_len", ctypes.c_void_p),
+        ("ctrl", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("n_bits", ctypes.c_int32),
+        ("max_ctx", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhata.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it first "
+                              "(python -m hash_top_sparse_encode_amd._build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        L.hata_encode_keys.argtypes = [vp, i64, i32, i64, i64, vp, vp, vp]
+        L.hata_encode_keys.restype = ctypes.c_int
+        L.hata_append.argtypes = [ctypes.POINTER(_CCache), vp, vp, vp, i32, vp, vp]
+        L.hata_append.restype = ctypes.c_int
+        L.hata_decode_workspace_bytes.argtypes = [ctypes.POINTER(_CCache), i32]
+        L.hata_decode_workspace_bytes.restype = sz
+        L.hata_decode_attn.argtypes = [ctypes.POINTER(_CCache), vp, vp, vp, i32, vp, vp, sz, vp,
+                                       vp, vp]
+        L.hata_decode_attn.restype = ctypes.c_int
+        L.hata_status_string.argtypes = [ctypes.c_int]
+        L.hata_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+class HataError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {hata_status_string(status)} (status {status})")
+        self.status = status
+
+
+def hata_status_string(status: int) -> str:
+    return lib().hata_status_string(int(status)).decode()
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != HATA_OK:
+        raise HataError(fn, status)
+
+
+def _need(t: torch.Tensor, name: str, dtype, numel: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, has {t.numel()}")
+
+
+class HataCache:
+    """Caller-owned cache tensors of include/hata.h's hata_cache.
+
+    k, v   : bf16 [batch][n_kv_heads][max_ctx][128]
+    codes  : int32 (u32 bit patterns) [batch][n_kv_heads][max_ctx][4]
+    seq_len: int32 [batch]
+    ctrl   : int32 [64], zero at creation
+    """
+
+    def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, max_ctx: int,
+                 device="cuda", k=None, v=None, codes=None, seq_len=None, ctrl=None):
+        self.batch, self.n_q_heads, self.n_kv_heads, self.max_ctx = (
+            int(batch), int(n_q_heads), int(n_kv_heads), int(max_ctx))
+        shape = (self.batch, self.n_kv_heads, self.max_ctx, HEAD_DIM)
+        self.k = k if k is not None else torch.empty(shape, dtype=torch.bfloat16, device=device)
+        self.v = v if v is not None else torch.empty(shape, dtype=torch.bfloat16, device=device)
+        self.codes = codes if codes is not None else torch.zeros(
+            shape[:3] + (CODE_WORDS,), dtype=torch.int32, device=device)
+        self.seq_len = seq_len if seq_len is not None else torch.zeros(
+            self.batch, dtype=torch.int32, device=device)
+        self.ctrl = ctrl if ctrl is not None else torch.zeros(CTRL_WORDS, dtype=torch.int32,
+                                                              device=device)
+        _need(self.k, "k", torch.bfloat16, self.batch * self.n_kv_heads * self.max_ctx * HEAD_DIM)
+        _need(self.v, "v", torch.bfloat16, self.k.numel())
+        _need(self.codes, "codes", torch.int32, self.batch * self.n_kv_heads * self.max_ctx * 4)
+        _need(self.seq_len, "seq_len", torch.int32, self.batch)
+        _need(self.ctrl, "ctrl", torch.int32, CTRL_WORDS)
+
+    def c_struct(self, head_dim: int = HEAD_DIM, n_bits: int = N_BITS) -> _CCache:
+        return _CCache(self.k.data_ptr(), self.v.data_ptr(), self.codes.data_ptr(),
+                       self.seq_len.data_ptr(), self.ctrl.data_ptr(), self.batch,
+                       self.n_q_heads, self.n_kv_heads, head_dim, n_bits, self.max_ctx)
+
+    def status(self) -> int:
+        """Sticky device status bits (HATA_DEV_*); reads device memory (syncs)."""
+        return int(self.ctrl[0].item())
+
+
+def hata_encode_keys(keys: torch.Tensor, w_h: torch.Tensor, codes_out: torch.Tensor = None,
+                     stream=None) -> torch.Tensor:
+    """Codes of keys [n_rows][n_heads][128] (bf16; the last dim contiguous, the
+    others with any stride) under w_h [n_heads][128][128] (fp32):
+    int32 [n_rows][n_heads][4]."""
+    if keys.dtype != torch.bfloat16 or keys.dim() != 3 or keys.shape[2] != HEAD_DIM:
+        raise ValueError("keys must be bf16 [n_rows][n_heads][128]")
+    if keys.stride(2) != 1:
+        raise ValueError("keys' last dimension must be contiguous")
+    n_rows, n_heads = keys.shape[0], keys.shape[1]
+    _need(w_h, "w_h", torch.float32, n_heads * HEAD_DIM * N_BITS)
+    if codes_out is None:
+        codes_out = torch.empty((n_rows, n_heads, CODE_WORDS), dtype=torch.int32,
+                                device=keys.device)
+    _need(codes_out, "codes_out", torch.int32, n_rows * n_heads * CODE_WORDS)
+    st = lib().hata_encode_keys(keys.data_ptr(), n_rows, n_heads, keys.stride(0),
+                                keys.stride(1), w_h.data_ptr(), codes_out.data_ptr(),
+                                _stream(stream))
+    _check("hata_encode_keys", st)
+    return codes_out
+
+
+def hata_append(cache: HataCache, k_new, v_new, n_new: torch.Tensor, t_max: int,
+                w_h: torch.Tensor, stream=None) -> None:
+    """Append up to t_max tokens per sequence (k_new, v_new bf16
+    [batch][t_max][n_kv_heads][128], or both None to encode rows already in
+    the cache); n_new int32 [batch] on the device."""
+    B, Hkv = cache.batch, cache.n_kv_heads
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new must both be given or both be None")
+    if k_new is not None:
+        _need(k_new, "k_new", torch.bfloat16, B * int(t_max) * Hkv * HEAD_DIM)
+        _need(v_new, "v_new", torch.bfloat16, B * int(t_max) * Hkv * HEAD_DIM)
+    _need(n_new, "n_new", torch.int32, B)
+    _need(w_h, "w_h", torch.float32, Hkv * HEAD_DIM * N_BITS)
+    c = cache.c_struct()
+    st = lib().hata_append(ctypes.byref(c), _ptr(k_new), _ptr(v_new), n_new.data_ptr(),
+                           int(t_max), w_h.data_ptr(), _stream(stream))
+    _check("hata_append", st)
+
+
+def hata_decode_workspace_bytes(cache: HataCache, k_max: int) -> int:
+    c = cache.c_struct()
+    return int(lib().hata_decode_workspace_bytes(ctypes.byref(c), int(k_max)))
+
+
+def alloc_workspace(cache: HataCache, k_max: int) -> torch.Tensor:
+    """A device byte tensor of the required size (torch allocations are 256-byte aligned)."""
+    n = hata_decode_workspace_bytes(cache, k_max)
+    if n == 0:
+        raise ValueError("unsupported cache shape")
+    return torch.empty(n, dtype=torch.uint8, device=cache.k.device)
+
+
+def hata_decode_attn(cache: HataCache, q: torch.Tensor, w_h: torch.Tensor, topk: torch.Tensor,
+                     k_max: int, out: torch.Tensor, workspace: torch.Tensor,
+                     sel_idx_out: torch.Tensor = None, scores_out: torch.Tensor = None,
+                     stream=None) -> torch.Tensor:
+    """One hashed top-k decode step: q bf16 [batch][n_q_heads][128] -> out
+    bf16 [batch][n_q_heads][128].  Optional debug outputs: sel_idx_out int32
+    [batch][n_kv_heads][k_max], scores_out int16 (u16 patterns)
+    [batch][n_kv_heads][max_ctx]."""
+    B, Hq, Hkv = cache.batch, cache.n_q_heads, cache.n_kv_heads
+    _need(q, "q", torch.bfloat16, B * Hq * HEAD_DIM)
+    _need(out, "out", torch.bfloat16, B * Hq * HEAD_DIM)
+    _need(w_h, "w_h", torch.float32, Hkv * HEAD_DIM * N_BITS)
+    _need(topk, "topk", torch.int32, B)
+    _need(workspace, "workspace", torch.uint8)
+    if sel_idx_out is not None:
+        _need(sel_idx_out, "sel_idx_out", torch.int32, B * Hkv * int(k_max))
+    if scores_out is not None:
+        _need(scores_out, "scores_out", torch.int16, B * Hkv * cache.max_ctx)
+    c = cache.c_struct()
+    st = lib().hata_decode_attn(ctypes.byref(c), q.data_ptr(), w_h.data_ptr(), topk.data_ptr(),
+                                int(k_max), out.data_ptr(), workspace.data_ptr(),
+                                workspace.numel(), _ptr(sel_idx_out), _ptr(scores_out),
+                                _stream(stream))
+    _check("hata_decode_attn", st)
+    return out

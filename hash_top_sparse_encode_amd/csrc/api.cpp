@@ -1,0 +1,98 @@
+// Host runtime behind include/hata.h: argument validation, workspace plan,
+// kernel launch sequencing.  Everything is enqueued on the caller's stream;
+// nothing here allocates, synchronises or reads device memory.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/hata.h"
+#include "hata_internal.h"
+
+using namespace hata;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hata_status check_cache(const hata_cache *c) {
+    if (!c) return HATA_ERR_INVALID_ARG;
+    if (c->head_dim != kHeadDim || c->n_bits != kBits) return HATA_ERR_UNSUPPORTED;
+    if (c->batch <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0) return HATA_ERR_INVALID_ARG;
+    if (c->n_q_heads % c->n_kv_heads) return HATA_ERR_UNSUPPORTED;
+    const int G = c->n_q_heads / c->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return HATA_ERR_UNSUPPORTED;
+    if ((int64_t)c->batch * c->n_kv_heads > 65535) return HATA_ERR_UNSUPPORTED;
+    if (c->max_ctx < 0 || c->max_ctx > (int64_t)INT32_MAX - 1) return HATA_ERR_INVALID_ARG;
+    if (!c->k || !c->v || !c->codes || !c->seq_len || !c->ctrl) return HATA_ERR_INVALID_ARG;
+    if (!aligned16(c->k) || !aligned16(c->v) || !aligned16(c->codes)) return HATA_ERR_INVALID_ARG;
+    return HATA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *hata_status_string(hata_status s) {
+    switch (s) {
+        case HATA_OK: return "ok";
+        case HATA_ERR_INVALID_ARG: return "invalid argument";
+        case HATA_ERR_UNSUPPORTED: return "unsupported shape (head_dim and n_bits must be 128, G in {1,2,4,8})";
+        case HATA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case HATA_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+hata_status hata_encode_keys(const uint16_t *keys, int64_t n_rows, int32_t n_heads,
+                             int64_t row_stride, int64_t head_stride, const float *w_h,
+                             uint32_t *codes_out, void *stream) {
+    if (n_rows < 0 || n_heads <= 0 || n_heads > 65535) return HATA_ERR_INVALID_ARG;
+    if (n_rows == 0) return HATA_OK;
+    if (!keys || !w_h || !codes_out) return HATA_ERR_INVALID_ARG;
+    if (row_stride < 0 || head_stride < 0) return HATA_ERR_INVALID_ARG;
+    if (n_heads > 1 && head_stride < kHeadDim && row_stride < kHeadDim) return HATA_ERR_INVALID_ARG;
+    hipError_t e = launch_encode_exact(keys, n_rows, n_heads, row_stride, head_stride, w_h,
+                                       codes_out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
+}
+
+hata_status hata_append(const hata_cache *c, const uint16_t *k_new, const uint16_t *v_new,
+                        const int32_t *n_new, int32_t t_max, const float *w_h, void *stream) {
+    hata_status st = check_cache(c);
+    if (st != HATA_OK) return st;
+    if (t_max < 0 || !n_new || !w_h) return HATA_ERR_INVALID_ARG;
+    if ((k_new == nullptr) != (v_new == nullptr)) return HATA_ERR_INVALID_ARG;
+    if (t_max == 0) return HATA_OK;
+    hipError_t e = launch_append_exact(c->k, c->v, c->codes, c->seq_len, c->ctrl, c->batch,
+                                       c->n_kv_heads, c->max_ctx, k_new, v_new, n_new, t_max,
+                                       w_h, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
+}
+
+size_t hata_decode_workspace_bytes(const hata_cache *c, int32_t k_max) {
+    if (!c || k_max < 0) return 0;
+    if (c->head_dim != kHeadDim || c->n_bits != kBits) return 0;
+    DecodePlan p;
+    if (!make_decode_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, &p)) return 0;
+    return p.total;
+}
+
+hata_status hata_decode_attn(const hata_cache *c, const uint16_t *q, const float *w_h,
+                             const int32_t *topk, int32_t k_max, uint16_t *out,
+                             void *workspace, size_t ws_bytes, int32_t *sel_idx_out,
+                             uint16_t *scores_out, void *stream) {
+    hata_status st = check_cache(c);
+    if (st != HATA_OK) return st;
+    if (!q || !w_h || !topk || !out || k_max < 0) return HATA_ERR_INVALID_ARG;
+    if (!aligned16(q)) return HATA_ERR_INVALID_ARG;
+    DecodePlan p;
+    if (!make_decode_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, &p))
+        return HATA_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return HATA_ERR_WORKSPACE;
+    hipError_t e = launch_decode(p, c->k, c->v, c->codes, c->seq_len, c->ctrl, q, w_h, topk,
+                                 k_max, out, workspace, sel_idx_out, scores_out,
+                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
+}
+
+}  // extern "C"

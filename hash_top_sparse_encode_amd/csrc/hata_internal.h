@@ -1,0 +1,59 @@
+// Internal declarations shared by the host runtime (api.cpp) and the HIP
+// kernel sources.  Not part of the public ABI (that is include/hata.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hata {
+
+constexpr int kHeadDim = 128;
+constexpr int kBits = 128;
+constexpr int kWords = 4;
+
+// ctrl[] word assignment (see hata_cache.ctrl in include/hata.h).
+constexpr int kCtrlStatus = 0;
+constexpr int kCtrlAppendDone = 1;
+constexpr int kCtrlEncodeFix = 2;
+
+// Decode-step plan: how the context is cut into scan chunks and attention
+// splits, and where each buffer sits in the workspace.  A pure function of
+// (batch, heads, max_ctx) so hata_decode_workspace_bytes and
+// hata_decode_attn agree.
+struct DecodePlan {
+    int B = 0, Hq = 0, Hkv = 0, G = 0, NB = 0;
+    int64_t max_ctx = 0;
+    int chunk = 0;       // keys per scan workgroup
+    int n_chunks = 0;    // ceil(max_ctx / chunk)
+    int cps = 0;         // scan chunks per attention split
+    int n_splits = 0;    // ceil(n_chunks / cps)
+    int64_t sstride = 0; // score row stride (elements) in the workspace
+    size_t off_qcodes = 0, off_unit_hist = 0, off_done = 0, off_chunk_hist = 0,
+           off_partials = 0, off_scores = 0, total = 0;
+};
+
+// floats per (unit, split, head) partial: m, l, 2 pad, o[128]
+constexpr int kPartialStride = 4 + kHeadDim;
+
+bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, DecodePlan *p);
+
+// ---- launchers (return hipSuccess or the launch error) ----
+
+hipError_t launch_append_exact(uint16_t *k_cache, uint16_t *v_cache, uint32_t *codes,
+                               int32_t *seq_len, int32_t *ctrl, int B, int Hkv, int64_t max_ctx,
+                               const uint16_t *k_new, const uint16_t *v_new,
+                               const int32_t *n_new, int t_max, const float *w,
+                               hipStream_t s);
+
+hipError_t launch_encode_exact(const uint16_t *keys, int64_t n_rows, int n_heads,
+                               int64_t row_stride, int64_t head_stride, const float *w,
+                               uint32_t *codes, hipStream_t s);
+
+hipError_t launch_decode(const DecodePlan &p, const uint16_t *k_cache, const uint16_t *v_cache,
+                         const uint32_t *codes, const int32_t *seq_len, int32_t *ctrl,
+                         const uint16_t *q, const float *w, const int32_t *topk, int k_max,
+                         uint16_t *out, void *ws, int32_t *sel_idx_out, uint16_t *scores_out,
+                         hipStream_t s);
+
+}  // namespace hata

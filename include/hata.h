@@ -1,0 +1,190 @@
+/*
+ * hata.h -- C ABI of the MI355X (gfx950) hash-aware top-k decode-attention
+ * library (libhata.so).
+ *
+ * The method (HATA: Trainable and Hardware-Efficient Hash-Aware Top-k
+ * Attention, arXiv 2506.02572; review on pith.science, "What carries the
+ * argument" and the Figure 2 caption with Algorithm 1): every cached key
+ * and every query head is encoded to an r = 128-bit sign code
+ * h(x) = sign(x W_H); the key codes are cached beside the KV cache
+ * (rbit/32 = 4 words per key); at decode the query code is XORed against
+ * every cached key code and popcounted into a Hamming score, the k keys of
+ * lowest score are selected, and exact softmax attention runs over only
+ * their K/V rows.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers must point to device memory that the
+ *     caller owns and keeps alive until the stream has finished the call.
+ *     The library never frees or retains them.
+ *   - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL
+ *     is the default stream).  No call allocates memory, synchronises the
+ *     stream or reads device memory on the host, so the calls can be
+ *     captured into a HIP graph.
+ *   - Host-side argument checks return a status code; nothing aborts.  A
+ *     non-OK status means nothing was enqueued.  Conditions only the device
+ *     can see (a cache overflow, an out-of-range length) set bits in the
+ *     cache's status word (HATA_DEV_*) and the affected batch entry is left
+ *     unchanged or clamped as documented below.
+ *   - Supported shapes: head_dim = 128, n_bits = 128, query heads a
+ *     multiple G of KV heads with G in {1, 2, 4, 8}.  Other shapes return
+ *     HATA_ERR_UNSUPPORTED.
+ *   - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *   - Reentrant: the library keeps no mutable global state.  Calls that use
+ *     the same cache or workspace must be ordered by the caller (same
+ *     stream, or events).
+ *
+ * Code convention (a reading the pages leave open): bit j of a code is
+ * [sum_d x_d * W_H[d][j] > 0] with the sum evaluated as a sequential
+ * double-precision sum over d = 0..127 (each product is exact in double),
+ * so a zero sum gives bit 0; bit j is stored in 32-bit word j / 32 at bit
+ * position j % 32.  The GPU result is bit-identical to that definition:
+ * fast products decide every bit whose margin is provably larger than
+ * their error bound, and every other bit is recomputed in that exact order.
+ */
+#ifndef HATA_H
+#define HATA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HATA_HEAD_DIM 128
+#define HATA_N_BITS 128
+#define HATA_CODE_WORDS 4
+
+/* Words of the per-cache control block (see hata_cache.ctrl). */
+#define HATA_CTRL_WORDS 64
+
+typedef enum {
+    HATA_OK = 0,
+    HATA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad stride ... */
+    HATA_ERR_UNSUPPORTED = 2, /* head_dim / n_bits != 128, G not in {1,2,4,8} */
+    HATA_ERR_WORKSPACE = 3,   /* workspace null or smaller than required */
+    HATA_ERR_HIP = 4          /* a HIP launch failed */
+} hata_status;
+
+/* Device status bits, OR-ed into ctrl[0] by kernels (sticky until the
+ * caller clears them). */
+#define HATA_DEV_APPEND_OVERFLOW 0x1 /* seq_len[b] + n_new[b] > max_ctx: entry b not appended */
+#define HATA_DEV_BAD_LENGTH 0x2      /* seq_len[b] outside [0, max_ctx] at decode: clamped */
+#define HATA_DEV_TOPK_CLAMPED 0x4    /* topk[b] > k_max at decode: clamped to k_max */
+#define HATA_DEV_BAD_NEW 0x8         /* n_new[b] < 0 or > t_max at append: entry b skipped */
+
+/*
+ * A key/value cache with its key-code cache, all device memory owned by the
+ * caller.  Sequence b, KV head g, position p:
+ *   k, v  : bf16  [batch][n_kv_heads][max_ctx][128], row (b, g, p) at
+ *           ((b * n_kv_heads + g) * max_ctx + p) * 128
+ *   codes : u32   [batch][n_kv_heads][max_ctx][4]
+ *   seq_len: int32 [batch], the number of valid positions of each sequence;
+ *           positions [0, seq_len[b]) hold keys, values and codes.
+ *   ctrl  : int32 [HATA_CTRL_WORDS], zero-filled by the caller once before
+ *           first use; word 0 is the sticky device status (HATA_DEV_*); the
+ *           other words are library counters that every call leaves at
+ *           zero again.
+ * This is the cache of Algorithm 1 in the Figure 2 caption of the review
+ * (K_cache, V_cache, and the code cache of rbit/32 words per key).
+ */
+typedef struct {
+    uint16_t *k;
+    uint16_t *v;
+    uint32_t *codes;
+    int32_t *seq_len;
+    int32_t *ctrl;
+    int32_t batch;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim; /* must be 128 */
+    int32_t n_bits;   /* must be 128 */
+    int64_t max_ctx;
+} hata_cache;
+
+/*
+ * Sign codes of a batch of key (or query) vectors: HashEncode(K) of
+ * Algorithm 1 (Figure 2 caption of the review), h(x) = sign(x W_H).
+ *   keys      device bf16; element (row n, head h, dim d) at
+ *             keys[n * row_stride + h * head_stride + d] (strides in
+ *             elements, d contiguous).
+ *   n_rows    >= 0 rows; n_heads >= 1 heads, each with its own W_H.
+ *   w_h       device fp32 [n_heads][128 (d)][128 (bit)].
+ *   codes_out device u32 [n_rows][n_heads][4], fully overwritten.
+ * Uses the MFMA encoder (bf16 matrix cores with a two-term split of W_H)
+ * plus an exact recheck of the bits inside the error band.
+ * Errors: HATA_ERR_INVALID_ARG for null pointers (with n_rows > 0),
+ * negative sizes or strides smaller than a row; HATA_ERR_HIP on launch
+ * failure.
+ */
+hata_status hata_encode_keys(const uint16_t *keys, int64_t n_rows, int32_t n_heads,
+                             int64_t row_stride, int64_t head_stride, const float *w_h,
+                             uint32_t *codes_out, void *stream);
+
+/*
+ * Append new tokens to the cache (Algorithm 1's cache fill at prefill; one
+ * token per sequence at decode): for each sequence b and t < n_new[b], key
+ * row t of b goes to position seq_len[b] + t, its code is computed with the
+ * KV head's W_H, and finally seq_len[b] += n_new[b].
+ *   k_new, v_new device bf16 [batch][t_max][n_kv_heads][128] (token-major),
+ *             or both NULL: the rows are already in the cache at
+ *             [seq_len[b], seq_len[b] + n_new[b]) and only their codes are
+ *             computed (encode in place).
+ *   n_new     device int32 [batch], each in [0, t_max].
+ *   t_max     host bound on n_new (sizes the launch); t_max = 0 is a no-op.
+ *   w_h       device fp32 [n_kv_heads][128][128].
+ * Device-detected errors: an entry with seq_len[b] + n_new[b] > max_ctx is
+ * not appended and sets HATA_DEV_APPEND_OVERFLOW; n_new[b] outside
+ * [0, t_max] sets HATA_DEV_BAD_NEW and the entry is skipped.
+ * Host errors: HATA_ERR_INVALID_ARG (null cache fields, exactly one of
+ * k_new / v_new null, t_max < 0), HATA_ERR_UNSUPPORTED (shape).
+ */
+hata_status hata_append(const hata_cache *c, const uint16_t *k_new, const uint16_t *v_new,
+                        const int32_t *n_new, int32_t t_max, const float *w_h, void *stream);
+
+/* Bytes of device workspace hata_decode_attn needs for this cache (depends
+ * on batch, heads and max_ctx only).  Returns 0 for an unsupported or
+ * invalid cache. */
+size_t hata_decode_workspace_bytes(const hata_cache *c, int32_t k_max);
+
+/*
+ * One decode step of hash-aware top-k attention (the decode workflow of
+ * Figure 2 in the review; TopK by Hamming distance as in its Algorithm 3,
+ * referenced in the referee report):
+ *   1. encode each query head with the W_H of its KV head
+ *      (KV head of query head h = h / G);
+ *   2. score every cached key i < seq_len[b] of KV head g by the sum over
+ *      the group's G query heads of popcount(q_code XOR k_code[i])
+ *      (range 0 .. 128 G);
+ *   3. select S = the k_eff = min(topk[b], k_max, seq_len[b]) keys of lowest
+ *      (score, index) -- ties at the cut go to the lowest indices;
+ *   4. for each query head: softmax over i in S of (q . k_i) / sqrt(128),
+ *      output sum_i p_i v_i (fp32 accumulation), stored as bf16.
+ *   q          device bf16 [batch][n_q_heads][128].
+ *   w_h        device fp32 [n_kv_heads][128][128].
+ *   topk       device int32 [batch]; values < 0 count as 0, values above
+ *              k_max are clamped (HATA_DEV_TOPK_CLAMPED).
+ *   k_max      host upper bound of the budget, >= 0.
+ *   out        device bf16 [batch][n_q_heads][128]; zero where k_eff = 0.
+ *   workspace  device, >= hata_decode_workspace_bytes(c, k_max) bytes,
+ *              256-byte aligned; contents need no initialisation.
+ *   sel_idx_out optional device int32 [batch][n_kv_heads][k_max]: the
+ *              selected indices in ascending order, -1 after k_eff.
+ *   scores_out optional device u16 [batch][n_kv_heads][max_ctx]: the
+ *              summed Hamming scores of positions < seq_len[b].
+ * Errors: HATA_ERR_INVALID_ARG, HATA_ERR_UNSUPPORTED, HATA_ERR_WORKSPACE,
+ * HATA_ERR_HIP.
+ */
+hata_status hata_decode_attn(const hata_cache *c, const uint16_t *q, const float *w_h,
+                             const int32_t *topk, int32_t k_max, uint16_t *out,
+                             void *workspace, size_t ws_bytes, int32_t *sel_idx_out,
+                             uint16_t *scores_out, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *hata_status_string(hata_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HATA_H */

@@ -1,0 +1,125 @@
+"""Host-side checks of the C ABI (no GPU needed: only argument validation and
+the workspace plan run, no kernel is launched).
+
+  - libhata.so loads and exports every function include/hata.h declares;
+  - status strings;
+  - every invalid or unsupported argument returns its status code before any
+    launch;
+  - hata_decode_workspace_bytes follows the plan for each configuration.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hash_top_sparse_encode_amd as hata
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hata.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hata_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(hata.EXPORTED_SYMBOLS)
+    L = hata.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    nm = os.popen(f"nm -D --defined-only {hata.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}$", nm, flags=re.M), n
+
+
+def test_status_strings():
+    for s in range(5):
+        assert hata.hata_status_string(s)
+    assert "unknown" in hata.hata_status_string(99)
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def cache(**kw):
+    base = dict(k=FAKE, v=FAKE, codes=FAKE, seq_len=FAKE, ctrl=FAKE, batch=2, n_q_heads=8,
+                n_kv_heads=2, head_dim=128, n_bits=128, max_ctx=1000)
+    base.update(kw)
+    return hata._CCache(**base)
+
+
+def decode(c, q=FAKE, w=FAKE, topk=FAKE, k_max=16, out=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return hata.lib().hata_decode_attn(ctypes.byref(c), q, w, topk, k_max, out, ws, ws_bytes,
+                                       None, None, None)
+
+
+def test_decode_validation():
+    E = hata
+    assert decode(cache(head_dim=64)) == E.HATA_ERR_UNSUPPORTED
+    assert decode(cache(n_bits=64)) == E.HATA_ERR_UNSUPPORTED
+    assert decode(cache(n_q_heads=6)) == E.HATA_ERR_UNSUPPORTED        # 6 % 4? G = 3
+    assert decode(cache(n_q_heads=32)) == E.HATA_ERR_UNSUPPORTED       # G = 16
+    assert decode(cache(n_q_heads=7)) == E.HATA_ERR_UNSUPPORTED        # not a multiple
+    assert decode(cache(batch=0)) == E.HATA_ERR_INVALID_ARG
+    assert decode(cache(max_ctx=-1)) == E.HATA_ERR_INVALID_ARG
+    assert decode(cache(max_ctx=1 << 33)) == E.HATA_ERR_INVALID_ARG
+    assert decode(cache(k=0)) == E.HATA_ERR_INVALID_ARG
+    assert decode(cache(codes=0)) == E.HATA_ERR_INVALID_ARG
+    assert decode(cache(ctrl=0)) == E.HATA_ERR_INVALID_ARG
+    assert decode(cache(k=FAKE + 2)) == E.HATA_ERR_INVALID_ARG         # misaligned
+    assert decode(cache(batch=40000)) == E.HATA_ERR_UNSUPPORTED        # > 65535 units
+    assert decode(cache(), q=0) == E.HATA_ERR_INVALID_ARG
+    assert decode(cache(), q=FAKE + 8) == E.HATA_ERR_INVALID_ARG
+    assert decode(cache(), out=0) == E.HATA_ERR_INVALID_ARG
+    assert decode(cache(), topk=0) == E.HATA_ERR_INVALID_ARG
+    assert decode(cache(), k_max=-1) == E.HATA_ERR_INVALID_ARG
+    assert decode(cache(), ws=0) == E.HATA_ERR_WORKSPACE
+    assert decode(cache(), ws=FAKE + 64) == E.HATA_ERR_WORKSPACE      # not 256-aligned
+    assert decode(cache(), ws_bytes=100) == E.HATA_ERR_WORKSPACE
+    assert hata.lib().hata_decode_attn(None, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 1 << 40, None,
+                                       None, None) == E.HATA_ERR_INVALID_ARG
+
+
+def test_append_validation():
+    L = hata.lib()
+    c = cache()
+
+    def app(c=c, k=FAKE, v=FAKE, n=FAKE, t=4, w=FAKE):
+        return L.hata_append(ctypes.byref(c), k, v, n, t, w, None)
+
+    assert app(k=None) == hata.HATA_ERR_INVALID_ARG      # only one of k_new / v_new
+    assert app(v=None) == hata.HATA_ERR_INVALID_ARG
+    assert app(n=None) == hata.HATA_ERR_INVALID_ARG
+    assert app(w=None) == hata.HATA_ERR_INVALID_ARG
+    assert app(t=-1) == hata.HATA_ERR_INVALID_ARG
+    assert app(c=cache(head_dim=96)) == hata.HATA_ERR_UNSUPPORTED
+    assert app(c=cache(seq_len=0)) == hata.HATA_ERR_INVALID_ARG
+    assert app(t=0) == hata.HATA_OK                       # nothing to append: no launch
+
+
+def test_encode_keys_validation():
+    L = hata.lib()
+    assert L.hata_encode_keys(FAKE, -1, 1, 128, 128, FAKE, FAKE, None) == hata.HATA_ERR_INVALID_ARG
+    assert L.hata_encode_keys(FAKE, 5, 0, 128, 128, FAKE, FAKE, None) == hata.HATA_ERR_INVALID_ARG
+    assert L.hata_encode_keys(None, 5, 1, 128, 128, FAKE, FAKE, None) == hata.HATA_ERR_INVALID_ARG
+    assert L.hata_encode_keys(FAKE, 5, 1, 128, 128, None, FAKE, None) == hata.HATA_ERR_INVALID_ARG
+    assert L.hata_encode_keys(FAKE, 5, 1, 128, 128, FAKE, None, None) == hata.HATA_ERR_INVALID_ARG
+    assert L.hata_encode_keys(FAKE, 5, 1, -128, 128, FAKE, FAKE, None) == hata.HATA_ERR_INVALID_ARG
+    assert L.hata_encode_keys(None, 0, 1, 128, 128, None, None, None) == hata.HATA_OK
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 8, 8, 4096), (8, 32, 8, 32768), (4, 32, 8, 131072),
+                                       (1, 32, 8, 1048576), (64, 32, 8, 65536)])
+def test_workspace_plan(B, Hq, Hkv, N):
+    c = cache(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, max_ctx=N + 8)
+    n = hata.lib().hata_decode_workspace_bytes(ctypes.byref(c), 2048)
+    units = B * Hkv
+    assert n >= units * (N + 8) * 2  # at least the u16 scores
+    assert n < units * (N + 8) * 2 * 1.5 + (1 << 22)
+    assert n % 256 == 0
+    assert hata.lib().hata_decode_workspace_bytes(ctypes.byref(cache(head_dim=64)), 1) == 0
+    assert hata.lib().hata_decode_workspace_bytes(None, 1) == 0

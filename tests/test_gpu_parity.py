@@ -1,0 +1,159 @@
+"""GPU parity of the decode step against the CPU oracle, through the C ABI.
+
+Bars (per unit (batch, KV head) checked):
+  - key codes, query-group Hamming scores and selected indices: bit-exact;
+  - attention outputs: max |gpu - oracle| <= 2e-2 (bf16 output, fp32
+    accumulation; the oracle is exact double precision).
+Small workloads are checked unit by unit in full; the full-size
+configurations are checked on sampled units, with structural properties
+(selection size, ordering, the -1 tail) on every unit.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from workload import GpuWorkload, bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 2e-2
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_unit(spec, wl, b, kv):
+    K, V = synth.unit_context(spec, b, kv, wl.q_host, wl.new_host)
+    G = spec.G
+    return oracle.decode_unit(wl.q_host[b, kv * G:(kv + 1) * G], wl.w_host[kv], K, V,
+                              spec.topk[b])
+
+
+def k_eff_of(spec, b, k_max):
+    return max(0, min(spec.topk[b], k_max, spec.lengths[b]))
+
+
+def check_unit(spec, wl, b, kv, out, sel, sc, ref=None):
+    G = spec.G
+    L = spec.lengths[b]
+    ref = ref if ref is not None else oracle_unit(spec, wl, b, kv)
+    codes = wl.cache.codes[b, kv, :L].cpu().numpy().view(np.uint32)
+    assert np.array_equal(codes, ref["kcodes"]), f"codes differ at unit {(b, kv)}: " \
+        f"{int((codes != ref['kcodes']).any(1).sum())} rows"
+    scores = sc[b, kv, :L].cpu().numpy().view(np.uint16).astype(np.int32)
+    assert np.array_equal(scores, ref["scores"]), f"scores differ at unit {(b, kv)}"
+    ke = k_eff_of(spec, b, wl.k_max)
+    s = sel[b, kv].cpu().numpy()
+    assert np.array_equal(s[:ke], ref["idx"]), f"selection differs at unit {(b, kv)}"
+    assert np.all(s[ke:] == -1)
+    o = out[b, kv * G:(kv + 1) * G].float().cpu().numpy().astype(np.float64)
+    err = np.abs(o - ref["out"]).max()
+    assert err <= OUT_TOL, f"output error {err} at unit {(b, kv)}"
+    return err
+
+
+def check_structure(spec, wl, sel):
+    s = sel.cpu().numpy()
+    for b in range(spec.B):
+        ke = k_eff_of(spec, b, wl.k_max)
+        for kv in range(spec.Hkv):
+            row = s[b, kv]
+            assert np.all(row[ke:] == -1)
+            head = row[:ke]
+            assert np.all(np.diff(head) > 0) and (ke == 0 or (head[0] >= 0 and head[-1] < spec.lengths[b]))
+
+
+def run_spec(spec, device, units=None, extra_ctx=3):
+    _say(f"[parity] {spec.name}: generating + prefill")
+    wl = GpuWorkload(spec, device, extra_ctx=extra_ctx)
+    out, sel, sc = wl.step(debug=True)
+    torch.cuda.synchronize()
+    assert wl.cache.status() == 0
+    assert wl.cache.seq_len.cpu().tolist() == list(spec.lengths)
+    check_structure(spec, wl, sel)
+    if units is None:
+        units = [(b, kv) for b in range(spec.B) for kv in range(spec.Hkv)]
+    errs = []
+    for (b, kv) in units:
+        _say(f"[parity] {spec.name}: oracle unit {(b, kv)} len {spec.lengths[b]}")
+        errs.append(check_unit(spec, wl, b, kv, out, sel, sc))
+    _say(f"[parity] {spec.name}: max out err {max(errs):.3e}")
+    return wl, out, sel, sc
+
+
+def test_config1_all_units(gpu):
+    run_spec(synth.config(1), gpu)
+
+
+FUZZ = [
+    synth.custom("g1 len1 dense", 2, 3, 3, [1, 5000], [4, 5000], [0, 4]),
+    synth.custom("g2 ragged k>len k=0", 3, 4, 2, [1030, 2049, 777], [16, 2054, 0], [2, 2, 1]),
+    synth.custom("g4 ragged", 2, 8, 2, [9000, 3100], [140, 48], [9, 3]),
+    synth.custom("g8", 1, 16, 2, [6000], [93], [6]),
+    synth.custom("g4 tiny", 3, 4, 1, [2, 3, 64], [1, 3, 5], [1, 1, 1]),
+]
+
+
+@pytest.mark.parametrize("spec", FUZZ, ids=[s.name for s in FUZZ])
+def test_fuzz_all_units(gpu, spec):
+    run_spec(spec, gpu)
+
+
+def test_many_units_dense_and_sparse(gpu):
+    # 512 units, so each unit has a single split of up to 3000 keys; half the
+    # sequences select everything (dense), which overflows the LDS index
+    # list and exercises its flush.
+    B = 32
+    lens = synth.ragged_lengths(11, B, 1500, 3000)
+    topk = [n if b % 2 == 0 else max(16, n // 64) for b, n in enumerate(lens)]
+    spec = synth.custom("many units", B, 16, 16, lens, topk, [3] * B, seed=11)
+    run_spec(spec, gpu, units=[(0, 0), (0, 15), (1, 3), (30, 7), (31, 0)])
+
+
+def test_determinism(gpu):
+    spec = synth.custom("det", 2, 8, 2, [20000, 7000], [300, 100], [20, 7], seed=5)
+    wl = GpuWorkload(spec, gpu, extra_ctx=1)
+    out1, sel1, sc1 = wl.step(debug=True)
+    out1, sel1, sc1 = out1.clone(), sel1.clone(), sc1.clone()
+    for _ in range(3):
+        wl.decode()
+        o2 = wl.out.clone()
+        assert torch.equal(bf16_bits_t(o2), bf16_bits_t(out1))
+    sel2 = torch.full_like(sel1, -7)
+    sc2 = torch.zeros_like(sc1)
+    wl.decode(sel_idx_out=sel2, scores_out=sc2)
+    assert torch.equal(sel1, sel2) and torch.equal(sc1, sc2)
+    assert torch.equal(bf16_bits_t(wl.out), bf16_bits_t(out1))
+
+
+def bf16_bits_t(t):
+    return t.view(torch.int16)
+
+
+@pytest.mark.parametrize("cfg,units", [
+    (2, [(0, 0), (7, 7), (3, 4)]),
+    (3, [(0, 0), (3, 7), (2, 5)]),
+])
+def test_full_config_sampled(gpu, cfg, units):
+    run_spec(synth.config(cfg), gpu, units=units)
+
+
+def test_config4_sampled(gpu):
+    run_spec(synth.config(4), gpu, units=[(0, 0), (0, 5)])
+
+
+def test_config5_sampled(gpu):
+    spec = synth.config(5)
+    lens = spec.lengths
+    bmax = int(np.argmax(lens))
+    bmin = int(np.argmin(lens))
+    run_spec(spec, gpu, units=[(bmax, 0), (bmin, 7), (17, 3)])
