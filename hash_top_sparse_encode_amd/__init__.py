@@ -25,7 +25,12 @@ LIB_PATH = os.path.join(_PKG, "libhata.so")
 HEAD_DIM = 128
 N_BITS = 128
 CODE_WORDS = 4
-CTRL_WORDS = 64
+
+
+def ctrl_words(batch: int, n_kv_heads: int) -> int:
+    """int32 words of a cache's control block (HATA_CTRL_WORDS)."""
+    return 16 + 64 * (int(batch) * int(n_kv_heads) + int(batch))
+
 
 HATA_OK = 0
 HATA_ERR_INVALID_ARG = 1
@@ -37,9 +42,10 @@ HATA_DEV_APPEND_OVERFLOW = 0x1
 HATA_DEV_BAD_LENGTH = 0x2
 HATA_DEV_TOPK_CLAMPED = 0x4
 HATA_DEV_BAD_NEW = 0x8
+HATA_DEV_STALL = 0x10
 
 EXPORTED_SYMBOLS = ("hata_encode_keys", "hata_append", "hata_decode_workspace_bytes",
-                    "hata_decode_attn", "hata_status_string")
+                    "hata_decode_attn", "hata_decode_step", "hata_status_string")
 
 
 class _CCache(ctypes.Structure):
@@ -79,6 +85,9 @@ def lib() -> ctypes.CDLL:
         L.hata_decode_attn.argtypes = [ctypes.POINTER(_CCache), vp, vp, vp, i32, vp, vp, sz, vp,
                                        vp, vp]
         L.hata_decode_attn.restype = ctypes.c_int
+        L.hata_decode_step.argtypes = [ctypes.POINTER(_CCache), vp, vp, vp, vp, vp, i32, vp, vp,
+                                       sz, vp, vp, vp]
+        L.hata_decode_step.restype = ctypes.c_int
         L.hata_status_string.argtypes = [ctypes.c_int]
         L.hata_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -129,7 +138,7 @@ class HataCache:
     k, v   : bf16 [batch][n_kv_heads][max_ctx][128]
     codes  : int32 (u32 bit patterns) [batch][n_kv_heads][max_ctx][4]
     seq_len: int32 [batch]
-    ctrl   : int32 [64], zero at creation
+    ctrl   : int32 [ctrl_words(batch, n_kv_heads)], zero at creation
     """
 
     def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, max_ctx: int,
@@ -143,13 +152,13 @@ class HataCache:
             shape[:3] + (CODE_WORDS,), dtype=torch.int32, device=device)
         self.seq_len = seq_len if seq_len is not None else torch.zeros(
             self.batch, dtype=torch.int32, device=device)
-        self.ctrl = ctrl if ctrl is not None else torch.zeros(CTRL_WORDS, dtype=torch.int32,
-                                                              device=device)
+        self.ctrl = ctrl if ctrl is not None else torch.zeros(
+            ctrl_words(self.batch, self.n_kv_heads), dtype=torch.int32, device=device)
         _need(self.k, "k", torch.bfloat16, self.batch * self.n_kv_heads * self.max_ctx * HEAD_DIM)
         _need(self.v, "v", torch.bfloat16, self.k.numel())
         _need(self.codes, "codes", torch.int32, self.batch * self.n_kv_heads * self.max_ctx * 4)
         _need(self.seq_len, "seq_len", torch.int32, self.batch)
-        _need(self.ctrl, "ctrl", torch.int32, CTRL_WORDS)
+        _need(self.ctrl, "ctrl", torch.int32, ctrl_words(self.batch, self.n_kv_heads))
 
     def c_struct(self, head_dim: int = HEAD_DIM, n_bits: int = N_BITS) -> _CCache:
         return _CCache(self.k.data_ptr(), self.v.data_ptr(), self.codes.data_ptr(),
@@ -239,4 +248,31 @@ def hata_decode_attn(cache: HataCache, q: torch.Tensor, w_h: torch.Tensor, topk:
                                 workspace.numel(), _ptr(sel_idx_out), _ptr(scores_out),
                                 _stream(stream))
     _check("hata_decode_attn", st)
+    return out
+
+
+def hata_decode_step(cache: HataCache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                     w_h: torch.Tensor, topk: torch.Tensor, k_max: int, out: torch.Tensor,
+                     workspace: torch.Tensor, sel_idx_out: torch.Tensor = None,
+                     scores_out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """Append one token per sequence (k_new, v_new bf16 [batch][n_kv_heads][128])
+    and decode over the grown context, in one kernel launch."""
+    B, Hq, Hkv = cache.batch, cache.n_q_heads, cache.n_kv_heads
+    _need(k_new, "k_new", torch.bfloat16, B * Hkv * HEAD_DIM)
+    _need(v_new, "v_new", torch.bfloat16, B * Hkv * HEAD_DIM)
+    _need(q, "q", torch.bfloat16, B * Hq * HEAD_DIM)
+    _need(out, "out", torch.bfloat16, B * Hq * HEAD_DIM)
+    _need(w_h, "w_h", torch.float32, Hkv * HEAD_DIM * N_BITS)
+    _need(topk, "topk", torch.int32, B)
+    _need(workspace, "workspace", torch.uint8)
+    if sel_idx_out is not None:
+        _need(sel_idx_out, "sel_idx_out", torch.int32, B * Hkv * int(k_max))
+    if scores_out is not None:
+        _need(scores_out, "scores_out", torch.int16, B * Hkv * cache.max_ctx)
+    c = cache.c_struct()
+    st = lib().hata_decode_step(ctypes.byref(c), k_new.data_ptr(), v_new.data_ptr(),
+                                q.data_ptr(), w_h.data_ptr(), topk.data_ptr(), int(k_max),
+                                out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                _ptr(sel_idx_out), _ptr(scores_out), _stream(stream))
+    _check("hata_decode_step", st)
     return out

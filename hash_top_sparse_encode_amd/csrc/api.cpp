@@ -76,10 +76,11 @@ size_t hata_decode_workspace_bytes(const hata_cache *c, int32_t k_max) {
     return p.total;
 }
 
-hata_status hata_decode_attn(const hata_cache *c, const uint16_t *q, const float *w_h,
-                             const int32_t *topk, int32_t k_max, uint16_t *out,
-                             void *workspace, size_t ws_bytes, int32_t *sel_idx_out,
-                             uint16_t *scores_out, void *stream) {
+static hata_status decode_common(const hata_cache *c, const uint16_t *k_new,
+                                 const uint16_t *v_new, const uint16_t *q, const float *w_h,
+                                 const int32_t *topk, int32_t k_max, uint16_t *out,
+                                 void *workspace, size_t ws_bytes, int32_t *sel_idx_out,
+                                 uint16_t *scores_out, void *stream) {
     hata_status st = check_cache(c);
     if (st != HATA_OK) return st;
     if (!q || !w_h || !topk || !out || k_max < 0) return HATA_ERR_INVALID_ARG;
@@ -89,10 +90,27 @@ hata_status hata_decode_attn(const hata_cache *c, const uint16_t *q, const float
         return HATA_ERR_UNSUPPORTED;
     if (!workspace || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return HATA_ERR_WORKSPACE;
-    hipError_t e = launch_decode(p, c->k, c->v, c->codes, c->seq_len, c->ctrl, q, w_h, topk,
-                                 k_max, out, workspace, sel_idx_out, scores_out,
+    hipError_t e = launch_decode(p, c->k, c->v, c->codes, c->seq_len, c->ctrl, k_new, v_new, q,
+                                 w_h, topk, k_max, out, workspace, sel_idx_out, scores_out,
                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
+}
+
+hata_status hata_decode_attn(const hata_cache *c, const uint16_t *q, const float *w_h,
+                             const int32_t *topk, int32_t k_max, uint16_t *out,
+                             void *workspace, size_t ws_bytes, int32_t *sel_idx_out,
+                             uint16_t *scores_out, void *stream) {
+    return decode_common(c, nullptr, nullptr, q, w_h, topk, k_max, out, workspace, ws_bytes,
+                         sel_idx_out, scores_out, stream);
+}
+
+hata_status hata_decode_step(const hata_cache *c, const uint16_t *k_new, const uint16_t *v_new,
+                             const uint16_t *q, const float *w_h, const int32_t *topk,
+                             int32_t k_max, uint16_t *out, void *workspace, size_t ws_bytes,
+                             int32_t *sel_idx_out, uint16_t *scores_out, void *stream) {
+    if (!k_new || !v_new) return HATA_ERR_INVALID_ARG;
+    return decode_common(c, k_new, v_new, q, w_h, topk, k_max, out, workspace, ws_bytes,
+                         sel_idx_out, scores_out, stream);
 }
 
 }  // extern "C"

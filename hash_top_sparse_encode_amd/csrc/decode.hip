@@ -1,74 +1,394 @@
-// Decode step of hash-aware top-k attention on gfx950 (HATA review,
-// "What carries the argument": query code XOR every cached key code,
-// popcount into a Hamming score, top-k, attention over the selected K/V;
-// TopK by Hamming distance per Algorithm 3 as discussed in the referee
+// Decode step of hash-aware top-k attention on gfx950, as one kernel launch
+// (HATA review, "What carries the argument": query code XOR every cached key
+// code, popcount into a Hamming score, top-k, attention over the selected
+// K/V; TopK by Hamming distance per the Algorithm 3 discussed in the referee
 // report, major comment 1).
 //
-// Three kernels, all on the caller's stream:
-//   k_qenc          one workgroup per (batch, KV head): exact sign codes of
-//                   the group's G query heads; clears the unit's histogram
-//                   and merge counter for this call.
-//   k_scan          one workgroup per (scan chunk, unit): 16-byte code loads,
-//                   G x (XOR + popcount) against the query codes held in
-//                   scalar registers, u16 score store, LDS histogram of the
-//                   0..128G score range; writes the chunk's cumulative
-//                   histogram and adds its counts into the unit histogram.
-//   k_select_attend one workgroup per (attention split, unit): finds the cut
-//                   score T and the tie quota from the unit histogram, the
-//                   ties already taken by earlier chunks from their
-//                   cumulative histograms, re-reads its u16 scores, compacts
-//                   the selected indices in index order into LDS, gathers
-//                   their bf16 K/V rows (16 lanes per row, 16 bytes per
-//                   lane) with an online softmax per 16-lane group, and
-//                   writes one (m, l, o) partial per query head.  The last
-//                   split of a unit to finish merges the partials in split
-//                   order and stores the bf16 output.
+// Work items, one per workgroup, in block-index order:
+//   PRO(u,p)   per unit u = (batch b, KV head g), four parts of 32 code
+//              bits each: exact codes of the G query heads and of the step's
+//              appended token; part 0 also appends the K/V row and clears
+//              the unit histogram.
+//   SCAN(u,c)  chunk c of up to 8192 keys, in passes of 4096: 16-byte code
+//              loads issued before anything else, G x (XOR + popcount) against query codes held in scalar
+//              registers, scores stored four to a 64-bit word, per-wave LDS
+//              histograms of the 0..128G range, the chunk's cumulative
+//              histogram, its counts added into the unit histogram.
+//              The last chunk of a unit to finish derives the selection plan
+//              from the unit and chunk histograms: the cut
+//              score T, the quota of score-T keys, and per split the score-T
+//              and below-T counts of the chunks before it.
+//   SEL(u,s)   split s (a run of chunks): reads its plan entries, re-reads
+//              its scores (four rounds prefetched),
+//              compact the selected indices in index order into LDS, gather
+//              bf16 K/V rows (32 lanes x 8 bytes per row, 8 rows per lane
+//              group in flight) with an online softmax; one (m, l, o)
+//              partial per query head.  The last split of a unit merges the
+//              partials in split order into the bf16 output.
+// The item order is PRO for every unit, then SCAN items unit by unit, then
+// SEL items unit by unit (the order also allows SEL items of unit u right
+// after the SCAN items of unit u + lag).
+//
+// Ordering: an item waits only for items of its own unit with smaller block
+// indices (SCAN on PRO, SEL on all SCANs).  Workgroups of a grid are started
+// in block order within each XCD, and a finished workgroup frees its slot, so
+// the smallest unfinished index can always start.  Every wait also gives up
+// after a bound (HATA_DEV_STALL), so the kernel always terminates.
+//
+// Coherence across the eight XCDs without cache flushes: every value one
+// workgroup produces for another (query codes, the appended row and code,
+// histograms, scores, partials, counters) is written with a device-scope
+// relaxed atomic store (write-through, "sc1") or atomic add, the producer
+// waits for its stores to complete (s_waitcnt) before bumping a counter, and
+// the consumer reads those values with device-scope atomic loads ("sc1"),
+// which are served by the device-coherent level.  An agent-scope fence would
+// write back / invalidate whole L2s instead, which costs more than the step.
 #include "device_util.h"
 #include "hata_internal.h"
 #include "../../include/hata.h"
 
 namespace hata {
 
-constexpr int kListCap = 4096;  // selected indices buffered in LDS
-constexpr int kSelBlock = 2048; // keys examined per selection round (256 x 8)
+constexpr int kThreads = 256;
+constexpr int kMaxChunk = 8192;    // keys per scan item
+constexpr int kScanPass = 4096;    // keys per pass: 16 per thread, 4 runs of 4 consecutive keys
+constexpr int kSelRound = 2048;    // 8 scores per thread per selection round
+constexpr int kListCap = 4096;     // selected indices buffered in LDS
+constexpr int kSpinLimit = 1 << 21;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint16_t kNoScore = 0xFFFF;
+
+typedef float fvec4 __attribute__((ext_vector_type(4)));
+
+// PRO work per unit is split over this many workgroups (32 code bits each)
+constexpr int kProParts = 4;
+
+// per-unit counter words
+constexpr int kPro = 0, kScan = 1, kAttn = 2, kFin = 3, kPlan = 4;
+constexpr int kUnitWords = 64;  // one 256-byte line per unit (and per batch entry)
+
+struct FusedArgs {
+    uint16_t *k_cache;
+    uint16_t *v_cache;
+    uint32_t *codes;
+    int32_t *seq_len;
+    int32_t *ctrl;
+    const uint16_t *k_new;  // [B][Hkv][128] or null (no append)
+    const uint16_t *v_new;
+    const uint16_t *q;
+    const float *w;
+    const int32_t *topk;
+    uint16_t *out;
+    int32_t *sel_out;        // optional debug output
+    uint16_t *scores_dbg;    // optional debug output, row stride max_ctx
+    uint16_t *scores;        // workspace, row stride sstride
+    uint32_t *qcodes;
+    uint32_t *unit_hist;
+    uint32_t *chunk_hist;
+    int32_t *sel_plan;       // per unit: T, quota, then (ties, below) before each split
+    float *part_ml;
+    float *part_o;
+    int64_t max_ctx;
+    int64_t sstride;
+    int B, Hkv, k_max;
+    int chunk, n_chunks, cps, n_splits, lag;
+    int n_items;
+};
+
+// ---------------------------------------------------------------- coherent access
+
+__device__ __forceinline__ void st_dev(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int32_t *p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(float *p, float v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_dev(const int32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p),
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ int add_dev(int32_t *p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until this thread's memory operations have completed.
+__device__ __forceinline__ void drain_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// ---------------------------------------------------------------- small helpers
 
 __device__ __forceinline__ int64_t clamp_len(int64_t v, int64_t hi) {
     return v < 0 ? 0 : (v > hi ? hi : v);
 }
 
-// ------------------------------------------------------------------ qenc
-// grid: B * Hkv; block: 128 (thread j = code bit j for every head of the group)
-template <int G>
-__global__ __launch_bounds__(128) void k_qenc(const uint16_t *__restrict__ q,
-                                              const float *__restrict__ w, int Hkv, int NB,
-                                              uint32_t *__restrict__ qcodes,
-                                              uint32_t *__restrict__ unit_hist,
-                                              uint32_t *__restrict__ done) {
-    __shared__ float xq[G][kHeadDim];
-    const int unit = blockIdx.x, b = unit / Hkv, kv = unit % Hkv, Hq = Hkv * G;
-    const int j = threadIdx.x;
-    float wv[kHeadDim];
-    load_wcol(w + (int64_t)kv * kHeadDim * kBits + j, wv);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-        xq[h][j] = bf16_to_f32(q[((int64_t)b * Hq + kv * G + h) * kHeadDim + j]);
-    for (int i = j; i < NB; i += 128) unit_hist[(int64_t)unit * NB + i] = 0u;
-    if (j == 0) done[unit] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const bool bit = exact_sign(xq[h], wv);
-        const uint64_t m = __ballot(bit);
-        if ((j & 63) == 0) {
-            uint32_t *dst = qcodes + ((int64_t)b * Hq + kv * G + h) * kWords + (j >> 6) * 2;
-            dst[0] = (uint32_t)m;
-            dst[1] = (uint32_t)(m >> 32);
-        }
-    }
+// Context of batch entry b for this step.  seq_len is only rewritten once
+// every item of the entry has finished, so all items see the same l0.
+struct StepLen {
+    int64_t l0;   // length before the append
+    int64_t len;  // length this step attends over
+    bool app;     // the step's token is appended at l0
+};
+
+__device__ __forceinline__ StepLen step_len(const FusedArgs &a, int b) {
+    StepLen s;
+    s.l0 = clamp_len(a.seq_len[b], a.max_ctx);
+    s.app = a.k_new != nullptr && s.l0 + 1 <= a.max_ctx;
+    s.len = s.l0 + (s.app ? 1 : 0);
+    return s;
 }
 
-// ------------------------------------------------------------------ scan
+__device__ __forceinline__ int64_t step_keff(const FusedArgs &a, int b, int64_t len) {
+    int64_t k = a.topk[b];
+    if (k < 0) k = 0;
+    if (k > a.k_max) k = a.k_max;
+    return k < len ? k : len;
+}
+
+__device__ __forceinline__ int32_t *unit_ctr(const FusedArgs &a, int u, int which) {
+    return a.ctrl + kCtrlUnitBase + kUnitWords * u + which;
+}
+__device__ __forceinline__ int32_t *batch_ctr(const FusedArgs &a, int b) {
+    return a.ctrl + kCtrlUnitBase + kUnitWords * (a.B * a.Hkv + b);
+}
+
+// Thread 0 polls until *p >= target; the workgroup continues together.
+__device__ __forceinline__ void wg_wait_geq(const FusedArgs &a, int32_t *p, int target) {
+    if (threadIdx.x == 0) {
+        int spins = 0;
+        while (ld_dev(p) < target) {
+            // back off: about 0.03, 0.2, then 0.9 microseconds between polls
+            if (spins < 8) __builtin_amdgcn_s_sleep(1);
+            else if (spins < 24) __builtin_amdgcn_s_sleep(8);
+            else __builtin_amdgcn_s_sleep(32);
+            if (++spins > kSpinLimit) {
+                atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_STALL);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Every thread's device-scope stores complete, then thread 0 counts.
+// Returns the counter's previous value (in thread 0).
+__device__ __forceinline__ int wg_signal(int32_t *p) {
+    drain_memory();
+    __syncthreads();
+    int prev = 0;
+    if (threadIdx.x == 0) prev = add_dev(p, 1);
+    return prev;
+}
+
+__device__ __forceinline__ void unpack_bf16x4(uint64_t r, float (&f)[4]) {
+    const uint32_t lo = (uint32_t)r, hi = (uint32_t)(r >> 32);
+    f[0] = __uint_as_float(lo << 16);
+    f[1] = __uint_as_float(lo & 0xFFFF0000u);
+    f[2] = __uint_as_float(hi << 16);
+    f[3] = __uint_as_float(hi & 0xFFFF0000u);
+}
+
+// ---------------------------------------------------------------- shared memory
+
+template <int G>
+struct SmemScan {
+    static constexpr int NB = G * kBits + 1;
+    uint32_t hist[4][NB];
+    int scan[4];
+    int last, T, below;
+};
+
+template <int G>
+struct SmemSel {
+    int list[kListCap];
+    float4 q[G][kHeadDim / 4];  // pre-scaled query heads
+    float wm[4][G];
+    float wl[4][G];
+    float wo[4][G][kHeadDim];
+    float mw[64][G];  // merge: per-split weights
+    float ml[G];
+    int scan[8];
+    long long red[4];
+    int T, below, last;
+};
+
+template <int G>
+struct SmemPro {
+    float x[G + 1][kHeadDim];                   // query heads, then the appended key or zeros
+    float w[kHeadDim][kBits / kProParts];       // this part's 32 columns of W_H
+    double py[4][G + 1][kBits / kProParts];     // per-wave partial sums
+    double pa[4][G + 1][kBits / kProParts];     // per-wave partial sums of |products|
+};
+
+template <int G>
+union Smem {
+    SmemScan<G> scan;
+    SmemSel<G> sel;
+    SmemPro<G> pro;
+};
+
+// ---------------------------------------------------------------- PRO(u)
+
+// Part p of unit u computes code bits [32 p, 32 p + 32) of the G query heads
+// and of the appended key; part 0 also copies the appended K/V rows, clears
+// the unit histogram and writes the outputs of an empty selection.
+//
+// Each bit is sign(y) with y = sum_t x[t] W[t][j] evaluated as a sequential
+// double sum in ascending t (bf16 x fp32 products are exact in double).
+// Fast path: sixteen-row segments summed sequentially, then combined in a
+// fixed tree -- at most 18 roundings deep -- alongside A = sum |x[t] W[t][j]|.
+// Both the tree and the sequential sum lie within gamma_127 A and gamma_18 A
+// of the exact sum (Higham, Accuracy and Stability of Numerical Algorithms,
+// ch. 4), so when |y_tree| > 2^-45 A both have the exact sum's sign.  Any
+// other bit (including non-finite inputs) is recomputed sequentially.
+template <int G>
+__device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Smem<G> &sm) {
+    constexpr int NB = G * kBits + 1;
+    constexpr int COLS = kBits / kProParts;  // 32
+    constexpr int NV = G + 1;                // query heads + appended key
+    const int b = u / a.Hkv, kv = u % a.Hkv, Hq = a.Hkv * G;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    // This part's 128 x 32 slice of W_H, 16 bytes per load, before anything else.
+    fvec4 wq[kHeadDim * COLS / 4 / kThreads];  // 4
+    {
+        const float *wk = a.w + (int64_t)kv * kHeadDim * kBits + part * COLS;
+#pragma unroll
+        for (int r = 0; r < kHeadDim * COLS / 4 / kThreads; ++r) {
+            const int f = r * kThreads + t;  // row f / 8, four columns at 4 (f % 8)
+            wq[r] = *reinterpret_cast<const fvec4 *>(wk + (f >> 3) * kBits + 4 * (f & 7));
+        }
+    }
+    const int64_t raw = a.seq_len[b];
+    const StepLen sl = step_len(a, b);
+    const int nvec = G + (sl.app ? 1 : 0);
+    // x rows (query heads, then the appended key or zeros): one 16-byte load
+    // per thread, 16 threads per row
+    if (t < NV * 16) {
+        const int v = t >> 4, d0 = (t & 15) * 8;
+        uint4 r = make_uint4(0, 0, 0, 0);
+        if (v < G) r = *reinterpret_cast<const uint4 *>(a.q + ((int64_t)b * Hq + kv * G + v) * kHeadDim + d0);
+        else if (sl.app) r = *reinterpret_cast<const uint4 *>(a.k_new + ((int64_t)b * a.Hkv + kv) * kHeadDim + d0);
+        const uint32_t wds[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sm.pro.x[v][d0 + 2 * e] = __uint_as_float(wds[e] << 16);
+            sm.pro.x[v][d0 + 2 * e + 1] = __uint_as_float(wds[e] & 0xFFFF0000u);
+        }
+    }
+    if (part == 0) {
+        if (kv == 0 && t == 0) {
+            int flags = 0;
+            if (raw < 0 || raw > a.max_ctx) flags |= HATA_DEV_BAD_LENGTH;
+            if (a.k_new != nullptr && !sl.app) flags |= HATA_DEV_APPEND_OVERFLOW;
+            if (a.topk[b] > a.k_max) flags |= HATA_DEV_TOPK_CLAMPED;
+            if (flags) atomicOr(&a.ctrl[kCtrlStatus], flags);
+        }
+        if (sl.app && t < 64) {
+            // the new K and V rows: 32 + 32 eight-byte words
+            const int64_t row = (int64_t)u * a.max_ctx + sl.l0;
+            const int64_t src = ((int64_t)b * a.Hkv + kv) * kHeadDim;
+            if (t < 32) {
+                st_dev(reinterpret_cast<uint64_t *>(a.k_cache + row * kHeadDim) + t,
+                       reinterpret_cast<const uint64_t *>(a.k_new + src)[t]);
+            } else {
+                st_dev(reinterpret_cast<uint64_t *>(a.v_cache + row * kHeadDim) + (t - 32),
+                       reinterpret_cast<const uint64_t *>(a.v_new + src)[t - 32]);
+            }
+        }
+        for (int i = t; i < NB; i += kThreads) st_dev(a.unit_hist + (int64_t)u * NB + i, 0u);
+        const int64_t k_eff = step_keff(a, b, sl.len);
+        if (a.sel_out) {
+            int32_t *su = a.sel_out + (int64_t)u * a.k_max;
+            for (int64_t p = k_eff + t; p < a.k_max; p += kThreads) su[p] = -1;
+        }
+        if (k_eff == 0) {
+            for (int i = t; i < G * kHeadDim; i += kThreads)
+                a.out[((int64_t)b * Hq + kv * G) * kHeadDim + i] = 0;
+        }
+    }
+    fvec4 *wl = reinterpret_cast<fvec4 *>(&sm.pro.w[0][0]);
+#pragma unroll
+    for (int r = 0; r < kHeadDim * COLS / 4 / kThreads; ++r) wl[r * kThreads + t] = wq[r];
+    __syncthreads();
+    // Segment sums: lane col = lane & 31 of wave w covers rows
+    // [16 seg, 16 seg + 16) with seg = 2 w + (lane >> 5).
+    {
+        const int col = lane & 31, seg = 2 * wv + (lane >> 5);
+        double ys[NV], as[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            ys[v] = 0.0;
+            as[v] = 0.0;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 16 * seg + r;
+            const double wd = (double)sm.pro.w[row][col];
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const double pr = (double)sm.pro.x[v][row] * wd;  // exact
+                ys[v] += pr;
+                as[v] += fabs(pr);
+            }
+        }
+        // pair the wave's two segments, then park the wave's partials
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const double yo = __shfl_xor(ys[v], 32, 64), ao = __shfl_xor(as[v], 32, 64);
+            if (lane < 32) {
+                sm.pro.py[wv][v][col] = ys[v] + yo;  // lower segment first
+                sm.pro.pa[wv][v][col] = as[v] + ao;
+            }
+        }
+    }
+    __syncthreads();
+    // Decide bit (v, col) for v = t >> 5 (and v = 8 + (t >> 5) on a second
+    // pass for G = 8): tree over the four waves, then the sign test.
+#pragma unroll
+    for (int pass = 0; pass < (NV + 7) / 8; ++pass) {
+        const int v = pass * 8 + (t >> 5), col = t & 31;
+        bool bit = false;
+        if (v < NV) {
+            const double y = (sm.pro.py[0][v][col] + sm.pro.py[1][v][col]) +
+                             (sm.pro.py[2][v][col] + sm.pro.py[3][v][col]);
+            const double A = ((sm.pro.pa[0][v][col] + sm.pro.pa[1][v][col]) +
+                              (sm.pro.pa[2][v][col] + sm.pro.pa[3][v][col])) * (1.0 + 0x1p-40);
+            if (fabs(y) > 0x1p-45 * A) {
+                bit = y > 0.0;
+            } else {
+                double ysq = 0.0;  // the defining sequential sum
+                for (int row = 0; row < kHeadDim; ++row)
+                    ysq = fma((double)sm.pro.x[v][row], (double)sm.pro.w[row][col], ysq);
+                bit = ysq > 0.0;
+            }
+        }
+        const uint64_t mb = __ballot(bit);
+        if ((t & 31) == 0 && v < nvec) {
+            const uint32_t word = (uint32_t)(((t >> 5) & 1) ? (mb >> 32) : mb);
+            if (v < G) st_dev(a.qcodes + ((int64_t)b * Hq + kv * G + v) * kWords + part, word);
+            else st_dev(a.codes + ((int64_t)u * a.max_ctx + sl.l0) * kWords + part, word);
+        }
+    }
+    if (sl.len > 0) wg_signal(unit_ctr(a, u, kPro));
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------- SCAN(u, c)
+
 template <int G>
 __device__ __forceinline__ int group_hamming(const uint4 &k, const uint32_t (&qc)[G][4]) {
     int s = 0;
@@ -79,72 +399,186 @@ __device__ __forceinline__ int group_hamming(const uint4 &k, const uint32_t (&qc
     return s;
 }
 
-// grid: (n_chunks, units); block 256
 template <int G>
-__global__ __launch_bounds__(256) void k_scan(const uint32_t *__restrict__ codes,
-                                              const int32_t *__restrict__ seq_len,
-                                              const uint32_t *__restrict__ qcodes,
-                                              int64_t max_ctx, int Hkv, int chunk, int n_chunks,
-                                              uint16_t *__restrict__ scores, int64_t sstride,
-                                              uint16_t *__restrict__ chunk_hist,
-                                              uint32_t *__restrict__ unit_hist) {
+__device__ __forceinline__ void item_scan(const FusedArgs &a, int u, int c, Smem<G> &sm) {
     constexpr int NB = G * kBits + 1;
-    constexpr int PER = (NB + 255) / 256;
-    __shared__ uint32_t hist[NB];
-    __shared__ int scan_tmp[4];
-    const int c = blockIdx.x, unit = blockIdx.y, b = unit / Hkv, kv = unit % Hkv;
-    const int64_t len = clamp_len(seq_len[b], max_ctx);
-    const int64_t c0 = (int64_t)c * chunk;
-    if (c0 >= len) return;
-    const int64_t c1 = c0 + chunk < len ? c0 + chunk : len;
-    for (int i = threadIdx.x; i < NB; i += 256) hist[i] = 0u;
-    uint32_t qc[G][4];
-    const uint32_t *qsrc = qcodes + ((int64_t)b * Hkv * G + kv * G) * kWords;
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) qc[h][t] = qsrc[h * 4 + t];
+    constexpr int PER = (NB + kThreads - 1) / kThreads;
+    constexpr int RUNS = kScanPass / (4 * kThreads);  // runs of 4 keys per thread and pass
+    const int b = u / a.Hkv, kv = u % a.Hkv;
+    const int t = threadIdx.x, wv = t >> 6;
+    const StepLen sl = step_len(a, b);
+    const int64_t c0 = (int64_t)c * a.chunk;
+    if (c0 >= sl.len) return;
+    const int64_t c1 = c0 + a.chunk < sl.len ? c0 + a.chunk : sl.len;
+    // While the unit's PRO parts are still running, give their W_H loads about
+    // a microsecond's head start before this chunk's loads join the queues.
+    if (t == 0 && ld_dev(unit_ctr(a, u, kPro)) < kProParts) {
+        __builtin_amdgcn_s_sleep(20);  // 20 x 64 cycles each
+        __builtin_amdgcn_s_sleep(20);
+    }
+    for (int i = t; i < 4 * NB; i += kThreads) (&sm.scan.hist[0][0])[i] = 0u;
     __syncthreads();
-    const uint4 *kc = reinterpret_cast<const uint4 *>(codes) + (int64_t)unit * max_ctx;
-    uint16_t *sc = scores + (int64_t)unit * sstride;
-    for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) {
-        const int s = group_hamming<G>(kc[i], qc);
-        sc[i] = (uint16_t)s;
-        atomicAdd(&hist[s], 1u);
+    const uint4 *kc = reinterpret_cast<const uint4 *>(a.codes) + (int64_t)u * a.max_ctx;
+    uint16_t *sc = a.scores + (int64_t)u * a.sstride;
+    uint16_t *sd = a.scores_dbg ? a.scores_dbg + (int64_t)u * a.max_ctx : nullptr;
+    uint32_t *wh = sm.scan.hist[wv];
+    uint32_t qc[G][4];
+    // The chunk in passes of kScanPass keys; each pass issues all its code
+    // loads before using any.  Only the appended code (written by PRO in this
+    // launch) is re-read after the wait for PRO.
+    for (int64_t p0 = c0; p0 < c1; p0 += kScanPass) {
+        uint4 kr[RUNS][4];
+#pragma unroll
+        for (int r = 0; r < RUNS; ++r) {
+            const int64_t i0 = p0 + (int64_t)r * 4 * kThreads + 4 * t;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                kr[r][e] = (i0 + e < c1) ? kc[i0 + e] : make_uint4(0, 0, 0, 0);
+        }
+        if (p0 == c0) {
+            wg_wait_geq(a, unit_ctr(a, u, kPro), kProParts);
+            const uint32_t *qsrc = a.qcodes + ((int64_t)b * a.Hkv * G + kv * G) * kWords;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const uint64_t lo = ld_dev(reinterpret_cast<const uint64_t *>(qsrc + h * 4));
+                const uint64_t hi = ld_dev(reinterpret_cast<const uint64_t *>(qsrc + h * 4 + 2));
+                qc[h][0] = __builtin_amdgcn_readfirstlane((uint32_t)lo);
+                qc[h][1] = __builtin_amdgcn_readfirstlane((uint32_t)(lo >> 32));
+                qc[h][2] = __builtin_amdgcn_readfirstlane((uint32_t)hi);
+                qc[h][3] = __builtin_amdgcn_readfirstlane((uint32_t)(hi >> 32));
+            }
+        }
+        const int64_t p1 = p0 + kScanPass < c1 ? p0 + kScanPass : c1;
+        if (sl.app && sl.l0 >= p0 && sl.l0 < p1) {
+            const int64_t off = sl.l0 - p0;
+            const int r = (int)(off / (4 * kThreads)), tt = (int)((off % (4 * kThreads)) / 4);
+            if (t == tt) {
+                const uint64_t *p = reinterpret_cast<const uint64_t *>(kc + sl.l0);
+                const uint64_t lo = ld_dev(p), hi = ld_dev(p + 1);
+                const uint4 v = make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
+                                           (uint32_t)(hi >> 32));
+#pragma unroll
+                for (int rr = 0; rr < RUNS; ++rr)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (rr == r && e == (int)(off % 4)) kr[rr][e] = v;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RUNS; ++r) {
+            const int64_t i0 = p0 + (int64_t)r * 4 * kThreads + 4 * t;
+            uint32_t s4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s4[e] = kNoScore;
+                if (i0 + e < c1) {
+                    const int s = group_hamming<G>(kr[r][e], qc);
+                    s4[e] = (uint32_t)s;
+                    atomicAdd(&wh[s], 1u);
+                    if (sd) sd[i0 + e] = (uint16_t)s;
+                }
+            }
+            if (i0 < c1)
+                st_dev(reinterpret_cast<uint64_t *>(sc + i0),
+                       (uint64_t)s4[0] | ((uint64_t)s4[1] << 16) | ((uint64_t)s4[2] << 32) |
+                           ((uint64_t)s4[3] << 48));
+        }
     }
     __syncthreads();
-    // cumulative histogram of the chunk, and its counts into the unit's
     uint32_t loc[PER];
     int tsum = 0;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        const int bin = threadIdx.x * PER + e;
-        loc[e] = bin < NB ? hist[bin] : 0u;
-        tsum += (int)loc[e];
+        const int bin = t * PER + e;
+        uint32_t v = 0;
+        if (bin < NB) v = sm.scan.hist[0][bin] + sm.scan.hist[1][bin] + sm.scan.hist[2][bin] +
+                          sm.scan.hist[3][bin];
+        loc[e] = v;
+        tsum += (int)v;
     }
     int tot;
-    int run = block_excl_scan_256(tsum, scan_tmp, &tot);
-    uint16_t *ch = chunk_hist + ((int64_t)unit * n_chunks + c) * NB;
-    uint32_t *uh = unit_hist + (int64_t)unit * NB;
+    int run = block_excl_scan_256(tsum, sm.scan.scan, &tot);
+    uint32_t *ch = a.chunk_hist + ((int64_t)u * a.n_chunks + c) * NB;
+    int32_t *uh = reinterpret_cast<int32_t *>(a.unit_hist) + (int64_t)u * NB;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        const int bin = threadIdx.x * PER + e;
+        const int bin = t * PER + e;
         if (bin < NB) {
             run += (int)loc[e];
-            ch[bin] = (uint16_t)run;
-            if (loc[e]) atomicAdd(&uh[bin], loc[e]);
+            st_dev(ch + bin, (uint32_t)run);
+            if (loc[e]) add_dev(uh + bin, (int)loc[e]);
         }
     }
+    const int prev = wg_signal(unit_ctr(a, u, kScan));
+    if (t == 0) sm.scan.last = prev;
+    __syncthreads();
+    const int n_chunks_u = (int)((sl.len + a.chunk - 1) / a.chunk);
+    if (sm.scan.last != n_chunks_u - 1) return;
+    // The last chunk of the unit to finish turns the histograms into the
+    // selection plan: the cut score T (first bin whose cumulative count
+    // reaches k_eff), the quota of score-T keys to take, and for each split
+    // the number of score-T and below-T keys in the chunks before it.
+    const int64_t k_eff = step_keff(a, b, sl.len);
+    if (k_eff > 0) {
+        int32_t *plan = a.sel_plan + (int64_t)u * (2 + 2 * a.n_splits);
+        // T = first bin whose cumulative unit count reaches k_eff (the counts
+        // sum to the unit length, so one exists); below = count before T.
+        const uint32_t *uhr = a.unit_hist + (int64_t)u * NB;
+        int tsum2 = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int bin = t * PER + e;
+            loc[e] = bin < NB ? ld_dev(uhr + bin) : 0u;
+            tsum2 += (int)loc[e];
+        }
+        if (t == 0) {
+            sm.scan.T = NB - 1;
+            sm.scan.below = 0;
+        }
+        int tot2;
+        int run2 = block_excl_scan_256(tsum2, sm.scan.scan, &tot2);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int nxt = run2 + (int)loc[e];
+            if ((int64_t)run2 < k_eff && (int64_t)nxt >= k_eff) {
+                sm.scan.T = t * PER + e;
+                sm.scan.below = run2;
+            }
+            run2 = nxt;
+        }
+        __syncthreads();
+        const int T = sm.scan.T;
+        int ties_run = 0, below_run = 0;
+        for (int cb = 0; cb < n_chunks_u; cb += kThreads) {
+            const int cc = cb + t;
+            int tie = 0, lo = 0;
+            if (cc < n_chunks_u) {
+                const uint32_t *chc = a.chunk_hist + ((int64_t)u * a.n_chunks + cc) * NB;
+                lo = T > 0 ? (int)ld_dev(chc + T - 1) : 0;
+                tie = (int)ld_dev(chc + T) - lo;
+            }
+            int tie_all, lo_all;
+            const int tie_pre = block_excl_scan_256(tie, sm.scan.scan, &tie_all);
+            const int lo_pre = block_excl_scan_256(lo, sm.scan.scan, &lo_all);
+            if (cc < n_chunks_u && cc % a.cps == 0) {
+                const int sidx = cc / a.cps;
+                st_dev(plan + 2 + 2 * sidx, ties_run + tie_pre);
+                st_dev(plan + 3 + 2 * sidx, below_run + lo_pre);
+            }
+            ties_run += tie_all;
+            below_run += lo_all;
+        }
+        if (t == 0) {
+            st_dev(plan + 0, T);
+            st_dev(plan + 1, (int32_t)(k_eff - sm.scan.below));
+        }
+    }
+    wg_signal(unit_ctr(a, u, kPlan));
+    __syncthreads();
 }
 
-// ------------------------------------------------------------------ select + attend
+// ---------------------------------------------------------------- SEL(u, s)
 
-struct SoftmaxState {
-    float m, l;
-};
-
-// Merge (m2, l2, o2) into (m, l, o): the log-sum-exp combination of two
-// partial softmax sums in base 2.
 __device__ __forceinline__ void lse_weights(float m1, float m2, float *M, float *a1, float *a2) {
     const float mm = fmaxf(m1, m2);
     *M = mm;
@@ -152,226 +586,210 @@ __device__ __forceinline__ void lse_weights(float m1, float m2, float *M, float 
     *a2 = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mm);
 }
 
-__device__ __forceinline__ void unpack_bf16x8(const uint4 &r, float (&f)[8]) {
-    f[0] = __uint_as_float(r.x << 16);
-    f[1] = __uint_as_float(r.x & 0xFFFF0000u);
-    f[2] = __uint_as_float(r.y << 16);
-    f[3] = __uint_as_float(r.y & 0xFFFF0000u);
-    f[4] = __uint_as_float(r.z << 16);
-    f[5] = __uint_as_float(r.z & 0xFFFF0000u);
-    f[6] = __uint_as_float(r.w << 16);
-    f[7] = __uint_as_float(r.w & 0xFFFF0000u);
+// Sum over the 32 lanes of a group (two 16-lane rows), every lane gets the
+// total: xor-1 and xor-2 quad permutes, half-row and row mirrors, then the
+// other row.
+__device__ __forceinline__ float group32_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    v += __shfl_xor(v, 16, 32);
+    return v;
 }
 
-template <int G>
-__device__ __forceinline__ void attend_one(const uint4 &kr, const uint4 &vr,
-                                           const float (&qs)[G][8], float (&m)[G], float (&l)[G],
-                                           float (&o)[G][8]) {
-    float kf[8], vf[8];
-    unpack_bf16x8(kr, kf);
-    unpack_bf16x8(vr, vf);
+__device__ __forceinline__ uint64_t load_row8(const uint16_t *row, int l32, bool coherent) {
+    const uint64_t *p = reinterpret_cast<const uint64_t *>(row) + l32;
+    return coherent ? ld_dev(p) : *p;
+}
+
+// Fold KS already-loaded rows (kr, vr entries [X0, X0 + KS)) into the online
+// softmax state; entries at or past n are padding.
+template <int G, int KL, int KS, int X0>
+__device__ __forceinline__ void attend_block(const uint64_t (&kr)[KL], const uint64_t (&vr)[KL], int j0,
+                                             int n, int l32, const float4 (*qs)[kHeadDim / 4],
+                                             float (&m)[G], float (&l)[G], float (&o)[G][4]) {
+    float z[KS][G];
+#pragma unroll
+    for (int x = 0; x < KS; ++x) {
+        float kf[4];
+        unpack_bf16x4(kr[X0 + x], kf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float4 q = qs[h][l32];
+            float d = q.x * kf[0];
+            d = fmaf(q.y, kf[1], d);
+            d = fmaf(q.z, kf[2], d);
+            z[x][h] = fmaf(q.w, kf[3], d);
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < KS; ++x)
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+            z[x][h] = (j0 + 8 * (X0 + x) < n) ? group32_sum(z[x][h]) : -INFINITY;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        float d = 0.f;
+        float mx = z[0][h];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(qs[h][e], kf[e], d);
-        d += __shfl_xor(d, 1, 16);
-        d += __shfl_xor(d, 2, 16);
-        d += __shfl_xor(d, 4, 16);
-        d += __shfl_xor(d, 8, 16);
-        const float mn = fmaxf(m[h], d);
-        const float a = exp2f(m[h] - mn);
-        const float p = exp2f(d - mn);
-        l[h] = fmaf(l[h], a, p);
+        for (int x = 1; x < KS; ++x) mx = fmaxf(mx, z[x][h]);
+        const float mn = fmaxf(m[h], mx);
+        if (mn == -INFINITY) continue;  // the whole block is padding
+        const float al = exp2f(m[h] - mn);
+        float lsum = 0.f;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = fmaf(o[h][e], a, p * vf[e]);
+        for (int x = 0; x < KS; ++x) {
+            const float p = exp2f(z[x][h] - mn);  // 0 for the padding entries
+            float vf[4];
+            unpack_bf16x4(vr[X0 + x], vf);
+            lsum += p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+        }
+        l[h] = fmaf(l[h], al, lsum);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[h][e] = fmaf(o[h][e], al, acc[e]);
         m[h] = mn;
     }
 }
 
-// Attend over list[0..n): 16 groups of 16 lanes, group g takes entries
-// g, g + 16, ...; lane l16 holds dims [8 l16, 8 l16 + 8).
+// Attend over list[0..n): 8 groups of 32 lanes; group g takes the entries
+// g, g + 8, g + 16, ...  Lane l32 holds dims [4 l32, 4 l32 + 4) of each row.
+// KL rows per group are loaded before any is used, then folded in blocks of
+// KS whose KS x G logits are reduced together (online softmax in base 2; the
+// query heads in LDS are pre-scaled by log2(e) / sqrt(128)).  The row
+// appended in this launch (app_row) is read through the coherent path.
 template <int G>
 __device__ __forceinline__ void attend_list(const uint16_t *__restrict__ Ku,
                                             const uint16_t *__restrict__ Vu, const int *list,
-                                            int n, int grp, int l16, const float (&qs)[G][8],
-                                            float (&m)[G], float (&l)[G], float (&o)[G][8]) {
-    int j = grp;
-    for (; j + 48 < n; j += 64) {
-        const int i0 = list[j], i1 = list[j + 16], i2 = list[j + 32], i3 = list[j + 48];
-        const uint4 k0 = *reinterpret_cast<const uint4 *>(Ku + (int64_t)i0 * kHeadDim + l16 * 8);
-        const uint4 k1 = *reinterpret_cast<const uint4 *>(Ku + (int64_t)i1 * kHeadDim + l16 * 8);
-        const uint4 k2 = *reinterpret_cast<const uint4 *>(Ku + (int64_t)i2 * kHeadDim + l16 * 8);
-        const uint4 k3 = *reinterpret_cast<const uint4 *>(Ku + (int64_t)i3 * kHeadDim + l16 * 8);
-        const uint4 v0 = *reinterpret_cast<const uint4 *>(Vu + (int64_t)i0 * kHeadDim + l16 * 8);
-        const uint4 v1 = *reinterpret_cast<const uint4 *>(Vu + (int64_t)i1 * kHeadDim + l16 * 8);
-        const uint4 v2 = *reinterpret_cast<const uint4 *>(Vu + (int64_t)i2 * kHeadDim + l16 * 8);
-        const uint4 v3 = *reinterpret_cast<const uint4 *>(Vu + (int64_t)i3 * kHeadDim + l16 * 8);
-        attend_one<G>(k0, v0, qs, m, l, o);
-        attend_one<G>(k1, v1, qs, m, l, o);
-        attend_one<G>(k2, v2, qs, m, l, o);
-        attend_one<G>(k3, v3, qs, m, l, o);
-    }
-    for (; j < n; j += 16) {
-        const int i0 = list[j];
-        const uint4 k0 = *reinterpret_cast<const uint4 *>(Ku + (int64_t)i0 * kHeadDim + l16 * 8);
-        const uint4 v0 = *reinterpret_cast<const uint4 *>(Vu + (int64_t)i0 * kHeadDim + l16 * 8);
-        attend_one<G>(k0, v0, qs, m, l, o);
+                                            int n, int grp, int l32, int64_t app_row,
+                                            const float4 (*qs)[kHeadDim / 4], float (&m)[G],
+                                            float (&l)[G], float (&o)[G][4]) {
+    constexpr int KL = 8;  // rows in flight per lane group (registers: 4 per row)
+    constexpr int KS = 4;
+    for (int j0 = grp; j0 < n; j0 += 8 * KL) {
+        uint64_t kr[KL], vr[KL];
+#pragma unroll
+        for (int x = 0; x < KL; ++x) {
+            const int jj = j0 + 8 * x;
+            kr[x] = 0;
+            vr[x] = 0;
+            if (jj < n) {
+                const int idx = list[jj];
+                const bool coh = idx == app_row;
+                kr[x] = load_row8(Ku + (int64_t)idx * kHeadDim, l32, coh);
+                vr[x] = load_row8(Vu + (int64_t)idx * kHeadDim, l32, coh);
+            }
+        }
+        attend_block<G, KL, KS, 0>(kr, vr, j0, n, l32, qs, m, l, o);
+        if (j0 + 8 * KS < n) attend_block<G, KL, KS, KS>(kr, vr, j0, n, l32, qs, m, l, o);
+        static_assert(KL == 2 * KS, "two logit blocks per load round");
     }
 }
 
-// grid: (n_splits, units); block 256
+// 8 consecutive scores from the workspace (aligned), kNoScore past s1.
+__device__ __forceinline__ uint4 load_scores8(const uint16_t *su, int64_t i0, int64_t s1) {
+    if (i0 >= s1) return make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
+    const uint64_t *p = reinterpret_cast<const uint64_t *>(su + i0);
+    const uint64_t lo = ld_dev(p);
+    const uint64_t hi = (i0 + 4 < s1) ? ld_dev(p + 1) : ~0ull;
+    return make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+}
+
 template <int G>
-__global__ __launch_bounds__(256) void k_select_attend(
-    const uint16_t *__restrict__ k_cache, const uint16_t *__restrict__ v_cache,
-    const int32_t *__restrict__ seq_len, const int32_t *__restrict__ topk, int k_max,
-    const uint16_t *__restrict__ q, int64_t max_ctx, int Hkv, int chunk, int n_chunks, int cps,
-    int n_splits, const uint16_t *__restrict__ scores, int64_t sstride,
-    const uint16_t *__restrict__ chunk_hist, const uint32_t *__restrict__ unit_hist,
-    float *__restrict__ partials, uint32_t *__restrict__ done, uint16_t *__restrict__ out,
-    int32_t *__restrict__ sel_out, int32_t *__restrict__ ctrl) {
-    constexpr int NB = G * kBits + 1;
-    constexpr int PER = (NB + 255) / 256;
-    __shared__ int s_list[kListCap];
-    __shared__ int s_scan[4];
-    __shared__ long long s_red[4];
-    __shared__ int s_T;
-    __shared__ int s_below;
-    __shared__ int s_last;
-    __shared__ float s_m[4][G], s_l[4][G];
-    __shared__ float s_o[4][G][kHeadDim];
+__device__ __forceinline__ void item_sel(const FusedArgs &a, int u, int s, Smem<G> &sm) {
+    constexpr int D = 4;  // selection rounds of scores in flight
+    const int b = u / a.Hkv, kv = u % a.Hkv, Hq = a.Hkv * G;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, l32 = t & 31, grp = t >> 5;
+    const StepLen sl = step_len(a, b);
+    const int64_t len = sl.len;
+    const int64_t k_eff = step_keff(a, b, len);
+    const int64_t span = (int64_t)a.cps * a.chunk;
+    const int64_t s0 = (int64_t)s * span;
+    if (k_eff == 0 || s0 >= len) return;
+    const int64_t s1 = s0 + span < len ? s0 + span : len;
+    const int n_splits_u = (int)((len + span - 1) / span);
 
-    const int split = blockIdx.x, unit = blockIdx.y, b = unit / Hkv, kv = unit % Hkv;
-    const int Hq = Hkv * G;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int l16 = tid & 15, grp = tid >> 4;
-
-    const int64_t len_raw = seq_len[b];
-    const int64_t len = clamp_len(len_raw, max_ctx);
-    int64_t kreq = topk[b];
-    if (kreq < 0) kreq = 0;
-    if (split == 0 && kv == 0 && tid == 0) {
-        int flags = 0;
-        if (len != len_raw) flags |= HATA_DEV_BAD_LENGTH;
-        if (kreq > k_max) flags |= HATA_DEV_TOPK_CLAMPED;
-        if (flags) atomicOr(&ctrl[kCtrlStatus], flags);
+    // the query heads, pre-scaled so exp2 gives exp((q.k) / sqrt(d))
+    {
+        const float qscale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
+        float *qf = &sm.sel.q[0][0].x;
+        for (int i = t; i < G * kHeadDim; i += kThreads)
+            qf[i] = bf16_to_f32(a.q[((int64_t)b * Hq + kv * G) * kHeadDim + i]) * qscale;
     }
-    if (kreq > k_max) kreq = k_max;
-    const int64_t k_eff = kreq < len ? kreq : len;
-    const int64_t s0 = (int64_t)split * cps * chunk;
-    const int64_t s1 = s0 + (int64_t)cps * chunk < len ? s0 + (int64_t)cps * chunk : len;
+    wg_wait_geq(a, unit_ctr(a, u, kPlan), 1);
 
-    int32_t *sel_u = sel_out ? sel_out + (int64_t)unit * k_max : nullptr;
-    if (sel_u && split == 0)
-        for (int64_t p = k_eff + tid; p < k_max; p += 256) sel_u[p] = -1;
+    // ---- the unit's selection plan and the first D rounds of scores
+    const int32_t *plan = a.sel_plan + (int64_t)u * (2 + 2 * a.n_splits);
+    const uint16_t *su = a.scores + (int64_t)u * a.sstride;
+    uint4 pf[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) pf[d] = load_scores8(su, s0 + (int64_t)d * kSelRound + 8 * t, s1);
+    const int T = ld_dev(plan + 0);
+    const int64_t quota = ld_dev(plan + 1);            // keys of score T to take, lowest index first
+    const int64_t ties_b = ld_dev(plan + 2 + 2 * s);   // score-T keys in earlier chunks
+    const int64_t below_b = ld_dev(plan + 3 + 2 * s);  // below-T keys in earlier chunks
+    const int64_t rem_quota = quota - ties_b > 0 ? quota - ties_b : 0;
+    int64_t out_pos = below_b + (ties_b < quota ? ties_b : quota);
 
-    float m[G], l[G], o[G][8];
+    int32_t *sel_u = a.sel_out ? a.sel_out + (int64_t)u * a.k_max : nullptr;
+    const uint16_t *Ku = a.k_cache + (int64_t)u * a.max_ctx * kHeadDim;
+    const uint16_t *Vu = a.v_cache + (int64_t)u * a.max_ctx * kHeadDim;
+    const int64_t app_row = sl.app ? sl.l0 : -1;
+    float m[G], l[G], o[G][4];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         m[h] = -INFINITY;
         l[h] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+        for (int e = 0; e < 4; ++e) o[h][e] = 0.f;
     }
-
-    if (k_eff > 0 && s0 < s1) {
-        // ---- cut score T: first bin whose cumulative count reaches k_eff
-        const uint32_t *uh = unit_hist + (int64_t)unit * NB;
-        uint32_t loc[PER];
-        int tsum = 0;
+    int64_t ties_acc = 0;
+    int list_n = 0;
+    for (int64_t rb = s0; rb < s1; rb += D * kSelRound) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int bin = tid * PER + e;
-            loc[e] = bin < NB ? uh[bin] : 0u;
-            tsum += (int)loc[e];
-        }
-        if (tid == 0) {  // defaults keep every index in range even for an inconsistent histogram
-            s_T = NB - 1;
-            s_below = 0;
-        }
-        int tot;
-        int run = block_excl_scan_256(tsum, s_scan, &tot);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int nxt = run + (int)loc[e];
-            if ((int64_t)run < k_eff && (int64_t)nxt >= k_eff) {
-                s_T = tid * PER + e;
-                s_below = run;
-            }
-            run = nxt;
-        }
-        __syncthreads();
-        const int T = s_T;
-        const int64_t quota = k_eff - s_below;  // keys of score T to take, lowest index first
-
-        // ---- what chunks before this split already took
-        const int cf = split * cps;
-        long long ties_b = 0, below_b = 0;
-        for (int cc = tid; cc < cf; cc += 256) {
-            const uint16_t *ch = chunk_hist + ((int64_t)unit * n_chunks + cc) * NB;
-            const int hi = ch[T];
-            const int lo = T > 0 ? ch[T - 1] : 0;
-            ties_b += hi - lo;
-            below_b += lo;
-        }
-        ties_b = block_sum_256(ties_b, s_red);
-        below_b = block_sum_256(below_b, s_red);
-        const int64_t rem_quota = quota - ties_b > 0 ? quota - ties_b : 0;
-        int64_t out_pos = below_b + (ties_b < quota ? ties_b : quota);
-
-        // ---- query slices, pre-scaled so exp2 gives exp((q.k)/sqrt(d))
-        float qs[G][8];
-        const float qscale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const uint4 r = *reinterpret_cast<const uint4 *>(
-                q + ((int64_t)b * Hq + kv * G + h) * kHeadDim + l16 * 8);
-            float f[8];
-            unpack_bf16x8(r, f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qs[h][e] = f[e] * qscale;
-        }
-
-        const uint16_t *su = scores + (int64_t)unit * sstride;
-        const uint16_t *Ku = k_cache + (int64_t)unit * max_ctx * kHeadDim;
-        const uint16_t *Vu = v_cache + (int64_t)unit * max_ctx * kHeadDim;
-        int64_t ties_acc = 0;
-        int list_n = 0;
-        for (int64_t base = s0; base < s1; base += kSelBlock) {
-            const int64_t i0 = base + (int64_t)tid * 8;
+        for (int d = 0; d < D; ++d) {
+            const int64_t base = rb + (int64_t)d * kSelRound;
+            if (base >= s1) break;
+            const int64_t i0 = base + (int64_t)t * 8;
+            const uint4 now = pf[d];
+            if (base + D * kSelRound < s1) pf[d] = load_scores8(su, i0 + D * kSelRound, s1);
             int sc[8];
+            sc[0] = now.x & 0xFFFF; sc[1] = now.x >> 16;
+            sc[2] = now.y & 0xFFFF; sc[3] = now.y >> 16;
+            sc[4] = now.z & 0xFFFF; sc[5] = now.z >> 16;
+            sc[6] = now.w & 0xFFFF; sc[7] = now.w >> 16;
             int n_eq = 0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                sc[e] = (i0 + e < s1) ? (int)su[i0 + e] : 0x7FFFFFFF;
-                n_eq += sc[e] == T;
-            }
+            for (int e = 0; e < 8; ++e) n_eq += (sc[e] == T && i0 + e < s1);
             int tie_tot;
-            const int tie_pre = block_excl_scan_256(n_eq, s_scan, &tie_tot);
+            const int tie_pre = block_excl_scan_small(n_eq, sm.sel.scan, 0, &tie_tot);
             int64_t tr = ties_acc + tie_pre;
             unsigned selmask = 0;
             int n_sel = 0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                bool sel = sc[e] < T;
+                if (i0 + e >= s1) continue;
+                bool take = sc[e] < T;
                 if (sc[e] == T) {
-                    sel = tr < rem_quota;
+                    take = tr < rem_quota;
                     ++tr;
                 }
-                if (sel) {
+                if (take) {
                     selmask |= 1u << e;
                     ++n_sel;
                 }
             }
             int sel_tot;
-            const int sel_pre = block_excl_scan_256(n_sel, s_scan, &sel_tot);
+            const int sel_pre = block_excl_scan_small(n_sel, sm.sel.scan, 1, &sel_tot);
             int p = list_n + sel_pre;
             int64_t gp = out_pos + sel_pre;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 if (selmask & (1u << e)) {
-                    s_list[p++] = (int)(i0 + e);
-                    if (sel_u && gp < k_max) sel_u[gp] = (int32_t)(i0 + e);
+                    sm.sel.list[p++] = (int)(i0 + e);
+                    if (sel_u && gp >= 0 && gp < a.k_max) sel_u[gp] = (int32_t)(i0 + e);
                     ++gp;
                 }
             }
@@ -379,97 +797,168 @@ __global__ __launch_bounds__(256) void k_select_attend(
             list_n += sel_tot;
             out_pos += sel_tot;
             ties_acc += tie_tot;
-            if (list_n > kListCap - kSelBlock || base + kSelBlock >= s1) {
-                attend_list<G>(Ku, Vu, s_list, list_n, grp, l16, qs, m, l, o);
+            if (list_n > kListCap - kSelRound || base + kSelRound >= s1) {
+                attend_list<G>(Ku, Vu, sm.sel.list, list_n, grp, l32, app_row, sm.sel.q, m, l, o);
                 __syncthreads();
                 list_n = 0;
             }
         }
     }
 
-    // ---- combine the 4 groups of each wave (lanes l16, +16, +32, +48)
+    // ---- combine the 2 groups of each wave (lanes l32 and l32 + 32), then the 4 waves
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+        const float m2 = __shfl_xor(m[h], 32, 64);
+        const float l2 = __shfl_xor(l[h], 32, 64);
+        float M, a1, a2;
+        lse_weights(m[h], m2, &M, &a1, &a2);
+        l[h] = l[h] * a1 + l2 * a2;
 #pragma unroll
-        for (int off = 16; off <= 32; off <<= 1) {
-            const float m2 = __shfl_xor(m[h], off, 64);
-            const float l2 = __shfl_xor(l[h], off, 64);
-            float M, a1, a2;
-            lse_weights(m[h], m2, &M, &a1, &a2);
-            l[h] = l[h] * a1 + l2 * a2;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float o2 = __shfl_xor(o[h][e], off, 64);
-                o[h][e] = o[h][e] * a1 + o2 * a2;
-            }
-            m[h] = M;
+        for (int e = 0; e < 4; ++e) {
+            const float o2 = __shfl_xor(o[h][e], 32, 64);
+            o[h][e] = o[h][e] * a1 + o2 * a2;
         }
+        m[h] = M;
     }
-    if (lane < 16) {
+    if (lane < 32) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             if (lane == 0) {
-                s_m[wv][h] = m[h];
-                s_l[wv][h] = l[h];
+                sm.sel.wm[wv][h] = m[h];
+                sm.sel.wl[wv][h] = l[h];
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s_o[wv][h][lane * 8 + e] = o[h][e];
+            for (int e = 0; e < 4; ++e) sm.sel.wo[wv][h][lane * 4 + e] = o[h][e];
         }
     }
     __syncthreads();
-    // ---- combine the 4 waves and write this split's partial
-    float *pu = partials + ((int64_t)unit * n_splits + split) * G * kPartialStride;
-    for (int pr = tid; pr < G * kHeadDim; pr += 256) {
+    float *pml = a.part_ml + ((int64_t)u * a.n_splits + s) * G * 2;
+    float *po = a.part_o + ((int64_t)u * a.n_splits + s) * G * kHeadDim;
+    for (int pr = t; pr < G * kHeadDim; pr += kThreads) {
         const int h = pr / kHeadDim, e = pr % kHeadDim;
-        float M = s_m[0][h], L = s_l[0][h], O = s_o[0][h][e];
+        float M = sm.sel.wm[0][h], L = sm.sel.wl[0][h], O = sm.sel.wo[0][h][e];
 #pragma unroll
         for (int w2 = 1; w2 < 4; ++w2) {
             float Mn, a1, a2;
-            lse_weights(M, s_m[w2][h], &Mn, &a1, &a2);
-            L = L * a1 + s_l[w2][h] * a2;
-            O = O * a1 + s_o[w2][h][e] * a2;
+            lse_weights(M, sm.sel.wm[w2][h], &Mn, &a1, &a2);
+            L = L * a1 + sm.sel.wl[w2][h] * a2;
+            O = O * a1 + sm.sel.wo[w2][h][e] * a2;
             M = Mn;
         }
-        float *ph = pu + h * kPartialStride;
-        ph[4 + e] = O;
+        st_dev(po + pr, O);
         if (e == 0) {
-            ph[0] = M;
-            ph[1] = L;
+            st_dev(pml + 2 * h, M);
+            st_dev(pml + 2 * h + 1, L);
         }
     }
+
     // ---- the last split of the unit merges all partials in split order
+    const int prev = wg_signal(unit_ctr(a, u, kAttn));
+    if (t == 0) sm.sel.last = (prev == n_splits_u - 1);
     __syncthreads();
-    if (tid == 0) {
-        __threadfence();
-        const unsigned prev = atomicAdd(&done[unit], 1u);
-        s_last = (prev == (unsigned)n_splits - 1);
-    }
+    if (!sm.sel.last) return;
+    const float *mlb = a.part_ml + (int64_t)u * a.n_splits * G * 2;
+    const float *ob = a.part_o + (int64_t)u * a.n_splits * G * kHeadDim;
+    for (int i = t; i < n_splits_u * G; i += kThreads) sm.sel.mw[i / G][i % G] = ld_dev(mlb + 2 * i);
     __syncthreads();
-    if (s_last) {
-        __threadfence();
-        const float *pb = partials + (int64_t)unit * n_splits * G * kPartialStride;
-        for (int pr = tid; pr < G * kHeadDim; pr += 256) {
-            const int h = pr / kHeadDim, e = pr % kHeadDim;
-            float M = -INFINITY;
-            for (int s = 0; s < n_splits; ++s) M = fmaxf(M, pb[(s * G + h) * kPartialStride]);
-            float L = 0.f, O = 0.f;
-            if (M != -INFINITY) {
-                for (int s = 0; s < n_splits; ++s) {
-                    const float *ph = pb + (s * G + h) * kPartialStride;
-                    const float ms = ph[0];
-                    const float a = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-                    L = fmaf(ph[1], a, L);
-                    O = fmaf(ph[4 + e], a, O);
-                }
-            }
-            out[((int64_t)b * Hq + kv * G + h) * kHeadDim + e] =
-                L > 0.f ? f32_to_bf16(O / L) : (uint16_t)0;
+    if (t < G) {
+        float M = -INFINITY;
+        for (int x = 0; x < n_splits_u; ++x) M = fmaxf(M, sm.sel.mw[x][t]);
+        float L = 0.f;
+        for (int x = 0; x < n_splits_u; ++x) {
+            const float ms = sm.sel.mw[x][t];
+            const float w8 = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+            sm.sel.mw[x][t] = w8;
+            L = fmaf(ld_dev(mlb + (x * G + t) * 2 + 1), w8, L);
         }
-        if (tid == 0) done[unit] = 0u;
+        sm.sel.ml[t] = L;
     }
+    __syncthreads();
+    for (int pr = t; pr < G * kHeadDim; pr += kThreads) {
+        const int h = pr / kHeadDim;
+        float O = 0.f;
+        int x = 0;
+        for (; x + 8 <= n_splits_u; x += 8) {
+            float v[8];
+#pragma unroll
+            for (int y = 0; y < 8; ++y) v[y] = ld_dev(ob + (int64_t)(x + y) * G * kHeadDim + pr);
+#pragma unroll
+            for (int y = 0; y < 8; ++y) O = fmaf(v[y], sm.sel.mw[x + y][h], O);
+        }
+        for (; x < n_splits_u; ++x) O = fmaf(ld_dev(ob + (int64_t)x * G * kHeadDim + pr), sm.sel.mw[x][h], O);
+        const float L = sm.sel.ml[h];
+        a.out[((int64_t)b * Hq + kv * G) * kHeadDim + pr] = L > 0.f ? f32_to_bf16(O / L) : (uint16_t)0;
+    }
+    __syncthreads();
 }
 
-// ------------------------------------------------------------------ plan + launch
+// ---------------------------------------------------------------- item order
+
+struct Item {
+    int kind;  // 0 PRO, 1 SCAN, 2 SEL
+    int u, i;
+};
+
+// PRO(u, p) for every unit and part; then for blocks x = 0 .. U+lag-1:
+// SCAN(x, *) if x < U, and SEL(x - lag, *) if x >= lag.
+__device__ __forceinline__ Item item_of(const FusedArgs &a, int tk) {
+    const int U = a.B * a.Hkv, C = a.n_chunks, S = a.n_splits;
+    const int lag = a.lag < U ? a.lag : U;
+    Item it;
+    if (tk < kProParts * U) {
+        it.kind = 0; it.u = tk / kProParts; it.i = tk % kProParts;
+        return it;
+    }
+    int r = tk - kProParts * U;
+    if (r < lag * C) {
+        it.kind = 1; it.u = r / C; it.i = r % C;
+        return it;
+    }
+    r -= lag * C;
+    const int midblocks = U - lag;
+    if (r < midblocks * (C + S)) {
+        const int blk = r / (C + S), off = r % (C + S);
+        if (off < C) {
+            it.kind = 1; it.u = lag + blk; it.i = off;
+        } else {
+            it.kind = 2; it.u = blk; it.i = off - C;
+        }
+        return it;
+    }
+    r -= midblocks * (C + S);
+    it.kind = 2; it.u = midblocks + r / S; it.i = r % S;
+    return it;
+}
+
+// Every item counts itself finished.  The last item of a unit resets the
+// unit's counters and counts the unit done for its batch entry; the last
+// unit of an entry publishes the new length and resets the entry counter.
+__device__ __forceinline__ void item_finish(const FusedArgs &a, int u) {
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    drain_memory();
+    const int per_unit = kProParts + a.n_chunks + a.n_splits;
+    if (add_dev(unit_ctr(a, u, kFin), 1) != per_unit - 1) return;
+    const int b = u / a.Hkv;
+    for (int w = 0; w < 5; ++w) st_dev(unit_ctr(a, u, w), 0);
+    drain_memory();
+    if (add_dev(batch_ctr(a, b), 1) != a.Hkv - 1) return;
+    const StepLen sl = step_len(a, b);
+    if (sl.app) st_dev(a.seq_len + b, (int32_t)(sl.l0 + 1));
+    st_dev(batch_ctr(a, b), 0);
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
+    __shared__ Smem<G> sm;
+    const Item it = item_of(a, blockIdx.x);
+    if (it.kind == 0) item_pro<G>(a, it.u, it.i, sm);
+    else if (it.kind == 1) item_scan<G>(a, it.u, it.i, sm);
+    else item_sel<G>(a, it.u, it.i, sm);
+    item_finish(a, it.u);
+}
+
+// ---------------------------------------------------------------- plan + launch
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -486,29 +975,36 @@ bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, DecodePlan *p) {
     d.G = G;
     d.NB = G * kBits + 1;
     d.max_ctx = max_ctx;
-    int chunk = 4096;
-    while (chunk > 1024 && units * ((max_ctx + chunk - 1) / chunk) < 1024) chunk >>= 1;
+    // Scan items: the largest chunk (8192 down to 1024 keys) that still gives
+    // at least 512 of them; selection splits: about 512 as well (at most 64
+    // per unit, the merge width).
+    int chunk = kMaxChunk;
+    while (chunk > 1024 && units * ((max_ctx + chunk - 1) / chunk) < 512) chunk >>= 1;
     d.chunk = chunk;
     d.n_chunks = (int)((max_ctx + chunk - 1) / chunk);
     if (d.n_chunks < 1) d.n_chunks = 1;
-    const int target = (int)((512 + units - 1) / units);
-    int cps = d.n_chunks / (target > 0 ? target : 1);
+    int64_t cps = (units * d.n_chunks) / 512;
     if (cps < 1) cps = 1;
+    if (cps > d.n_chunks) cps = d.n_chunks;
     if ((d.n_chunks + cps - 1) / cps > 64) cps = (d.n_chunks + 63) / 64;
-    d.cps = cps;
-    d.n_splits = (d.n_chunks + cps - 1) / cps;
+    d.cps = (int)cps;
+    d.n_splits = (int)((d.n_chunks + cps - 1) / cps);
     d.sstride = ((max_ctx + 63) / 64) * 64;
+    const int64_t items = units * (kProParts + d.n_chunks + d.n_splits);
+    if (items > INT32_MAX / 2) return false;
     size_t off = 0;
     d.off_qcodes = off;
     off = align256(off + (size_t)B * Hq * kWords * 4);
     d.off_unit_hist = off;
     off = align256(off + (size_t)units * d.NB * 4);
-    d.off_done = off;
-    off = align256(off + (size_t)units * 4);
     d.off_chunk_hist = off;
-    off = align256(off + (size_t)units * d.n_chunks * d.NB * 2);
-    d.off_partials = off;
-    off = align256(off + (size_t)units * d.n_splits * G * kPartialStride * 4);
+    off = align256(off + (size_t)units * d.n_chunks * d.NB * 4);
+    d.off_sel_plan = off;
+    off = align256(off + (size_t)units * (2 + 2 * d.n_splits) * 4);
+    d.off_part_ml = off;
+    off = align256(off + (size_t)units * d.n_splits * G * 2 * 4);
+    d.off_part_o = off;
+    off = align256(off + (size_t)units * d.n_splits * G * kHeadDim * 4);
     d.off_scores = off;
     off = align256(off + (size_t)units * d.sstride * 2);
     d.total = off;
@@ -517,58 +1013,57 @@ bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, DecodePlan *p) {
 }
 
 template <int G>
-static hipError_t launch_decode_g(const DecodePlan &p, const uint16_t *k_cache,
-                                  const uint16_t *v_cache, const uint32_t *codes,
-                                  const int32_t *seq_len, int32_t *ctrl, const uint16_t *q,
-                                  const float *w, const int32_t *topk, int k_max, uint16_t *out,
-                                  void *ws, int32_t *sel_idx_out, uint16_t *scores_out,
-                                  hipStream_t s) {
-    char *base = static_cast<char *>(ws);
-    uint32_t *qcodes = reinterpret_cast<uint32_t *>(base + p.off_qcodes);
-    uint32_t *unit_hist = reinterpret_cast<uint32_t *>(base + p.off_unit_hist);
-    uint32_t *done = reinterpret_cast<uint32_t *>(base + p.off_done);
-    uint16_t *chunk_hist = reinterpret_cast<uint16_t *>(base + p.off_chunk_hist);
-    float *partials = reinterpret_cast<float *>(base + p.off_partials);
-    uint16_t *scores = scores_out ? scores_out : reinterpret_cast<uint16_t *>(base + p.off_scores);
-    const int64_t sstride = scores_out ? p.max_ctx : p.sstride;
-    const int units = p.B * p.Hkv;
-
-    hipLaunchKernelGGL(k_qenc<G>, dim3(units), dim3(128), 0, s, q, w, p.Hkv, p.NB, qcodes,
-                       unit_hist, done);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_scan<G>, dim3(p.n_chunks, units), dim3(256), 0, s, codes, seq_len,
-                       qcodes, p.max_ctx, p.Hkv, p.chunk, p.n_chunks, scores, sstride,
-                       chunk_hist, unit_hist);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_select_attend<G>, dim3(p.n_splits, units), dim3(256), 0, s, k_cache,
-                       v_cache, seq_len, topk, k_max, q, p.max_ctx, p.Hkv, p.chunk, p.n_chunks,
-                       p.cps, p.n_splits, scores, sstride, chunk_hist, unit_hist, partials, done,
-                       out, sel_idx_out, ctrl);
+static hipError_t launch_g(const DecodePlan &p, FusedArgs &a, hipStream_t s) {
+    // Every selection item is queued behind every scan item.
+    a.lag = p.B * p.Hkv;
+    hipLaunchKernelGGL(k_decode_fused<G>, dim3(a.n_items), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodePlan &p, const uint16_t *k_cache, const uint16_t *v_cache,
-                         const uint32_t *codes, const int32_t *seq_len, int32_t *ctrl,
-                         const uint16_t *q, const float *w, const int32_t *topk, int k_max,
-                         uint16_t *out, void *ws, int32_t *sel_idx_out, uint16_t *scores_out,
-                         hipStream_t s) {
+hipError_t launch_decode(const DecodePlan &p, uint16_t *k_cache, uint16_t *v_cache,
+                         uint32_t *codes, int32_t *seq_len, int32_t *ctrl,
+                         const uint16_t *k_new, const uint16_t *v_new, const uint16_t *q,
+                         const float *w, const int32_t *topk, int k_max, uint16_t *out, void *ws,
+                         int32_t *sel_idx_out, uint16_t *scores_out, hipStream_t s) {
+    char *base = static_cast<char *>(ws);
+    FusedArgs a;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.codes = codes;
+    a.seq_len = seq_len;
+    a.ctrl = ctrl;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.q = q;
+    a.w = w;
+    a.topk = topk;
+    a.out = out;
+    a.sel_out = sel_idx_out;
+    a.scores_dbg = scores_out;
+    a.scores = reinterpret_cast<uint16_t *>(base + p.off_scores);
+    a.sstride = p.sstride;
+    a.qcodes = reinterpret_cast<uint32_t *>(base + p.off_qcodes);
+    a.unit_hist = reinterpret_cast<uint32_t *>(base + p.off_unit_hist);
+    a.chunk_hist = reinterpret_cast<uint32_t *>(base + p.off_chunk_hist);
+    a.sel_plan = reinterpret_cast<int32_t *>(base + p.off_sel_plan);
+    a.part_ml = reinterpret_cast<float *>(base + p.off_part_ml);
+    a.part_o = reinterpret_cast<float *>(base + p.off_part_o);
+    a.max_ctx = p.max_ctx;
+    a.B = p.B;
+    a.Hkv = p.Hkv;
+    a.k_max = k_max;
+    a.chunk = p.chunk;
+    a.n_chunks = p.n_chunks;
+    a.cps = p.cps;
+    a.n_splits = p.n_splits;
+    a.lag = 1;
+    a.n_items = p.B * p.Hkv * (kProParts + p.n_chunks + p.n_splits);
     switch (p.G) {
-        case 1:
-            return launch_decode_g<1>(p, k_cache, v_cache, codes, seq_len, ctrl, q, w, topk,
-                                      k_max, out, ws, sel_idx_out, scores_out, s);
-        case 2:
-            return launch_decode_g<2>(p, k_cache, v_cache, codes, seq_len, ctrl, q, w, topk,
-                                      k_max, out, ws, sel_idx_out, scores_out, s);
-        case 4:
-            return launch_decode_g<4>(p, k_cache, v_cache, codes, seq_len, ctrl, q, w, topk,
-                                      k_max, out, ws, sel_idx_out, scores_out, s);
-        case 8:
-            return launch_decode_g<8>(p, k_cache, v_cache, codes, seq_len, ctrl, q, w, topk,
-                                      k_max, out, ws, sel_idx_out, scores_out, s);
-        default:
-            return hipErrorInvalidValue;
+        case 1: return launch_g<1>(p, a, s);
+        case 2: return launch_g<2>(p, a, s);
+        case 4: return launch_g<4>(p, a, s);
+        case 8: return launch_g<8>(p, a, s);
+        default: return hipErrorInvalidValue;
     }
 }
 

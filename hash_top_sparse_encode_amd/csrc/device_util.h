@@ -42,6 +42,36 @@ __device__ __forceinline__ int block_excl_scan_256(int v, int *tmp, int *total) 
     return pre + x - v;
 }
 
+// Exclusive prefix sum over the 256 threads of a workgroup for small values
+// (0 <= v < 16): per wave, bit-plane ballots counted below each lane
+// (mbcnt); across the 4 waves, one LDS exchange.  `tmp` is 8 ints of LDS
+// used as two alternating halves (`phase` 0/1), so consecutive calls with
+// alternating phases need only one barrier each.  Every thread must call it.
+__device__ __forceinline__ int block_excl_scan_small(int v, int *tmp, int phase, int *total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int pre = 0, wtot = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint64_t m = __ballot((v >> b) & 1);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        pre += below << b;
+        wtot += __popcll(m) << b;
+    }
+    int *slot = tmp + 4 * phase;
+    if (lane == 0) slot[w] = wtot;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int x = slot[i];
+        base += (i < w) ? x : 0;
+        tot += x;
+    }
+    *total = tot;
+    return base + pre;
+}
+
 // Sum over the 256 threads of a workgroup (64-bit).
 __device__ __forceinline__ long long block_sum_256(long long v, long long *tmp) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;

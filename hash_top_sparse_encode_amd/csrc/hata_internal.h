@@ -12,10 +12,12 @@ constexpr int kHeadDim = 128;
 constexpr int kBits = 128;
 constexpr int kWords = 4;
 
-// ctrl[] word assignment (see hata_cache.ctrl in include/hata.h).
+// ctrl[] word assignment (see hata_cache.ctrl in include/hata.h): global
+// words first, then one 64-word (256-byte) line per (batch, KV head) unit
+// and one per batch entry for the decode kernel.
 constexpr int kCtrlStatus = 0;
 constexpr int kCtrlAppendDone = 1;
-constexpr int kCtrlEncodeFix = 2;
+constexpr int kCtrlUnitBase = 16;
 
 // Decode-step plan: how the context is cut into scan chunks and attention
 // splits, and where each buffer sits in the workspace.  A pure function of
@@ -29,12 +31,9 @@ struct DecodePlan {
     int cps = 0;         // scan chunks per attention split
     int n_splits = 0;    // ceil(n_chunks / cps)
     int64_t sstride = 0; // score row stride (elements) in the workspace
-    size_t off_qcodes = 0, off_unit_hist = 0, off_done = 0, off_chunk_hist = 0,
-           off_partials = 0, off_scores = 0, total = 0;
+    size_t off_qcodes = 0, off_unit_hist = 0, off_chunk_hist = 0, off_sel_plan = 0, off_part_ml = 0,
+           off_part_o = 0, off_scores = 0, total = 0;
 };
-
-// floats per (unit, split, head) partial: m, l, 2 pad, o[128]
-constexpr int kPartialStride = 4 + kHeadDim;
 
 bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, DecodePlan *p);
 
@@ -50,10 +49,12 @@ hipError_t launch_encode_exact(const uint16_t *keys, int64_t n_rows, int n_heads
                                int64_t row_stride, int64_t head_stride, const float *w,
                                uint32_t *codes, hipStream_t s);
 
-hipError_t launch_decode(const DecodePlan &p, const uint16_t *k_cache, const uint16_t *v_cache,
-                         const uint32_t *codes, const int32_t *seq_len, int32_t *ctrl,
-                         const uint16_t *q, const float *w, const int32_t *topk, int k_max,
-                         uint16_t *out, void *ws, int32_t *sel_idx_out, uint16_t *scores_out,
-                         hipStream_t s);
+// One decode step as a single persistent kernel.  k_new / v_new (bf16
+// [B][Hkv][128]) append one token per sequence first; both null: no append.
+hipError_t launch_decode(const DecodePlan &p, uint16_t *k_cache, uint16_t *v_cache,
+                         uint32_t *codes, int32_t *seq_len, int32_t *ctrl,
+                         const uint16_t *k_new, const uint16_t *v_new, const uint16_t *q,
+                         const float *w, const int32_t *topk, int k_max, uint16_t *out, void *ws,
+                         int32_t *sel_idx_out, uint16_t *scores_out, hipStream_t s);
 
 }  // namespace hata

@@ -55,8 +55,9 @@ extern "C" {
 #define HATA_N_BITS 128
 #define HATA_CODE_WORDS 4
 
-/* Words of the per-cache control block (see hata_cache.ctrl). */
-#define HATA_CTRL_WORDS 64
+/* int32 words of the per-cache control block (see hata_cache.ctrl). */
+#define HATA_CTRL_WORDS(batch, n_kv_heads) \
+    (16 + 64 * ((int64_t)(batch) * (int64_t)(n_kv_heads) + (int64_t)(batch)))
 
 typedef enum {
     HATA_OK = 0,
@@ -72,6 +73,7 @@ typedef enum {
 #define HATA_DEV_BAD_LENGTH 0x2      /* seq_len[b] outside [0, max_ctx] at decode: clamped */
 #define HATA_DEV_TOPK_CLAMPED 0x4    /* topk[b] > k_max at decode: clamped to k_max */
 #define HATA_DEV_BAD_NEW 0x8         /* n_new[b] < 0 or > t_max at append: entry b skipped */
+#define HATA_DEV_STALL 0x10          /* a decode wait timed out: outputs of that call invalid */
 
 /*
  * A key/value cache with its key-code cache, all device memory owned by the
@@ -81,10 +83,10 @@ typedef enum {
  *   codes : u32   [batch][n_kv_heads][max_ctx][4]
  *   seq_len: int32 [batch], the number of valid positions of each sequence;
  *           positions [0, seq_len[b]) hold keys, values and codes.
- *   ctrl  : int32 [HATA_CTRL_WORDS], zero-filled by the caller once before
- *           first use; word 0 is the sticky device status (HATA_DEV_*); the
- *           other words are library counters that every call leaves at
- *           zero again.
+ *   ctrl  : int32 [HATA_CTRL_WORDS(batch, n_kv_heads)], zero-filled by the
+ *           caller once before first use; word 0 is the sticky device status
+ *           (HATA_DEV_*); the other words are library counters that every
+ *           call leaves at zero again.
  * This is the cache of Algorithm 1 in the Figure 2 caption of the review
  * (K_cache, V_cache, and the code cache of rbit/32 words per key).
  */
@@ -111,8 +113,7 @@ typedef struct {
  *   n_rows    >= 0 rows; n_heads >= 1 heads, each with its own W_H.
  *   w_h       device fp32 [n_heads][128 (d)][128 (bit)].
  *   codes_out device u32 [n_rows][n_heads][4], fully overwritten.
- * Uses the MFMA encoder (bf16 matrix cores with a two-term split of W_H)
- * plus an exact recheck of the bits inside the error band.
+ * Every bit is the exact sign of the code convention above.
  * Errors: HATA_ERR_INVALID_ARG for null pointers (with n_rows > 0),
  * negative sizes or strides smaller than a row; HATA_ERR_HIP on launch
  * failure.
@@ -179,6 +180,21 @@ hata_status hata_decode_attn(const hata_cache *c, const uint16_t *q, const float
                              const int32_t *topk, int32_t k_max, uint16_t *out,
                              void *workspace, size_t ws_bytes, int32_t *sel_idx_out,
                              uint16_t *scores_out, void *stream);
+
+/*
+ * One whole decode step: append one token per sequence (as hata_append with
+ * n_new[b] = 1 for every b), then hata_decode_attn over the grown context --
+ * in a single kernel launch.
+ *   k_new, v_new device bf16 [batch][n_kv_heads][128], the step's new key
+ *                and value of every sequence.
+ * A sequence whose cache is full (seq_len[b] == max_ctx) is not appended
+ * (HATA_DEV_APPEND_OVERFLOW) and decodes over its existing context.  All
+ * other arguments and errors as hata_decode_attn.
+ */
+hata_status hata_decode_step(const hata_cache *c, const uint16_t *k_new, const uint16_t *v_new,
+                             const uint16_t *q, const float *w_h, const int32_t *topk,
+                             int32_t k_max, uint16_t *out, void *workspace, size_t ws_bytes,
+                             int32_t *sel_idx_out, uint16_t *scores_out, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *hata_status_string(hata_status s);

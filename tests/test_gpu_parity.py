@@ -72,10 +72,10 @@ def check_structure(spec, wl, sel):
             assert np.all(np.diff(head) > 0) and (ke == 0 or (head[0] >= 0 and head[-1] < spec.lengths[b]))
 
 
-def run_spec(spec, device, units=None, extra_ctx=3):
+def run_spec(spec, device, units=None, extra_ctx=3, fused=True):
     _say(f"[parity] {spec.name}: generating + prefill")
     wl = GpuWorkload(spec, device, extra_ctx=extra_ctx)
-    out, sel, sc = wl.step(debug=True)
+    out, sel, sc = wl.step(debug=True, fused=fused)
     torch.cuda.synchronize()
     assert wl.cache.status() == 0
     assert wl.cache.seq_len.cpu().tolist() == list(spec.lengths)
@@ -106,6 +106,29 @@ FUZZ = [
 @pytest.mark.parametrize("spec", FUZZ, ids=[s.name for s in FUZZ])
 def test_fuzz_all_units(gpu, spec):
     run_spec(spec, gpu)
+
+
+@pytest.mark.parametrize("spec", FUZZ[1:3], ids=[s.name for s in FUZZ[1:3]])
+def test_fuzz_append_then_decode(gpu, spec):
+    # the two-call path: hata_append (one token) then hata_decode_attn
+    run_spec(spec, gpu, fused=False)
+
+
+def test_fused_matches_two_calls(gpu):
+    spec = synth.custom("paths", 3, 8, 4, [7000, 300, 12000], [100, 9, 180], [7, 1, 12], seed=9)
+    a = GpuWorkload(spec, gpu, extra_ctx=2)
+    b = GpuWorkload(spec, gpu, extra_ctx=2)
+    oa, sa, ca = a.step(debug=True, fused=True)
+    ob, sb, cb = b.step(debug=True, fused=False)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+    assert torch.equal(sa, sb) and torch.equal(ca, cb)
+    assert torch.equal(a.cache.codes, b.cache.codes) and torch.equal(a.cache.k, b.cache.k)
+    assert torch.equal(a.cache.v, b.cache.v)
+    assert torch.equal(a.cache.seq_len, b.cache.seq_len)
+    assert a.cache.status() == 0 and b.cache.status() == 0
+    # counters are back at zero after each call
+    assert int(a.cache.ctrl[1:].abs().sum().item()) == 0
 
 
 def test_many_units_dense_and_sparse(gpu):

@@ -78,15 +78,25 @@ class GpuWorkload:
                                      self.out if out is None else out, self.ws,
                                      sel_idx_out=sel_idx_out, scores_out=scores_out)
 
-    def step(self, debug: bool = False):
-        """Append the step's token and decode; with debug, also return the
-        selected indices and the scores."""
-        self.append_token()
-        if not debug:
-            self.decode()
-            return self.out, None, None
+    def fused_step(self, sel_idx_out=None, scores_out=None, out=None):
+        return hata.hata_decode_step(self.cache, self.k_new, self.v_new, self.q, self.w,
+                                     self.topk, self.k_max, self.out if out is None else out,
+                                     self.ws, sel_idx_out=sel_idx_out, scores_out=scores_out)
+
+    def debug_buffers(self):
         B, Hkv = self.spec.B, self.spec.Hkv
         sel = torch.full((B, Hkv, self.k_max), -7, dtype=torch.int32, device=self.device)
         sc = torch.zeros((B, Hkv, self.max_ctx), dtype=torch.int16, device=self.device)
-        self.decode(sel_idx_out=sel, scores_out=sc)
+        return sel, sc
+
+    def step(self, debug: bool = False, fused: bool = True):
+        """The decode step: append the step's token, then decode -- one fused
+        launch (hata_decode_step) or hata_append + hata_decode_attn.  With
+        debug, also return the selected indices and the scores."""
+        sel, sc = self.debug_buffers() if debug else (None, None)
+        if fused:
+            self.fused_step(sel_idx_out=sel, scores_out=sc)
+        else:
+            self.append_token()
+            self.decode(sel_idx_out=sel, scores_out=sc)
         return self.out, sel, sc
