@@ -9,7 +9,9 @@ append of one new token per sequence (K/V row copy + its code), query codes,
 Hamming scan, top-k select, gather + softmax attention -- one kernel launch.  Steps cycle over
 LAYERS independent layer caches (same contents, distinct memory), as a model
 visits its layers, so the 256 MB last-level cache cannot hold the scanned
-codes between two visits of the same layer.
+codes between two visits of the same layer, and over QUERIES step queries
+(step 0's is the one the planted keys align with; the others are fresh
+draws), so the gathered rows change from visit to visit.
 
 Prints one JSON line.  value = decode steps per second on one GPU.
 """
@@ -30,6 +32,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 HBM_PEAK_GBS = 8000.0
 LAYERS = 8
+QUERIES = 7  # distinct step queries, coprime with LAYERS: 56 (layer, query) pairs
 
 
 def parse():
@@ -140,11 +143,15 @@ def main():
 
     k_new = base.k_new.view(B, Hkv, 128)
     v_new = base.v_new.view(B, Hkv, 128)
+    # A different query at each step, as in decoding, so that consecutive
+    # visits of a layer select different rows.
+    from workload import bf16_dev
+    queries = [base.q] + [bf16_dev(synth.gen_q(spec, i), dev) for i in range(1, QUERIES)]
 
     def step(s):
         ly = layers[s % L]
-        hata.hata_decode_step(ly.cache, k_new, v_new, base.q, base.w, base.topk, base.k_max,
-                              ly.out, ly.ws)
+        hata.hata_decode_step(ly.cache, k_new, v_new, queries[s % QUERIES], base.w, base.topk,
+                              base.k_max, ly.out, ly.ws)
 
     for s in range(args.warmup):
         step(s)
@@ -196,7 +203,7 @@ def main():
         "config": {
             "workload": "hashed top-k decode step: B=4, Hq=32, Hkv=8, d=128, r=128, "
                         f"context {N} (+{args.steps // L} appended), top-k {K}, "
-                        f"{L} layer caches visited in turn",
+                        f"{L} layer caches visited in turn, {QUERIES} step queries",
             "tokens_per_s": steps_per_s * B,
             "us_per_step": ms_per_step * 1e3,
             "step_alg_bytes": step_bytes,

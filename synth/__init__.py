@@ -237,10 +237,12 @@ def custom(name, B, Hq, Hkv, lengths, topk, planted, seed=0, stride=None) -> Spe
 # tensors
 # --------------------------------------------------------------------------
 
-def gen_q(spec: Spec) -> np.ndarray:
-    """Decode-step queries, bf16 bits [B][Hq][128]."""
+def gen_q(spec: Spec, step: int = 0) -> np.ndarray:
+    """Decode-step queries, bf16 bits [B][Hq][128].  Step 0 is the query the
+    planted keys are aligned with; step i > 0 takes the next block of the same
+    stream (independent N(0, 1) draws, aligned with no planted key)."""
     n = spec.B * spec.Hq * HEAD_DIM
-    return normal_bf16(spec.seed, T_Q, 0, n).reshape(spec.B, spec.Hq, HEAD_DIM)
+    return normal_bf16(spec.seed, T_Q, step * n, n).reshape(spec.B, spec.Hq, HEAD_DIM)
 
 
 def gen_w(spec: Spec) -> np.ndarray:
