@@ -50,21 +50,29 @@
 namespace hata {
 
 constexpr int kThreads = 256;
-constexpr int kMaxChunk = 8192;    // keys per scan item
-constexpr int kScanPass = 4096;    // keys per pass: 16 per thread, 4 runs of 4 consecutive keys
+constexpr int kChunk = 4096;       // keys per scan item: 16 per thread
+constexpr int kRuns = kChunk / kThreads;
+#ifndef HATA_SEL_LAG
+#define HATA_SEL_LAG (1 << 20)
+#endif
+constexpr int kSelLag = HATA_SEL_LAG;  // SEL items of unit u follow the SCAN items of unit u + lag
+constexpr int kMinCps = 2;         // scan chunks per selection split, at least
+constexpr int kMaxSplits = 64;     // selection splits per unit, at most (the merge width)
 constexpr int kSelRound = 2048;    // 8 scores per thread per selection round
-constexpr int kListCap = 4096;     // selected indices buffered in LDS
-constexpr int kSpinLimit = 1 << 21;
+constexpr int kSelRounds = 4;      // selection rounds per batch (scores prefetched together)
+constexpr int kListCap = kSelRounds * kSelRound;  // selected indices buffered in LDS
+constexpr int kSpinLimit = 1 << 22;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint16_t kNoScore = 0xFFFF;
 
 typedef float fvec4 __attribute__((ext_vector_type(4)));
+typedef uint32_t uvec4 __attribute__((ext_vector_type(4)));
 
 // PRO work per unit is split over this many workgroups (32 code bits each)
 constexpr int kProParts = 4;
 
 // per-unit counter words
-constexpr int kPro = 0, kScan = 1, kAttn = 2, kFin = 3, kPlan = 4;
+constexpr int kPro = 0, kScan = 1, kAttn = 2, kFin = 3, kNumCtr = 4;
 constexpr int kUnitWords = 64;  // one 256-byte line per unit (and per batch entry)
 
 struct FusedArgs {
@@ -83,15 +91,14 @@ struct FusedArgs {
     uint16_t *scores_dbg;    // optional debug output, row stride max_ctx
     uint16_t *scores;        // workspace, row stride sstride
     uint32_t *qcodes;
-    uint32_t *unit_hist;
-    uint32_t *chunk_hist;
-    int32_t *sel_plan;       // per unit: T, quota, then (ties, below) before each split
+    uint32_t *unit_hist;     // per unit: 128 G + 2 words (bins in pairs)
+    uint32_t *chunk_hist;    // per unit and scan slot: cumulative counts, 128 G + 1 bins
     float *part_ml;
     float *part_o;
     int64_t max_ctx;
     int64_t sstride;
     int B, Hkv, k_max;
-    int chunk, n_chunks, cps, n_splits, lag;
+    int n_chunks, cps, n_splits, lag;
     int n_items;
 };
 
@@ -171,10 +178,7 @@ __device__ __forceinline__ void wg_wait_geq(const FusedArgs &a, int32_t *p, int 
     if (threadIdx.x == 0) {
         int spins = 0;
         while (ld_dev(p) < target) {
-            // back off: about 0.03, 0.2, then 0.9 microseconds between polls
-            if (spins < 8) __builtin_amdgcn_s_sleep(1);
-            else if (spins < 24) __builtin_amdgcn_s_sleep(8);
-            else __builtin_amdgcn_s_sleep(32);
+            __builtin_amdgcn_s_sleep(2);
             if (++spins > kSpinLimit) {
                 atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_STALL);
                 break;
@@ -209,7 +213,6 @@ struct SmemScan {
     static constexpr int NB = G * kBits + 1;
     uint32_t hist[4][NB];
     int scan[4];
-    int last, T, below;
 };
 
 template <int G>
@@ -219,7 +222,8 @@ struct SmemSel {
     float wm[4][G];
     float wl[4][G];
     float wo[4][G][kHeadDim];
-    float mw[64][G];  // merge: per-split weights
+    float mw[kMaxSplits][G];  // merge: per-split maxima, then weights
+    float lv[kMaxSplits][G];  // merge: per-split sums
     float ml[G];
     int scan[8];
     long long red[4];
@@ -309,7 +313,7 @@ __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Sm
                        reinterpret_cast<const uint64_t *>(a.v_new + src)[t - 32]);
             }
         }
-        for (int i = t; i < NB; i += kThreads) st_dev(a.unit_hist + (int64_t)u * NB + i, 0u);
+        for (int i = t; i < NB + 1; i += kThreads) st_dev(a.unit_hist + (int64_t)u * (NB + 1) + i, 0u);
         const int64_t k_eff = step_keff(a, b, sl.len);
         if (a.sel_out) {
             int32_t *su = a.sel_out + (int64_t)u * a.k_max;
@@ -387,10 +391,10 @@ __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Sm
     __syncthreads();
 }
 
-// ---------------------------------------------------------------- SCAN(u, c)
+// ---------------------------------------------------------------- scanners
 
 template <int G>
-__device__ __forceinline__ int group_hamming(const uint4 &k, const uint32_t (&qc)[G][4]) {
+__device__ __forceinline__ int group_hamming(const uvec4 &k, const uint32_t (&qc)[G][4]) {
     int s = 0;
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -399,91 +403,121 @@ __device__ __forceinline__ int group_hamming(const uint4 &k, const uint32_t (&qc
     return s;
 }
 
+// Chunk c of unit u: keys [c kChunk, min((c + 1) kChunk, len)).
+struct Slot {
+    int u, c;
+    int64_t p0, p1;  // key range, empty if p0 >= p1
+    StepLen sl;
+};
+
+__device__ __forceinline__ Slot slot_of(const FusedArgs &a, int u, int c) {
+    Slot s;
+    s.u = u;
+    s.c = c;
+    s.sl = step_len(a, s.u / a.Hkv);
+    s.p0 = (int64_t)s.c * kChunk;
+    s.p1 = s.p0 + kChunk < s.sl.len ? s.p0 + kChunk : s.sl.len;
+    return s;
+}
+
+// Issue a chunk's 16-byte code loads (thread t: keys p0 + 256 r + t, r <
+// kRuns: each instruction reads 1 KB per wave, contiguous) and, in thread
+// 0, a poll of the unit's PRO counter that returns right behind them.
+__device__ __forceinline__ void slot_issue(const FusedArgs &a, const Slot &s, uvec4 (&buf)[kRuns],
+                                           int &poll) {
+    const int t = threadIdx.x;
+    const uvec4 *kc = reinterpret_cast<const uvec4 *>(a.codes) + (int64_t)s.u * a.max_ctx;
+#pragma unroll
+    for (int r = 0; r < kRuns; ++r) {
+        const int64_t i = s.p0 + r * kThreads + t;
+        buf[r] = i < s.p1 ? kc[i] : uvec4{0u, 0u, 0u, 0u};
+    }
+    poll = kProParts;
+    if (t == 0 && s.p0 < s.p1) poll = ld_dev(unit_ctr(a, s.u, kPro));
+}
+
+// Wait for the unit's PRO parts (the prefetched poll usually settles it),
+// then issue the loads of the query codes and, where the slot holds the key
+// appended in this launch, of its code.  Nothing waits for these loads here.
 template <int G>
-__device__ __forceinline__ void item_scan(const FusedArgs &a, int u, int c, Smem<G> &sm) {
-    constexpr int NB = G * kBits + 1;
-    constexpr int PER = (NB + kThreads - 1) / kThreads;
-    constexpr int RUNS = kScanPass / (4 * kThreads);  // runs of 4 keys per thread and pass
-    const int b = u / a.Hkv, kv = u % a.Hkv;
-    const int t = threadIdx.x, wv = t >> 6;
-    const StepLen sl = step_len(a, b);
-    const int64_t c0 = (int64_t)c * a.chunk;
-    if (c0 >= sl.len) return;
-    const int64_t c1 = c0 + a.chunk < sl.len ? c0 + a.chunk : sl.len;
-    // While the unit's PRO parts are still running, give their W_H loads about
-    // a microsecond's head start before this chunk's loads join the queues.
-    if (t == 0 && ld_dev(unit_ctr(a, u, kPro)) < kProParts) {
-        __builtin_amdgcn_s_sleep(20);  // 20 x 64 cycles each
-        __builtin_amdgcn_s_sleep(20);
+__device__ __forceinline__ void slot_begin(const FusedArgs &a, const Slot &s, int poll,
+                                           uint64_t (&qraw)[G][2], uint64_t (&app)[2]) {
+    if (threadIdx.x == 0 && poll < kProParts) {
+        int spins = 0;
+        while (ld_dev(unit_ctr(a, s.u, kPro)) < kProParts) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins > kSpinLimit) {
+                atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_STALL);
+                break;
+            }
+        }
     }
-    for (int i = t; i < 4 * NB; i += kThreads) (&sm.scan.hist[0][0])[i] = 0u;
     __syncthreads();
-    const uint4 *kc = reinterpret_cast<const uint4 *>(a.codes) + (int64_t)u * a.max_ctx;
-    uint16_t *sc = a.scores + (int64_t)u * a.sstride;
-    uint16_t *sd = a.scores_dbg ? a.scores_dbg + (int64_t)u * a.max_ctx : nullptr;
-    uint32_t *wh = sm.scan.hist[wv];
-    uint32_t qc[G][4];
-    // The chunk in passes of kScanPass keys; each pass issues all its code
-    // loads before using any.  Only the appended code (written by PRO in this
-    // launch) is re-read after the wait for PRO.
-    for (int64_t p0 = c0; p0 < c1; p0 += kScanPass) {
-        uint4 kr[RUNS][4];
+    const int b = s.u / a.Hkv, kv = s.u % a.Hkv;
+    const uint64_t *qsrc =
+        reinterpret_cast<const uint64_t *>(a.qcodes + ((int64_t)b * a.Hkv * G + kv * G) * kWords);
 #pragma unroll
-        for (int r = 0; r < RUNS; ++r) {
-            const int64_t i0 = p0 + (int64_t)r * 4 * kThreads + 4 * t;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                kr[r][e] = (i0 + e < c1) ? kc[i0 + e] : make_uint4(0, 0, 0, 0);
-        }
-        if (p0 == c0) {
-            wg_wait_geq(a, unit_ctr(a, u, kPro), kProParts);
-            const uint32_t *qsrc = a.qcodes + ((int64_t)b * a.Hkv * G + kv * G) * kWords;
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const uint64_t lo = ld_dev(reinterpret_cast<const uint64_t *>(qsrc + h * 4));
-                const uint64_t hi = ld_dev(reinterpret_cast<const uint64_t *>(qsrc + h * 4 + 2));
-                qc[h][0] = __builtin_amdgcn_readfirstlane((uint32_t)lo);
-                qc[h][1] = __builtin_amdgcn_readfirstlane((uint32_t)(lo >> 32));
-                qc[h][2] = __builtin_amdgcn_readfirstlane((uint32_t)hi);
-                qc[h][3] = __builtin_amdgcn_readfirstlane((uint32_t)(hi >> 32));
-            }
-        }
-        const int64_t p1 = p0 + kScanPass < c1 ? p0 + kScanPass : c1;
-        if (sl.app && sl.l0 >= p0 && sl.l0 < p1) {
-            const int64_t off = sl.l0 - p0;
-            const int r = (int)(off / (4 * kThreads)), tt = (int)((off % (4 * kThreads)) / 4);
-            if (t == tt) {
-                const uint64_t *p = reinterpret_cast<const uint64_t *>(kc + sl.l0);
-                const uint64_t lo = ld_dev(p), hi = ld_dev(p + 1);
-                const uint4 v = make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi,
-                                           (uint32_t)(hi >> 32));
-#pragma unroll
-                for (int rr = 0; rr < RUNS; ++rr)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (rr == r && e == (int)(off % 4)) kr[rr][e] = v;
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < RUNS; ++r) {
-            const int64_t i0 = p0 + (int64_t)r * 4 * kThreads + 4 * t;
-            uint32_t s4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                s4[e] = kNoScore;
-                if (i0 + e < c1) {
-                    const int s = group_hamming<G>(kr[r][e], qc);
-                    s4[e] = (uint32_t)s;
-                    atomicAdd(&wh[s], 1u);
-                    if (sd) sd[i0 + e] = (uint16_t)s;
-                }
-            }
-            if (i0 < c1)
-                st_dev(reinterpret_cast<uint64_t *>(sc + i0),
-                       (uint64_t)s4[0] | ((uint64_t)s4[1] << 16) | ((uint64_t)s4[2] << 32) |
-                           ((uint64_t)s4[3] << 48));
+    for (int h = 0; h < G; ++h) {
+        qraw[h][0] = ld_dev(qsrc + 2 * h);
+        qraw[h][1] = ld_dev(qsrc + 2 * h + 1);
+    }
+    app[0] = app[1] = 0;
+    if (s.sl.app && s.sl.l0 >= s.p0 && s.sl.l0 < s.p1) {
+        const int64_t off = s.sl.l0 - s.p0;
+        if (threadIdx.x == (int)(off % kThreads)) {
+            const uint64_t *p = reinterpret_cast<const uint64_t *>(
+                reinterpret_cast<const uvec4 *>(a.codes) + (int64_t)s.u * a.max_ctx + s.sl.l0);
+            app[0] = ld_dev(p);
+            app[1] = ld_dev(p + 1);
         }
     }
+}
+
+// Scores of the chunk's keys: lane pairs store two to a 32-bit word; every
+// score is counted into its wave's LDS histogram.
+template <int G>
+__device__ __forceinline__ void slot_score(const FusedArgs &a, const Slot &s, const uvec4 (&buf)[kRuns],
+                                           const uint64_t (&qraw)[G][2], const uint64_t (&app)[2],
+                                           Smem<G> &sm) {
+    const int t = threadIdx.x, wv = t >> 6;
+    uint32_t qc[G][4];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        qc[h][0] = __builtin_amdgcn_readfirstlane((uint32_t)qraw[h][0]);
+        qc[h][1] = __builtin_amdgcn_readfirstlane((uint32_t)(qraw[h][0] >> 32));
+        qc[h][2] = __builtin_amdgcn_readfirstlane((uint32_t)qraw[h][1]);
+        qc[h][3] = __builtin_amdgcn_readfirstlane((uint32_t)(qraw[h][1] >> 32));
+    }
+    const int64_t app_row = s.sl.app ? s.sl.l0 : -1;
+    const uvec4 appv = {(uint32_t)app[0], (uint32_t)(app[0] >> 32), (uint32_t)app[1],
+                        (uint32_t)(app[1] >> 32)};
+    uint32_t *wh = sm.scan.hist[wv];
+    uint16_t *sc = a.scores + (int64_t)s.u * a.sstride;
+    uint16_t *sd = a.scores_dbg ? a.scores_dbg + (int64_t)s.u * a.max_ctx : nullptr;
+#pragma unroll
+    for (int r = 0; r < kRuns; ++r) {
+        const int64_t i = s.p0 + r * kThreads + t;
+        uint32_t sv = kNoScore;
+        if (i < s.p1) {
+            const uvec4 k = (i == app_row) ? appv : buf[r];
+            sv = (uint32_t)group_hamming<G>(k, qc);
+            atomicAdd(&wh[sv], 1u);
+            if (sd) sd[i] = (uint16_t)sv;
+        }
+        const uint32_t nb = (uint32_t)__shfl_xor((int)sv, 1, 64);
+        if (!(t & 1) && i < s.p1) st_dev(reinterpret_cast<uint32_t *>(sc + i), sv | (nb << 16));
+    }
+}
+
+// The chunk's histogram: its cumulative counts (bin by bin) go to the
+// chunk's row of chunk_hist, and its counts are added into the unit
+// histogram two bins per 64-bit atomic.
+template <int G>
+__device__ __forceinline__ void slot_publish(const FusedArgs &a, const Slot &s, Smem<G> &sm) {
+    constexpr int NB = G * kBits + 1;
+    constexpr int NP = (NB + 1) / 2;
+    constexpr int PER = (NB + kThreads - 1) / kThreads;
+    const int t = threadIdx.x;
     __syncthreads();
     uint32_t loc[PER];
     int tsum = 0;
@@ -491,90 +525,75 @@ __device__ __forceinline__ void item_scan(const FusedArgs &a, int u, int c, Smem
     for (int e = 0; e < PER; ++e) {
         const int bin = t * PER + e;
         uint32_t v = 0;
-        if (bin < NB) v = sm.scan.hist[0][bin] + sm.scan.hist[1][bin] + sm.scan.hist[2][bin] +
-                          sm.scan.hist[3][bin];
+        if (bin < NB) {
+            v = sm.scan.hist[0][bin] + sm.scan.hist[1][bin] + sm.scan.hist[2][bin] +
+                sm.scan.hist[3][bin];
+            sm.scan.hist[0][bin] = v;
+            sm.scan.hist[1][bin] = 0u;
+            sm.scan.hist[2][bin] = 0u;
+            sm.scan.hist[3][bin] = 0u;
+        }
         loc[e] = v;
         tsum += (int)v;
     }
     int tot;
-    int run = block_excl_scan_256(tsum, sm.scan.scan, &tot);
-    uint32_t *ch = a.chunk_hist + ((int64_t)u * a.n_chunks + c) * NB;
-    int32_t *uh = reinterpret_cast<int32_t *>(a.unit_hist) + (int64_t)u * NB;
+    int run = block_excl_scan_256(tsum, sm.scan.scan, &tot);  // its barriers publish hist[0]
+    uint32_t *ch = a.chunk_hist + ((int64_t)s.u * a.n_chunks + s.c) * NB;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
         const int bin = t * PER + e;
         if (bin < NB) {
             run += (int)loc[e];
             st_dev(ch + bin, (uint32_t)run);
-            if (loc[e]) add_dev(uh + bin, (int)loc[e]);
         }
     }
-    const int prev = wg_signal(unit_ctr(a, u, kScan));
-    if (t == 0) sm.scan.last = prev;
-    __syncthreads();
-    const int n_chunks_u = (int)((sl.len + a.chunk - 1) / a.chunk);
-    if (sm.scan.last != n_chunks_u - 1) return;
-    // The last chunk of the unit to finish turns the histograms into the
-    // selection plan: the cut score T (first bin whose cumulative count
-    // reaches k_eff), the quota of score-T keys to take, and for each split
-    // the number of score-T and below-T keys in the chunks before it.
-    const int64_t k_eff = step_keff(a, b, sl.len);
-    if (k_eff > 0) {
-        int32_t *plan = a.sel_plan + (int64_t)u * (2 + 2 * a.n_splits);
-        // T = first bin whose cumulative unit count reaches k_eff (the counts
-        // sum to the unit length, so one exists); below = count before T.
-        const uint32_t *uhr = a.unit_hist + (int64_t)u * NB;
-        int tsum2 = 0;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int bin = t * PER + e;
-            loc[e] = bin < NB ? ld_dev(uhr + bin) : 0u;
-            tsum2 += (int)loc[e];
-        }
-        if (t == 0) {
-            sm.scan.T = NB - 1;
-            sm.scan.below = 0;
-        }
-        int tot2;
-        int run2 = block_excl_scan_256(tsum2, sm.scan.scan, &tot2);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int nxt = run2 + (int)loc[e];
-            if ((int64_t)run2 < k_eff && (int64_t)nxt >= k_eff) {
-                sm.scan.T = t * PER + e;
-                sm.scan.below = run2;
-            }
-            run2 = nxt;
-        }
-        __syncthreads();
-        const int T = sm.scan.T;
-        int ties_run = 0, below_run = 0;
-        for (int cb = 0; cb < n_chunks_u; cb += kThreads) {
-            const int cc = cb + t;
-            int tie = 0, lo = 0;
-            if (cc < n_chunks_u) {
-                const uint32_t *chc = a.chunk_hist + ((int64_t)u * a.n_chunks + cc) * NB;
-                lo = T > 0 ? (int)ld_dev(chc + T - 1) : 0;
-                tie = (int)ld_dev(chc + T) - lo;
-            }
-            int tie_all, lo_all;
-            const int tie_pre = block_excl_scan_256(tie, sm.scan.scan, &tie_all);
-            const int lo_pre = block_excl_scan_256(lo, sm.scan.scan, &lo_all);
-            if (cc < n_chunks_u && cc % a.cps == 0) {
-                const int sidx = cc / a.cps;
-                st_dev(plan + 2 + 2 * sidx, ties_run + tie_pre);
-                st_dev(plan + 3 + 2 * sidx, below_run + lo_pre);
-            }
-            ties_run += tie_all;
-            below_run += lo_all;
-        }
-        if (t == 0) {
-            st_dev(plan + 0, T);
-            st_dev(plan + 1, (int32_t)(k_eff - sm.scan.below));
-        }
+    uint64_t *uh = reinterpret_cast<uint64_t *>(a.unit_hist) + (int64_t)s.u * NP;
+    for (int pr = t; pr < NP; pr += kThreads) {
+        const uint32_t lo = sm.scan.hist[0][2 * pr];
+        const uint32_t hi = 2 * pr + 1 < NB ? sm.scan.hist[0][2 * pr + 1] : 0u;
+        if (lo | hi)
+            __hip_atomic_fetch_add(uh + pr, (uint64_t)lo | ((uint64_t)hi << 32), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
     }
-    wg_signal(unit_ctr(a, u, kPlan));
-    __syncthreads();
+}
+
+// Thread 0 only: count one item of unit u finished.  The last item of a
+// unit resets the unit's counters and counts the unit done for its batch
+// entry; the last unit of an entry publishes the new length and resets the
+// entry counter.
+__device__ __forceinline__ void unit_finish(const FusedArgs &a, int u) {
+    drain_memory();
+    const int per_unit = kProParts + a.n_chunks + a.n_splits;
+    if (add_dev(unit_ctr(a, u, kFin), 1) != per_unit - 1) return;
+    const int b = u / a.Hkv;
+    for (int w = 0; w < kNumCtr; ++w) st_dev(unit_ctr(a, u, w), 0);
+    drain_memory();
+    if (add_dev(batch_ctr(a, b), 1) != a.Hkv - 1) return;
+    const StepLen sl = step_len(a, b);
+    if (sl.app) st_dev(a.seq_len + b, (int32_t)(sl.l0 + 1));
+    st_dev(batch_ctr(a, b), 0);
+}
+
+// SCAN(u, c): the chunk's code loads go out first (all 64 KB of them), then
+// the wait for the unit's query codes, the scores, the histograms and the
+// signal.
+template <int G>
+__device__ __forceinline__ void item_scan(const FusedArgs &a, int u, int c, Smem<G> &sm) {
+    constexpr int NB = G * kBits + 1;
+    const Slot cur = slot_of(a, u, c);
+    if (cur.p0 >= cur.p1) return;
+    // While the unit's PRO parts are still running, give their W_H loads a
+    // short head start before this chunk's loads join the queues.
+    if (ld_dev(unit_ctr(a, u, kPro)) < kProParts) __builtin_amdgcn_s_sleep(20);
+    uvec4 buf[kRuns];
+    int poll;
+    slot_issue(a, cur, buf, poll);
+    for (int i = threadIdx.x; i < 4 * NB; i += kThreads) (&sm.scan.hist[0][0])[i] = 0u;
+    uint64_t qraw[G][2], app[2];
+    slot_begin<G>(a, cur, poll, qraw, app);  // its barrier also orders the clearing
+    slot_score<G>(a, cur, buf, qraw, app, sm);
+    slot_publish<G>(a, cur, sm);
+    wg_signal(unit_ctr(a, u, kScan));
 }
 
 // ---------------------------------------------------------------- SEL(u, s)
@@ -699,16 +718,19 @@ __device__ __forceinline__ uint4 load_scores8(const uint16_t *su, int64_t i0, in
 
 template <int G>
 __device__ __forceinline__ void item_sel(const FusedArgs &a, int u, int s, Smem<G> &sm) {
-    constexpr int D = 4;  // selection rounds of scores in flight
+    constexpr int D = kSelRounds;  // selection rounds of scores in flight
+    constexpr int NB = G * kBits + 1;
+    constexpr int PER = (NB + kThreads - 1) / kThreads;
     const int b = u / a.Hkv, kv = u % a.Hkv, Hq = a.Hkv * G;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6, l32 = t & 31, grp = t >> 5;
     const StepLen sl = step_len(a, b);
     const int64_t len = sl.len;
     const int64_t k_eff = step_keff(a, b, len);
-    const int64_t span = (int64_t)a.cps * a.chunk;
+    const int64_t span = (int64_t)a.cps * kChunk;
     const int64_t s0 = (int64_t)s * span;
     if (k_eff == 0 || s0 >= len) return;
     const int64_t s1 = s0 + span < len ? s0 + span : len;
+    const int n_chunks_u = (int)((len + kChunk - 1) / kChunk);
     const int n_splits_u = (int)((len + span - 1) / span);
 
     // the query heads, pre-scaled so exp2 gives exp((q.k) / sqrt(d))
@@ -718,18 +740,54 @@ __device__ __forceinline__ void item_sel(const FusedArgs &a, int u, int s, Smem<
         for (int i = t; i < G * kHeadDim; i += kThreads)
             qf[i] = bf16_to_f32(a.q[((int64_t)b * Hq + kv * G) * kHeadDim + i]) * qscale;
     }
-    wg_wait_geq(a, unit_ctr(a, u, kPlan), 1);
+    wg_wait_geq(a, unit_ctr(a, u, kScan), n_chunks_u);
 
-    // ---- the unit's selection plan and the first D rounds of scores
-    const int32_t *plan = a.sel_plan + (int64_t)u * (2 + 2 * a.n_splits);
+    // ---- the unit histogram and the first D rounds of this split's scores
     const uint16_t *su = a.scores + (int64_t)u * a.sstride;
     uint4 pf[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) pf[d] = load_scores8(su, s0 + (int64_t)d * kSelRound + 8 * t, s1);
-    const int T = ld_dev(plan + 0);
-    const int64_t quota = ld_dev(plan + 1);            // keys of score T to take, lowest index first
-    const int64_t ties_b = ld_dev(plan + 2 + 2 * s);   // score-T keys in earlier chunks
-    const int64_t below_b = ld_dev(plan + 3 + 2 * s);  // below-T keys in earlier chunks
+    {
+        const uint32_t *uhr = a.unit_hist + (int64_t)u * (NB + 1);
+        uint32_t loc[PER];
+        int tsum = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int bin = t * PER + e;
+            loc[e] = bin < NB ? ld_dev(uhr + bin) : 0u;
+            tsum += (int)loc[e];
+        }
+        if (t == 0) {
+            sm.sel.T = NB - 1;
+            sm.sel.below = 0;
+        }
+        int tot;
+        int run = block_excl_scan_256(tsum, sm.sel.scan, &tot);
+        // the cut T: first bin whose cumulative count reaches k_eff (the
+        // counts sum to len >= k_eff); below: the count under T
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int nxt = run + (int)loc[e];
+            if ((int64_t)run < k_eff && (int64_t)nxt >= k_eff) {
+                sm.sel.T = t * PER + e;
+                sm.sel.below = run;
+            }
+            run = nxt;
+        }
+        __syncthreads();
+    }
+    const int T = sm.sel.T;
+    // ---- score-T and below-T keys in the chunks before this split
+    long long tie = 0, lo = 0;
+    for (int cc = t; cc < s * a.cps; cc += kThreads) {
+        const uint32_t *chc = a.chunk_hist + ((int64_t)u * a.n_chunks + cc) * NB;
+        const uint32_t l = T > 0 ? ld_dev(chc + T - 1) : 0u;
+        tie += (long long)ld_dev(chc + T) - l;
+        lo += l;
+    }
+    const int64_t ties_b = block_sum_256(tie, sm.sel.red);
+    const int64_t below_b = block_sum_256(lo, sm.sel.red);
+    const int64_t quota = k_eff - sm.sel.below;  // keys of score T to take, lowest index first
     const int64_t rem_quota = quota - ties_b > 0 ? quota - ties_b : 0;
     int64_t out_pos = below_b + (ties_b < quota ? ties_b : quota);
 
@@ -797,12 +855,11 @@ __device__ __forceinline__ void item_sel(const FusedArgs &a, int u, int s, Smem<
             list_n += sel_tot;
             out_pos += sel_tot;
             ties_acc += tie_tot;
-            if (list_n > kListCap - kSelRound || base + kSelRound >= s1) {
-                attend_list<G>(Ku, Vu, sm.sel.list, list_n, grp, l32, app_row, sm.sel.q, m, l, o);
-                __syncthreads();
-                list_n = 0;
-            }
         }
+        // the batch's selections (at most kListCap) through the attention
+        attend_list<G>(Ku, Vu, sm.sel.list, list_n, grp, l32, app_row, sm.sel.q, m, l, o);
+        __syncthreads();
+        list_n = 0;
     }
 
     // ---- combine the 2 groups of each wave (lanes l32 and l32 + 32), then the 4 waves
@@ -857,37 +914,79 @@ __device__ __forceinline__ void item_sel(const FusedArgs &a, int u, int s, Smem<
     if (t == 0) sm.sel.last = (prev == n_splits_u - 1);
     __syncthreads();
     if (!sm.sel.last) return;
+    // Per split x and head h: weight w = exp2(m_x - M) with M the maximum
+    // over splits; out = sum_x w o_x / sum_x w l_x.  Output pair pr (floats
+    // 2 pr, 2 pr + 1 of the G x 128 block) is thread pr's; its partials are
+    // loaded for up to XB splits at a time, the first batch before the (m, l)
+    // loads so both travel together.
+    constexpr int NPR = G * kHeadDim / 2;
+    constexpr int PPT = (NPR + kThreads - 1) / kThreads;
+    constexpr int XB = 16 / PPT;
     const float *mlb = a.part_ml + (int64_t)u * a.n_splits * G * 2;
-    const float *ob = a.part_o + (int64_t)u * a.n_splits * G * kHeadDim;
-    for (int i = t; i < n_splits_u * G; i += kThreads) sm.sel.mw[i / G][i % G] = ld_dev(mlb + 2 * i);
+    const uint64_t *ob = reinterpret_cast<const uint64_t *>(a.part_o + (int64_t)u * a.n_splits * G * kHeadDim);
+    const int n = n_splits_u;
+    uint64_t ov[PPT][XB];
+#pragma unroll
+    for (int k = 0; k < PPT; ++k)
+#pragma unroll
+        for (int x = 0; x < XB; ++x) {
+            const int pr = t + k * kThreads;
+            ov[k][x] = (pr < NPR && x < n) ? ld_dev(ob + (int64_t)x * NPR + pr) : 0ull;
+        }
+    for (int i = t; i < n * G; i += kThreads) {
+        sm.sel.mw[i / G][i % G] = ld_dev(mlb + 2 * i);
+        sm.sel.lv[i / G][i % G] = ld_dev(mlb + 2 * i + 1);
+    }
     __syncthreads();
     if (t < G) {
         float M = -INFINITY;
-        for (int x = 0; x < n_splits_u; ++x) M = fmaxf(M, sm.sel.mw[x][t]);
+        for (int x = 0; x < n; ++x) M = fmaxf(M, sm.sel.mw[x][t]);
         float L = 0.f;
-        for (int x = 0; x < n_splits_u; ++x) {
+        for (int x = 0; x < n; ++x) {
             const float ms = sm.sel.mw[x][t];
-            const float w8 = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-            sm.sel.mw[x][t] = w8;
-            L = fmaf(ld_dev(mlb + (x * G + t) * 2 + 1), w8, L);
+            const float wx = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+            sm.sel.mw[x][t] = wx;
+            L = fmaf(sm.sel.lv[x][t], wx, L);
         }
         sm.sel.ml[t] = L;
     }
     __syncthreads();
-    for (int pr = t; pr < G * kHeadDim; pr += kThreads) {
-        const int h = pr / kHeadDim;
-        float O = 0.f;
-        int x = 0;
-        for (; x + 8 <= n_splits_u; x += 8) {
-            float v[8];
+    float O[PPT][2];
 #pragma unroll
-            for (int y = 0; y < 8; ++y) v[y] = ld_dev(ob + (int64_t)(x + y) * G * kHeadDim + pr);
+    for (int k = 0; k < PPT; ++k) O[k][0] = O[k][1] = 0.f;
+    for (int x0 = 0; x0 < n; x0 += XB) {
+        if (x0 > 0) {
 #pragma unroll
-            for (int y = 0; y < 8; ++y) O = fmaf(v[y], sm.sel.mw[x + y][h], O);
+            for (int k = 0; k < PPT; ++k)
+#pragma unroll
+                for (int x = 0; x < XB; ++x) {
+                    const int pr = t + k * kThreads;
+                    ov[k][x] = (pr < NPR && x0 + x < n) ? ld_dev(ob + (int64_t)(x0 + x) * NPR + pr) : 0ull;
+                }
         }
-        for (; x < n_splits_u; ++x) O = fmaf(ld_dev(ob + (int64_t)x * G * kHeadDim + pr), sm.sel.mw[x][h], O);
-        const float L = sm.sel.ml[h];
-        a.out[((int64_t)b * Hq + kv * G) * kHeadDim + pr] = L > 0.f ? f32_to_bf16(O / L) : (uint16_t)0;
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int h = (2 * (t + k * kThreads)) / kHeadDim;
+#pragma unroll
+            for (int x = 0; x < XB; ++x) {
+                if (x0 + x < n && t + k * kThreads < NPR) {
+                    const float wx = sm.sel.mw[x0 + x][h];
+                    O[k][0] = fmaf(__uint_as_float((uint32_t)ov[k][x]), wx, O[k][0]);
+                    O[k][1] = fmaf(__uint_as_float((uint32_t)(ov[k][x] >> 32)), wx, O[k][1]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int pr = t + k * kThreads;
+        if (pr < NPR) {
+            const int h = (2 * pr) / kHeadDim;
+            const float L = sm.sel.ml[h];
+            uint16_t *o = a.out + ((int64_t)b * Hq + kv * G) * kHeadDim + 2 * pr;
+            o[0] = L > 0.f ? f32_to_bf16(O[k][0] / L) : (uint16_t)0;
+            o[1] = L > 0.f ? f32_to_bf16(O[k][1] / L) : (uint16_t)0;
+        }
     }
     __syncthreads();
 }
@@ -899,8 +998,11 @@ struct Item {
     int u, i;
 };
 
-// PRO(u, p) for every unit and part; then for blocks x = 0 .. U+lag-1:
-// SCAN(x, *) if x < U, and SEL(x - lag, *) if x >= lag.
+// PRO(u, p) for every unit and part; then for x = 0 .. U + lag - 1 the
+// SCAN(x, *) items if x < U followed by the SEL(x - lag, *) items if
+// x >= lag.  The dispatcher starts workgroups in this order as slots free
+// up, so the scan front moves through the units in order and the
+// selection of unit u runs while the units after u + lag are scanned.
 __device__ __forceinline__ Item item_of(const FusedArgs &a, int tk) {
     const int U = a.B * a.Hkv, C = a.n_chunks, S = a.n_splits;
     const int lag = a.lag < U ? a.lag : U;
@@ -915,8 +1017,8 @@ __device__ __forceinline__ Item item_of(const FusedArgs &a, int tk) {
         return it;
     }
     r -= lag * C;
-    const int midblocks = U - lag;
-    if (r < midblocks * (C + S)) {
+    const int mid = U - lag;
+    if (r < mid * (C + S)) {
         const int blk = r / (C + S), off = r % (C + S);
         if (off < C) {
             it.kind = 1; it.u = lag + blk; it.i = off;
@@ -925,27 +1027,9 @@ __device__ __forceinline__ Item item_of(const FusedArgs &a, int tk) {
         }
         return it;
     }
-    r -= midblocks * (C + S);
-    it.kind = 2; it.u = midblocks + r / S; it.i = r % S;
+    r -= mid * (C + S);
+    it.kind = 2; it.u = mid + r / S; it.i = r % S;
     return it;
-}
-
-// Every item counts itself finished.  The last item of a unit resets the
-// unit's counters and counts the unit done for its batch entry; the last
-// unit of an entry publishes the new length and resets the entry counter.
-__device__ __forceinline__ void item_finish(const FusedArgs &a, int u) {
-    __syncthreads();
-    if (threadIdx.x != 0) return;
-    drain_memory();
-    const int per_unit = kProParts + a.n_chunks + a.n_splits;
-    if (add_dev(unit_ctr(a, u, kFin), 1) != per_unit - 1) return;
-    const int b = u / a.Hkv;
-    for (int w = 0; w < 5; ++w) st_dev(unit_ctr(a, u, w), 0);
-    drain_memory();
-    if (add_dev(batch_ctr(a, b), 1) != a.Hkv - 1) return;
-    const StepLen sl = step_len(a, b);
-    if (sl.app) st_dev(a.seq_len + b, (int32_t)(sl.l0 + 1));
-    st_dev(batch_ctr(a, b), 0);
 }
 
 template <int G>
@@ -955,7 +1039,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
     if (it.kind == 0) item_pro<G>(a, it.u, it.i, sm);
     else if (it.kind == 1) item_scan<G>(a, it.u, it.i, sm);
     else item_sel<G>(a, it.u, it.i, sm);
-    item_finish(a, it.u);
+    __syncthreads();
+    if (threadIdx.x == 0) unit_finish(a, it.u);
 }
 
 // ---------------------------------------------------------------- plan + launch
@@ -975,32 +1060,29 @@ bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, DecodePlan *p) {
     d.G = G;
     d.NB = G * kBits + 1;
     d.max_ctx = max_ctx;
-    // Scan items: the largest chunk (8192 down to 1024 keys) that still gives
-    // at least 512 of them; selection splits: about 512 as well (at most 64
-    // per unit, the merge width).
-    int chunk = kMaxChunk;
-    while (chunk > 1024 && units * ((max_ctx + chunk - 1) / chunk) < 512) chunk >>= 1;
-    d.chunk = chunk;
-    d.n_chunks = (int)((max_ctx + chunk - 1) / chunk);
-    if (d.n_chunks < 1) d.n_chunks = 1;
-    int64_t cps = (units * d.n_chunks) / 512;
-    if (cps < 1) cps = 1;
-    if (cps > d.n_chunks) cps = d.n_chunks;
-    if ((d.n_chunks + cps - 1) / cps > 64) cps = (d.n_chunks + 63) / 64;
-    d.cps = (int)cps;
-    d.n_splits = (int)((d.n_chunks + cps - 1) / cps);
-    d.sstride = ((max_ctx + 63) / 64) * 64;
-    const int64_t items = units * (kProParts + d.n_chunks + d.n_splits);
+    d.chunk = kChunk;
+    const int64_t C = max_ctx > 0 ? (max_ctx + kChunk - 1) / kChunk : 1;
+    // selection splits: kMinCps chunks each, more when a unit would get
+    // more than kMaxSplits of them
+    int64_t cps = (C + kMaxSplits - 1) / kMaxSplits;
+    if (cps < kMinCps) cps = kMinCps;
+    if (cps > C) cps = C;
+    const int64_t NS = (C + cps - 1) / cps;
+    const int64_t items = units * (kProParts + C + NS);
     if (items > INT32_MAX / 2) return false;
+    d.n_chunks = (int)C;
+    d.cps = (int)cps;
+    d.n_splits = (int)NS;
+    d.lag = kSelLag;
+    d.n_items = (int)items;
+    d.sstride = ((max_ctx + 63) / 64) * 64;
     size_t off = 0;
     d.off_qcodes = off;
     off = align256(off + (size_t)B * Hq * kWords * 4);
     d.off_unit_hist = off;
-    off = align256(off + (size_t)units * d.NB * 4);
+    off = align256(off + (size_t)units * (d.NB + 1) * 4);
     d.off_chunk_hist = off;
     off = align256(off + (size_t)units * d.n_chunks * d.NB * 4);
-    d.off_sel_plan = off;
-    off = align256(off + (size_t)units * (2 + 2 * d.n_splits) * 4);
     d.off_part_ml = off;
     off = align256(off + (size_t)units * d.n_splits * G * 2 * 4);
     d.off_part_o = off;
@@ -1014,8 +1096,7 @@ bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, DecodePlan *p) {
 
 template <int G>
 static hipError_t launch_g(const DecodePlan &p, FusedArgs &a, hipStream_t s) {
-    // Every selection item is queued behind every scan item.
-    a.lag = p.B * p.Hkv;
+    (void)p;
     hipLaunchKernelGGL(k_decode_fused<G>, dim3(a.n_items), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
@@ -1045,19 +1126,17 @@ hipError_t launch_decode(const DecodePlan &p, uint16_t *k_cache, uint16_t *v_cac
     a.qcodes = reinterpret_cast<uint32_t *>(base + p.off_qcodes);
     a.unit_hist = reinterpret_cast<uint32_t *>(base + p.off_unit_hist);
     a.chunk_hist = reinterpret_cast<uint32_t *>(base + p.off_chunk_hist);
-    a.sel_plan = reinterpret_cast<int32_t *>(base + p.off_sel_plan);
     a.part_ml = reinterpret_cast<float *>(base + p.off_part_ml);
     a.part_o = reinterpret_cast<float *>(base + p.off_part_o);
     a.max_ctx = p.max_ctx;
     a.B = p.B;
     a.Hkv = p.Hkv;
     a.k_max = k_max;
-    a.chunk = p.chunk;
     a.n_chunks = p.n_chunks;
     a.cps = p.cps;
     a.n_splits = p.n_splits;
-    a.lag = 1;
-    a.n_items = p.B * p.Hkv * (kProParts + p.n_chunks + p.n_splits);
+    a.lag = p.lag;
+    a.n_items = p.n_items;
     switch (p.G) {
         case 1: return launch_g<1>(p, a, s);
         case 2: return launch_g<2>(p, a, s);
