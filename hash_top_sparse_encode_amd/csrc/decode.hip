@@ -50,14 +50,9 @@
 namespace hata {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 4096;       // keys per scan item: 16 per thread
-constexpr int kRuns = kChunk / kThreads;
-#ifndef HATA_SEL_LAG
-#define HATA_SEL_LAG (1 << 20)
-#endif
-constexpr int kSelLag = HATA_SEL_LAG;  // SEL items of unit u follow the SCAN items of unit u + lag
-constexpr int kMinCps = 2;         // scan chunks per selection split, at least
-constexpr int kMaxSplits = 64;     // selection splits per unit, at most (the merge width)
+constexpr int kSpanUnit = 8192;    // a work item's span of keys is a multiple of this
+constexpr int kSub = 4;            // keys per thread in one sub-batch of code loads (1024 per workgroup)
+constexpr int kMaxSplits = 64;     // work items per unit, at most (the merge width)
 constexpr int kSelRound = 2048;    // 8 scores per thread per selection round
 constexpr int kSelRounds = 4;      // selection rounds per batch (scores prefetched together)
 constexpr int kListCap = kSelRounds * kSelRound;  // selected indices buffered in LDS
@@ -67,6 +62,8 @@ constexpr uint16_t kNoScore = 0xFFFF;
 
 typedef float fvec4 __attribute__((ext_vector_type(4)));
 typedef uint32_t uvec4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // PRO work per unit is split over this many workgroups (32 code bits each)
 constexpr int kProParts = 4;
@@ -98,7 +95,8 @@ struct FusedArgs {
     int64_t max_ctx;
     int64_t sstride;
     int B, Hkv, k_max;
-    int n_chunks, cps, n_splits, lag;
+    int64_t span;            // keys per work item
+    int n_chunks;            // work items per unit
     int n_items;
 };
 
@@ -208,17 +206,25 @@ __device__ __forceinline__ void unpack_bf16x4(uint64_t r, float (&f)[4]) {
 
 // ---------------------------------------------------------------- shared memory
 
+// A work item's two phases share memory.  Both begin with the span's scores
+// (kept in LDS between the phases when the span is kSpanUnit keys).
 template <int G>
 struct SmemScan {
     static constexpr int NB = G * kBits + 1;
-    uint32_t hist[4][NB];
+    // sub-histograms: each wave counts into NH / 4 of them by lane, which
+    // keeps equal scores of one instruction apart (LDS atomics on one address
+    // serialise)
+    static constexpr int NH = G <= 4 ? 16 : 8;
+    uint16_t scores[kSpanUnit];
+    uint32_t hist[NH][NB];
     int scan[4];
 };
 
 template <int G>
 struct SmemSel {
-    int list[kListCap];
-    float4 q[G][kHeadDim / 4];  // pre-scaled query heads
+    uint16_t scores[kSpanUnit];
+    uint16_t list[kListCap];  // selected keys of a batch, as offsets from its first key
+    float pb[4][32 * G];      // per wave: softmax numerators of its 32 keys of a round
     float wm[4][G];
     float wl[4][G];
     float wo[4][G][kHeadDim];
@@ -226,6 +232,7 @@ struct SmemSel {
     float lv[kMaxSplits][G];  // merge: per-split sums
     float ml[G];
     int scan[8];
+    int weq[4], wlt[4];  // per-wave counts of score-T and below-T keys in a batch
     long long red[4];
     int T, below, last;
 };
@@ -403,7 +410,7 @@ __device__ __forceinline__ int group_hamming(const uvec4 &k, const uint32_t (&qc
     return s;
 }
 
-// Chunk c of unit u: keys [c kChunk, min((c + 1) kChunk, len)).
+// Work item c of unit u: keys [c span, min((c + 1) span, len)).
 struct Slot {
     int u, c;
     int64_t p0, p1;  // key range, empty if p0 >= p1
@@ -415,34 +422,32 @@ __device__ __forceinline__ Slot slot_of(const FusedArgs &a, int u, int c) {
     s.u = u;
     s.c = c;
     s.sl = step_len(a, s.u / a.Hkv);
-    s.p0 = (int64_t)s.c * kChunk;
-    s.p1 = s.p0 + kChunk < s.sl.len ? s.p0 + kChunk : s.sl.len;
+    s.p0 = (int64_t)s.c * a.span;
+    s.p1 = s.p0 + a.span < s.sl.len ? s.p0 + a.span : s.sl.len;
     return s;
 }
 
-// Issue a chunk's 16-byte code loads (thread t: keys p0 + 256 r + t, r <
-// kRuns: each instruction reads 1 KB per wave, contiguous) and, in thread
-// 0, a poll of the unit's PRO counter that returns right behind them.
-__device__ __forceinline__ void slot_issue(const FusedArgs &a, const Slot &s, uvec4 (&buf)[kRuns],
-                                           int &poll) {
+// Issue the 16-byte code loads of sub-batch sb of a chunk (thread t: keys
+// p0 + 256 (kSub sb + r) + t, r < kSub: each instruction reads 1 KB per
+// wave, contiguous).
+__device__ __forceinline__ void slot_issue(const FusedArgs &a, const Slot &s, int sb,
+                                           uvec4 (&buf)[kSub]) {
     const int t = threadIdx.x;
     const uvec4 *kc = reinterpret_cast<const uvec4 *>(a.codes) + (int64_t)s.u * a.max_ctx;
 #pragma unroll
-    for (int r = 0; r < kRuns; ++r) {
-        const int64_t i = s.p0 + r * kThreads + t;
+    for (int r = 0; r < kSub; ++r) {
+        const int64_t i = s.p0 + (int64_t)(kSub * sb + r) * kThreads + t;
         buf[r] = i < s.p1 ? kc[i] : uvec4{0u, 0u, 0u, 0u};
     }
-    poll = kProParts;
-    if (t == 0 && s.p0 < s.p1) poll = ld_dev(unit_ctr(a, s.u, kPro));
 }
 
 // Wait for the unit's PRO parts (the prefetched poll usually settles it),
 // then issue the loads of the query codes and, where the slot holds the key
 // appended in this launch, of its code.  Nothing waits for these loads here.
 template <int G>
-__device__ __forceinline__ void slot_begin(const FusedArgs &a, const Slot &s, int poll,
-                                           uint64_t (&qraw)[G][2], uint64_t (&app)[2]) {
-    if (threadIdx.x == 0 && poll < kProParts) {
+__device__ __forceinline__ void slot_begin(const FusedArgs &a, const Slot &s, uint64_t (&qraw)[G][2],
+                                           uint64_t (&app)[2]) {
+    if (threadIdx.x == 0 && ld_dev(unit_ctr(a, s.u, kPro)) < kProParts) {
         int spins = 0;
         while (ld_dev(unit_ctr(a, s.u, kPro)) < kProParts) {
             __builtin_amdgcn_s_sleep(2);
@@ -473,14 +478,9 @@ __device__ __forceinline__ void slot_begin(const FusedArgs &a, const Slot &s, in
     }
 }
 
-// Scores of the chunk's keys: lane pairs store two to a 32-bit word; every
-// score is counted into its wave's LDS histogram.
+// Query codes from their (uniform) loaded words into scalar registers.
 template <int G>
-__device__ __forceinline__ void slot_score(const FusedArgs &a, const Slot &s, const uvec4 (&buf)[kRuns],
-                                           const uint64_t (&qraw)[G][2], const uint64_t (&app)[2],
-                                           Smem<G> &sm) {
-    const int t = threadIdx.x, wv = t >> 6;
-    uint32_t qc[G][4];
+__device__ __forceinline__ void qcodes_sgpr(const uint64_t (&qraw)[G][2], uint32_t (&qc)[G][4]) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         qc[h][0] = __builtin_amdgcn_readfirstlane((uint32_t)qraw[h][0]);
@@ -488,24 +488,39 @@ __device__ __forceinline__ void slot_score(const FusedArgs &a, const Slot &s, co
         qc[h][2] = __builtin_amdgcn_readfirstlane((uint32_t)qraw[h][1]);
         qc[h][3] = __builtin_amdgcn_readfirstlane((uint32_t)(qraw[h][1] >> 32));
     }
+}
+
+// Scores of sub-batch sb, counted into the LDS sub-histograms and kept in
+// LDS (spans of kSpanUnit keys) or stored to the workspace two to a 32-bit
+// word.
+template <int G>
+__device__ __forceinline__ void slot_score(const FusedArgs &a, const Slot &s, int sb,
+                                           const uvec4 (&buf)[kSub], const uint32_t (&qc)[G][4],
+                                           const uint64_t (&app)[2], Smem<G> &sm) {
+    const int t = threadIdx.x, wv = t >> 6;
     const int64_t app_row = s.sl.app ? s.sl.l0 : -1;
     const uvec4 appv = {(uint32_t)app[0], (uint32_t)(app[0] >> 32), (uint32_t)app[1],
                         (uint32_t)(app[1] >> 32)};
-    uint32_t *wh = sm.scan.hist[wv];
+    constexpr int HPW = SmemScan<G>::NH / 4;  // sub-histograms per wave
+    uint32_t *wh = sm.scan.hist[wv * HPW + (t & (HPW - 1))];
     uint16_t *sc = a.scores + (int64_t)s.u * a.sstride;
     uint16_t *sd = a.scores_dbg ? a.scores_dbg + (int64_t)s.u * a.max_ctx : nullptr;
+    const bool in_lds = a.span <= kSpanUnit;
 #pragma unroll
-    for (int r = 0; r < kRuns; ++r) {
-        const int64_t i = s.p0 + r * kThreads + t;
+    for (int r = 0; r < kSub; ++r) {
+        const int64_t i = s.p0 + (int64_t)(kSub * sb + r) * kThreads + t;
         uint32_t sv = kNoScore;
         if (i < s.p1) {
             const uvec4 k = (i == app_row) ? appv : buf[r];
             sv = (uint32_t)group_hamming<G>(k, qc);
             atomicAdd(&wh[sv], 1u);
             if (sd) sd[i] = (uint16_t)sv;
+            if (in_lds) sm.scan.scores[i - s.p0] = (uint16_t)sv;
         }
-        const uint32_t nb = (uint32_t)__shfl_xor((int)sv, 1, 64);
-        if (!(t & 1) && i < s.p1) st_dev(reinterpret_cast<uint32_t *>(sc + i), sv | (nb << 16));
+        if (!in_lds) {
+            const uint32_t nb = (uint32_t)__shfl_xor((int)sv, 1, 64);
+            if (!(t & 1) && i < s.p1) st_dev(reinterpret_cast<uint32_t *>(sc + i), sv | (nb << 16));
+        }
     }
 }
 
@@ -526,12 +541,9 @@ __device__ __forceinline__ void slot_publish(const FusedArgs &a, const Slot &s, 
         const int bin = t * PER + e;
         uint32_t v = 0;
         if (bin < NB) {
-            v = sm.scan.hist[0][bin] + sm.scan.hist[1][bin] + sm.scan.hist[2][bin] +
-                sm.scan.hist[3][bin];
+#pragma unroll
+            for (int h = 0; h < SmemScan<G>::NH; ++h) v += sm.scan.hist[h][bin];
             sm.scan.hist[0][bin] = v;
-            sm.scan.hist[1][bin] = 0u;
-            sm.scan.hist[2][bin] = 0u;
-            sm.scan.hist[3][bin] = 0u;
         }
         loc[e] = v;
         tsum += (int)v;
@@ -563,7 +575,7 @@ __device__ __forceinline__ void slot_publish(const FusedArgs &a, const Slot &s, 
 // entry counter.
 __device__ __forceinline__ void unit_finish(const FusedArgs &a, int u) {
     drain_memory();
-    const int per_unit = kProParts + a.n_chunks + a.n_splits;
+    const int per_unit = kProParts + a.n_chunks;
     if (add_dev(unit_ctr(a, u, kFin), 1) != per_unit - 1) return;
     const int b = u / a.Hkv;
     for (int w = 0; w < kNumCtr; ++w) st_dev(unit_ctr(a, u, w), 0);
@@ -574,29 +586,33 @@ __device__ __forceinline__ void unit_finish(const FusedArgs &a, int u) {
     st_dev(batch_ctr(a, b), 0);
 }
 
-// SCAN(u, c): the chunk's code loads go out first (all 64 KB of them), then
-// the wait for the unit's query codes, the scores, the histograms and the
-// signal.
+// Scan phase of work item (u, c): its span's codes in sub-batches of 16 KB,
+// two in flight at a time; the wait for the unit's query codes sits behind
+// the first two.  Scores go to the workspace, the histograms are published
+// and the unit's scan counter is bumped.
 template <int G>
-__device__ __forceinline__ void item_scan(const FusedArgs &a, int u, int c, Smem<G> &sm) {
+__device__ __forceinline__ void scan_phase(const FusedArgs &a, const Slot &cur, Smem<G> &sm) {
     constexpr int NB = G * kBits + 1;
-    const Slot cur = slot_of(a, u, c);
-    if (cur.p0 >= cur.p1) return;
-    // While the unit's PRO parts are still running, give their W_H loads a
-    // short head start before this chunk's loads join the queues.
-    if (ld_dev(unit_ctr(a, u, kPro)) < kProParts) __builtin_amdgcn_s_sleep(20);
-    uvec4 buf[kRuns];
-    int poll;
-    slot_issue(a, cur, buf, poll);
-    for (int i = threadIdx.x; i < 4 * NB; i += kThreads) (&sm.scan.hist[0][0])[i] = 0u;
+    const int n_sub = (int)((cur.p1 - cur.p0 + kSub * kThreads - 1) / (kSub * kThreads));
+    uvec4 bufA[kSub], bufB[kSub];
+    slot_issue(a, cur, 0, bufA);
+    slot_issue(a, cur, 1, bufB);
+    for (int i = threadIdx.x; i < SmemScan<G>::NH * NB; i += kThreads) (&sm.scan.hist[0][0])[i] = 0u;
     uint64_t qraw[G][2], app[2];
-    slot_begin<G>(a, cur, poll, qraw, app);  // its barrier also orders the clearing
-    slot_score<G>(a, cur, buf, qraw, app, sm);
+    slot_begin<G>(a, cur, qraw, app);  // its barrier also orders the clearing
+    uint32_t qc[G][4];
+    qcodes_sgpr<G>(qraw, qc);
+    for (int sb = 0; sb < n_sub; sb += 2) {
+        slot_score<G>(a, cur, sb, bufA, qc, app, sm);
+        if (sb + 2 < n_sub) slot_issue(a, cur, sb + 2, bufA);
+        slot_score<G>(a, cur, sb + 1, bufB, qc, app, sm);
+        if (sb + 3 < n_sub) slot_issue(a, cur, sb + 3, bufB);
+    }
     slot_publish<G>(a, cur, sm);
-    wg_signal(unit_ctr(a, u, kScan));
+    wg_signal(unit_ctr(a, cur.u, kScan));
 }
 
-// ---------------------------------------------------------------- SEL(u, s)
+// ---------------------------------------------------------------- selection phase
 
 __device__ __forceinline__ void lse_weights(float m1, float m2, float *M, float *a1, float *a2) {
     const float mm = fmaxf(m1, m2);
@@ -605,148 +621,225 @@ __device__ __forceinline__ void lse_weights(float m1, float m2, float *M, float 
     *a2 = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mm);
 }
 
-// Sum over the 32 lanes of a group (two 16-lane rows), every lane gets the
-// total: xor-1 and xor-2 quad permutes, half-row and row mirrors, then the
-// other row.
-__device__ __forceinline__ float group32_sum(float v) {
+// All-reduce over the 16 lanes of a row (lanes 16 g .. 16 g + 15): xor-1 and
+// xor-2 quad permutes, then the half-row and row mirrors.
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
-    v += __shfl_xor(v, 16, 32);
     return v;
 }
 
-__device__ __forceinline__ uint64_t load_row8(const uint16_t *row, int l32, bool coherent) {
-    const uint64_t *p = reinterpret_cast<const uint64_t *>(row) + l32;
-    return coherent ? ld_dev(p) : *p;
-}
-
-// Fold KS already-loaded rows (kr, vr entries [X0, X0 + KS)) into the online
-// softmax state; entries at or past n are padding.
-template <int G, int KL, int KS, int X0>
-__device__ __forceinline__ void attend_block(const uint64_t (&kr)[KL], const uint64_t (&vr)[KL], int j0,
-                                             int n, int l32, const float4 (*qs)[kHeadDim / 4],
-                                             float (&m)[G], float (&l)[G], float (&o)[G][4]) {
-    float z[KS][G];
-#pragma unroll
-    for (int x = 0; x < KS; ++x) {
-        float kf[4];
-        unpack_bf16x4(kr[X0 + x], kf);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float4 q = qs[h][l32];
-            float d = q.x * kf[0];
-            d = fmaf(q.y, kf[1], d);
-            d = fmaf(q.z, kf[2], d);
-            z[x][h] = fmaf(q.w, kf[3], d);
-        }
-    }
-#pragma unroll
-    for (int x = 0; x < KS; ++x)
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-            z[x][h] = (j0 + 8 * (X0 + x) < n) ? group32_sum(z[x][h]) : -INFINITY;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float mx = z[0][h];
-#pragma unroll
-        for (int x = 1; x < KS; ++x) mx = fmaxf(mx, z[x][h]);
-        const float mn = fmaxf(m[h], mx);
-        if (mn == -INFINITY) continue;  // the whole block is padding
-        const float al = exp2f(m[h] - mn);
-        float lsum = 0.f;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int x = 0; x < KS; ++x) {
-            const float p = exp2f(z[x][h] - mn);  // 0 for the padding entries
-            float vf[4];
-            unpack_bf16x4(vr[X0 + x], vf);
-            lsum += p;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
-        }
-        l[h] = fmaf(l[h], al, lsum);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[h][e] = fmaf(o[h][e], al, acc[e]);
-        m[h] = mn;
-    }
-}
-
-// Attend over list[0..n): 8 groups of 32 lanes; group g takes the entries
-// g, g + 8, g + 16, ...  Lane l32 holds dims [4 l32, 4 l32 + 4) of each row.
-// KL rows per group are loaded before any is used, then folded in blocks of
-// KS whose KS x G logits are reduced together (online softmax in base 2; the
-// query heads in LDS are pre-scaled by log2(e) / sqrt(128)).  The row
-// appended in this launch (app_row) is read through the coherent path.
+// The query heads as the A operand of v_mfma_f32_16x16x32_bf16: lane l holds
+// row l % 16 (head; zero for heads >= G) and, for MFMA j, dims
+// 32 (l / 16) + 8 j .. + 8 (the same dims its B operand brings for a key).
 template <int G>
-__device__ __forceinline__ void attend_list(const uint16_t *__restrict__ Ku,
-                                            const uint16_t *__restrict__ Vu, const int *list,
-                                            int n, int grp, int l32, int64_t app_row,
-                                            const float4 (*qs)[kHeadDim / 4], float (&m)[G],
-                                            float (&l)[G], float (&o)[G][4]) {
-    constexpr int KL = 8;  // rows in flight per lane group (registers: 4 per row)
-    constexpr int KS = 4;
-    for (int j0 = grp; j0 < n; j0 += 8 * KL) {
-        uint64_t kr[KL], vr[KL];
+__device__ __forceinline__ void load_q_operand(const uint16_t *qg, bf16x8 (&qa)[4]) {
+    const int lane = threadIdx.x & 63, h = lane & 15, grp = lane >> 4;
 #pragma unroll
-        for (int x = 0; x < KL; ++x) {
-            const int jj = j0 + 8 * x;
-            kr[x] = 0;
-            vr[x] = 0;
-            if (jj < n) {
-                const int idx = list[jj];
-                const bool coh = idx == app_row;
-                kr[x] = load_row8(Ku + (int64_t)idx * kHeadDim, l32, coh);
-                vr[x] = load_row8(Vu + (int64_t)idx * kHeadDim, l32, coh);
+    for (int j = 0; j < 4; ++j) {
+        uvec4 v = {0u, 0u, 0u, 0u};
+        if (h < G) v = *reinterpret_cast<const uvec4 *>(qg + h * kHeadDim + 32 * grp + 8 * j);
+        qa[j] = __builtin_bit_cast(bf16x8, v);
+    }
+}
+
+// Attention over the rows Kb / Vb + list[0..n) (offsets from a batch's first
+// key; the row at offset app_off is this step's appended key, read from
+// kapp / vapp).  Each wave takes 32 keys of every 128: logits of two 16-key
+// tiles by MFMA (lane (g, c) brings dims 32 g .. 32 g + 32 of key c of a
+// tile; its accumulator holds heads 4 g .. 4 g + 3 of key c), an online
+// softmax in base 2 per head (running m, l per lane for its four heads), and
+// P.V on the vector units with every lane holding dims 2 lane, 2 lane + 1 of
+// each row.  Loads of a round are all issued before any is used.
+template <int G>
+__device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
+                                            const uint16_t *__restrict__ Vb,
+                                            const uint16_t *__restrict__ kapp,
+                                            const uint16_t *__restrict__ vapp, int app_off,
+                                            const uint16_t *list, int n, const bf16x8 (&qa)[4],
+                                            float *pw, float (&m)[4], float (&lsum)[4],
+                                            float (&o)[G][2]) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, grp = lane >> 4, c = lane & 15;
+    constexpr float kScale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
+    for (int base = 32 * wv; base < n; base += 128) {
+        const int kc = n - base < 32 ? n - base : 32;
+        // K rows: key 16 tau + c, dims 32 grp .. +32
+        uvec4 kr[2][4];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            const int kk = 16 * tau + c;
+            const int off = kk < kc ? (int)list[base + kk] : -1;
+            const uint16_t *row = off == app_off ? kapp : Kb + off * kHeadDim;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                kr[tau][j] = uvec4{0u, 0u, 0u, 0u};
+                if (off >= 0) kr[tau][j] = *reinterpret_cast<const uvec4 *>(row + 32 * grp + 8 * j);
             }
         }
-        attend_block<G, KL, KS, 0>(kr, vr, j0, n, l32, qs, m, l, o);
-        if (j0 + 8 * KS < n) attend_block<G, KL, KS, KS>(kr, vr, j0, n, l32, qs, m, l, o);
-        static_assert(KL == 2 * KS, "two logit blocks per load round");
+        // V rows: dims 2 lane, 2 lane + 1 of each of the kc keys
+        const int offl = lane < kc ? (int)list[base + lane] : -1;
+        uint32_t vr[32];
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            vr[k] = 0u;
+            const int off = __builtin_amdgcn_readlane(offl, k);
+            if (k < kc) {
+                const uint16_t *row = off == app_off ? vapp : Vb + off * kHeadDim;
+                vr[k] = *reinterpret_cast<const uint32_t *>(row + 2 * lane);
+            }
+        }
+        // logits
+        f32x4 acc[2];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            acc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], __builtin_bit_cast(bf16x8, kr[tau][j]),
+                                                                   acc[tau], 0, 0, 0);
+        }
+        // online softmax for this lane's heads 4 grp + i
+        float alv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool hv = 4 * grp + i < G;
+            const float z0 = (hv && c < kc) ? acc[0][i] * kScale : -INFINITY;
+            const float z1 = (hv && 16 + c < kc) ? acc[1][i] * kScale : -INFINITY;
+            const float M = fmaxf(m[i], row16_max(fmaxf(z0, z1)));
+            const float al = (M == -INFINITY) ? 1.f : exp2f(m[i] - M);
+            const float p0 = (z0 == -INFINITY) ? 0.f : exp2f(z0 - M);
+            const float p1 = (z1 == -INFINITY) ? 0.f : exp2f(z1 - M);
+            lsum[i] = lsum[i] * al + row16_sum(p0 + p1);
+            m[i] = M;
+            alv[i] = al;
+            if (hv) {
+                pw[c * G + 4 * grp + i] = p0;
+                pw[(16 + c) * G + 4 * grp + i] = p1;
+            }
+        }
+        // rescale the accumulators (head h's factor lives in lane 16 (h / 4))
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float al =
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alv[h & 3]), 16 * (h >> 2)));
+            o[h][0] *= al;
+            o[h][1] *= al;
+        }
+        // P.V
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            if (k < kc) {
+                const float v0 = __uint_as_float(vr[k] << 16), v1 = __uint_as_float(vr[k] & 0xFFFF0000u);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float pk = pw[k * G + h];
+                    o[h][0] = fmaf(pk, v0, o[h][0]);
+                    o[h][1] = fmaf(pk, v1, o[h][1]);
+                }
+            }
+        }
     }
 }
 
-// 8 consecutive scores from the workspace (aligned), kNoScore past s1.
-__device__ __forceinline__ uint4 load_scores8(const uint16_t *su, int64_t i0, int64_t s1) {
-    if (i0 >= s1) return make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
-    const uint64_t *p = reinterpret_cast<const uint64_t *>(su + i0);
-    const uint64_t lo = ld_dev(p);
-    const uint64_t hi = (i0 + 4 < s1) ? ld_dev(p + 1) : ~0ull;
+// Exclusive prefix sum over the lanes of a wave for 0 <= v < 16 (bit-plane
+// ballots counted below each lane); *total gets the wave's sum.
+__device__ __forceinline__ int wave_excl_scan16(int v, int *total) {
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint64_t m = __ballot((v >> b) & 1);
+        pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0)) << b;
+        tot += __popcll(m) << b;
+    }
+    *total = tot;
+    return pre;
+}
+
+// Sum over the lanes of a wave for 0 <= v < 64.
+__device__ __forceinline__ int wave_sum64(int v) {
+    int tot = 0;
+#pragma unroll
+    for (int b = 0; b < 6; ++b) tot += __popcll(__ballot((v >> b) & 1)) << b;
+    return tot;
+}
+
+// Score e (0..7) of eight packed u16 scores.
+__device__ __forceinline__ int score_at(const uint4 &v, int e) {
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    return (e & 1) ? (int)(w >> 16) : (int)(w & 0xFFFF);
+}
+
+// 8 consecutive scores from LDS at offset o (aligned); offsets at or past n
+// read as kNoScore.
+__device__ __forceinline__ uint4 lds_scores8(const uint16_t *sc, int o, int64_t n) {
+    if (o >= n) return make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
+    const uint4 v = *reinterpret_cast<const uint4 *>(sc + o);
+    uint64_t lo = (uint64_t)v.x | ((uint64_t)v.y << 32), hi = (uint64_t)v.z | ((uint64_t)v.w << 32);
+    const int64_t nv = n - o;
+    if (nv < 4) lo |= ~0ull << (16 * nv);
+    if (nv < 8) hi |= nv <= 4 ? ~0ull : ~0ull << (16 * (nv - 4));
     return make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
 }
 
+// 8 consecutive scores from the workspace (aligned); keys at or past s1
+// read as kNoScore.
+__device__ __forceinline__ uint4 load_scores8(const uint16_t *su, int64_t i0, int64_t s1) {
+    if (i0 >= s1) return make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
+    const uint64_t *p = reinterpret_cast<const uint64_t *>(su + i0);
+    uint64_t lo = ld_dev(p);
+    uint64_t hi = (i0 + 4 < s1) ? ld_dev(p + 1) : ~0ull;
+    const int64_t nv = s1 - i0;  // valid keys among the eight
+    if (nv < 4) lo |= ~0ull << (16 * nv);
+    else if (nv < 8) hi |= ~0ull << (16 * (nv - 4));
+    return make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+}
+
+// Selection phase of work item (u, c), once every item of the unit has
+// scanned: the cut T from the unit histogram, the score-T and below-T keys
+// of the items before it from their cumulative histograms, then the span's
+// selected keys compacted in index order (in batches of kListCap keys),
+// gathered and attended; the (m, l, o) partials of the items are merged in
+// item order by the last one.
 template <int G>
-__device__ __forceinline__ void item_sel(const FusedArgs &a, int u, int s, Smem<G> &sm) {
+__device__ __forceinline__ void sel_phase(const FusedArgs &a, const Slot &cur, Smem<G> &sm) {
     constexpr int D = kSelRounds;  // selection rounds of scores in flight
     constexpr int NB = G * kBits + 1;
     constexpr int PER = (NB + kThreads - 1) / kThreads;
+    const int u = cur.u, s = cur.c;
     const int b = u / a.Hkv, kv = u % a.Hkv, Hq = a.Hkv * G;
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, l32 = t & 31, grp = t >> 5;
-    const StepLen sl = step_len(a, b);
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const StepLen sl = cur.sl;
     const int64_t len = sl.len;
     const int64_t k_eff = step_keff(a, b, len);
-    const int64_t span = (int64_t)a.cps * kChunk;
-    const int64_t s0 = (int64_t)s * span;
-    if (k_eff == 0 || s0 >= len) return;
-    const int64_t s1 = s0 + span < len ? s0 + span : len;
-    const int n_chunks_u = (int)((len + kChunk - 1) / kChunk);
-    const int n_splits_u = (int)((len + span - 1) / span);
+    const int64_t s0 = cur.p0, s1 = cur.p1;
+    if (k_eff == 0) return;
+    const int n_splits_u = (int)((len + a.span - 1) / a.span);
 
-    // the query heads, pre-scaled so exp2 gives exp((q.k) / sqrt(d))
-    {
-        const float qscale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
-        float *qf = &sm.sel.q[0][0].x;
-        for (int i = t; i < G * kHeadDim; i += kThreads)
-            qf[i] = bf16_to_f32(a.q[((int64_t)b * Hq + kv * G) * kHeadDim + i]) * qscale;
-    }
-    wg_wait_geq(a, unit_ctr(a, u, kScan), n_chunks_u);
+    // the query heads as MFMA operands
+    bf16x8 qa[4];
+    load_q_operand<G>(a.q + ((int64_t)b * Hq + kv * G) * kHeadDim, qa);
+    wg_wait_geq(a, unit_ctr(a, u, kScan), n_splits_u);
 
     // ---- the unit histogram and the first D rounds of this split's scores
     const uint16_t *su = a.scores + (int64_t)u * a.sstride;
+    // batch layout: wave w holds keys [rb + 2048 w, rb + 2048 (w + 1)), lane
+    // `lane` of it keys rb + 2048 w + 512 d + 8 lane + e (d < D, e < 8)
+    const int64_t woff = (int64_t)wv * (kSelRounds * kSelRound / 4) + 8 * lane;
+    const bool in_lds = a.span <= kSpanUnit;
     uint4 pf[D];
 #pragma unroll
-    for (int d = 0; d < D; ++d) pf[d] = load_scores8(su, s0 + (int64_t)d * kSelRound + 8 * t, s1);
+    for (int d = 0; d < D; ++d)
+        pf[d] = in_lds ? lds_scores8(sm.sel.scores, woff + d * 512, s1 - s0)
+                       : load_scores8(su, s0 + woff + (int64_t)d * 512, s1);
     {
         const uint32_t *uhr = a.unit_hist + (int64_t)u * (NB + 1);
         uint32_t loc[PER];
@@ -779,7 +872,7 @@ __device__ __forceinline__ void item_sel(const FusedArgs &a, int u, int s, Smem<
     const int T = sm.sel.T;
     // ---- score-T and below-T keys in the chunks before this split
     long long tie = 0, lo = 0;
-    for (int cc = t; cc < s * a.cps; cc += kThreads) {
+    for (int cc = t; cc < s; cc += kThreads) {
         const uint32_t *chc = a.chunk_hist + ((int64_t)u * a.n_chunks + cc) * NB;
         const uint32_t l = T > 0 ? ld_dev(chc + T - 1) : 0u;
         tie += (long long)ld_dev(chc + T) - l;
@@ -795,102 +888,118 @@ __device__ __forceinline__ void item_sel(const FusedArgs &a, int u, int s, Smem<
     const uint16_t *Ku = a.k_cache + (int64_t)u * a.max_ctx * kHeadDim;
     const uint16_t *Vu = a.v_cache + (int64_t)u * a.max_ctx * kHeadDim;
     const int64_t app_row = sl.app ? sl.l0 : -1;
-    float m[G], l[G], o[G][4];
+    const uint16_t *kapp = sl.app ? a.k_new + ((int64_t)b * a.Hkv + kv) * kHeadDim : nullptr;
+    const uint16_t *vapp = sl.app ? a.v_new + ((int64_t)b * a.Hkv + kv) * kHeadDim : nullptr;
+    float m[4], l[4], o[G][2];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[h][e] = 0.f;
+    for (int i = 0; i < 4; ++i) {
+        m[i] = -INFINITY;
+        l[i] = 0.f;
     }
+#pragma unroll
+    for (int h = 0; h < G; ++h) o[h][0] = o[h][1] = 0.f;
     int64_t ties_acc = 0;
-    int list_n = 0;
-    for (int64_t rb = s0; rb < s1; rb += D * kSelRound) {
+    for (int64_t rb = s0; rb < s1; rb += kListCap) {
+        // pass 1: this wave's score-T and below-T counts (past s1 the words
+        // read as kNoScore, which is above every T)
+        int n_eq = 0, n_lt = 0;
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sv = score_at(pf[d], e);
+                n_eq += sv == T;
+                n_lt += sv < T;
+            }
+        {
+            const int weq = wave_sum64(n_eq), wlt = wave_sum64(n_lt);
+            if (lane == 0) {
+                sm.sel.weq[wv] = weq;
+                sm.sel.wlt[wv] = wlt;
+            }
+        }
+        __syncthreads();
+        // this wave's place in the batch: ties and selections of the waves before it
+        int64_t tie_base = ties_acc;
+        int sel_base = 0, batch_sel = 0, batch_eq = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+            const int e2 = sm.sel.weq[w2], l2 = sm.sel.wlt[w2];
+            const int64_t tb = ties_acc + batch_eq;
+            int64_t take = rem_quota - tb;
+            take = take < 0 ? 0 : (take > e2 ? e2 : take);
+            const int sw = l2 + (int)take;
+            if (w2 < wv) {
+                tie_base += e2;
+                sel_base += sw;
+            }
+            batch_eq += e2;
+            batch_sel += sw;
+        }
+        // pass 2: select in index order (d, lane, e) and write the list
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const int64_t base = rb + (int64_t)d * kSelRound;
-            if (base >= s1) break;
-            const int64_t i0 = base + (int64_t)t * 8;
-            const uint4 now = pf[d];
-            if (base + D * kSelRound < s1) pf[d] = load_scores8(su, i0 + D * kSelRound, s1);
-            int sc[8];
-            sc[0] = now.x & 0xFFFF; sc[1] = now.x >> 16;
-            sc[2] = now.y & 0xFFFF; sc[3] = now.y >> 16;
-            sc[4] = now.z & 0xFFFF; sc[5] = now.z >> 16;
-            sc[6] = now.w & 0xFFFF; sc[7] = now.w >> 16;
-            int n_eq = 0;
+            int ne = 0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) n_eq += (sc[e] == T && i0 + e < s1);
-            int tie_tot;
-            const int tie_pre = block_excl_scan_small(n_eq, sm.sel.scan, 0, &tie_tot);
-            int64_t tr = ties_acc + tie_pre;
+            for (int e = 0; e < 8; ++e) ne += score_at(pf[d], e) == T;
+            int ne_tot;
+            int64_t tr = tie_base + wave_excl_scan16(ne, &ne_tot);
             unsigned selmask = 0;
             int n_sel = 0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                if (i0 + e >= s1) continue;
-                bool take = sc[e] < T;
-                if (sc[e] == T) {
+                const int sv = score_at(pf[d], e);
+                bool take = sv < T;
+                if (sv == T) {
                     take = tr < rem_quota;
                     ++tr;
                 }
-                if (take) {
-                    selmask |= 1u << e;
-                    ++n_sel;
-                }
+                selmask |= (take ? 1u : 0u) << e;
+                n_sel += take;
             }
-            int sel_tot;
-            const int sel_pre = block_excl_scan_small(n_sel, sm.sel.scan, 1, &sel_tot);
-            int p = list_n + sel_pre;
-            int64_t gp = out_pos + sel_pre;
+            int ns_tot;
+            int p = sel_base + wave_excl_scan16(n_sel, &ns_tot);
+            const int o0 = (int)woff + d * 512;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (selmask & (1u << e)) {
-                    sm.sel.list[p++] = (int)(i0 + e);
-                    if (sel_u && gp >= 0 && gp < a.k_max) sel_u[gp] = (int32_t)(i0 + e);
-                    ++gp;
-                }
-            }
-            __syncthreads();
-            list_n += sel_tot;
-            out_pos += sel_tot;
-            ties_acc += tie_tot;
+            for (int e = 0; e < 8; ++e)
+                if (selmask & (1u << e)) sm.sel.list[p++] = (uint16_t)(o0 + e);
+            tie_base += ne_tot;
+            sel_base += ns_tot;
         }
-        // the batch's selections (at most kListCap) through the attention
-        attend_list<G>(Ku, Vu, sm.sel.list, list_n, grp, l32, app_row, sm.sel.q, m, l, o);
+        // the next batch's scores are on their way during this one's attention
+        if (rb + kListCap < s1) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) pf[d] = load_scores8(su, rb + kListCap + woff + (int64_t)d * 512, s1);
+        }
         __syncthreads();
-        list_n = 0;
+        if (sel_u) {
+            for (int i = t; i < batch_sel; i += kThreads) {
+                const int64_t gp = out_pos + i;
+                if (gp >= 0 && gp < a.k_max) sel_u[gp] = (int32_t)(rb + sm.sel.list[i]);
+            }
+        }
+        out_pos += batch_sel;
+        ties_acc += batch_eq;
+        // the batch's selections through the attention
+        const int app_off = (app_row >= rb && app_row < rb + kListCap) ? (int)(app_row - rb) : -1;
+        attend_mfma<G>(Ku + rb * kHeadDim, Vu + rb * kHeadDim, kapp, vapp, app_off, sm.sel.list,
+                       batch_sel, qa, sm.sel.pb[wv], m, l, o);
+        __syncthreads();
     }
 
-    // ---- combine the 2 groups of each wave (lanes l32 and l32 + 32), then the 4 waves
+    // ---- the waves' states into LDS, then combined per output
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        const float m2 = __shfl_xor(m[h], 32, 64);
-        const float l2 = __shfl_xor(l[h], 32, 64);
-        float M, a1, a2;
-        lse_weights(m[h], m2, &M, &a1, &a2);
-        l[h] = l[h] * a1 + l2 * a2;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float o2 = __shfl_xor(o[h][e], 32, 64);
-            o[h][e] = o[h][e] * a1 + o2 * a2;
+        if (lane == 16 * (h >> 2)) {
+            sm.sel.wm[wv][h] = m[h & 3];
+            sm.sel.wl[wv][h] = l[h & 3];
         }
-        m[h] = M;
-    }
-    if (lane < 32) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            if (lane == 0) {
-                sm.sel.wm[wv][h] = m[h];
-                sm.sel.wl[wv][h] = l[h];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sm.sel.wo[wv][h][lane * 4 + e] = o[h][e];
-        }
+        sm.sel.wo[wv][h][2 * lane] = o[h][0];
+        sm.sel.wo[wv][h][2 * lane + 1] = o[h][1];
     }
     __syncthreads();
-    float *pml = a.part_ml + ((int64_t)u * a.n_splits + s) * G * 2;
-    float *po = a.part_o + ((int64_t)u * a.n_splits + s) * G * kHeadDim;
+    float *pml = a.part_ml + ((int64_t)u * a.n_chunks + s) * G * 2;
+    float *po = a.part_o + ((int64_t)u * a.n_chunks + s) * G * kHeadDim;
     for (int pr = t; pr < G * kHeadDim; pr += kThreads) {
         const int h = pr / kHeadDim, e = pr % kHeadDim;
         float M = sm.sel.wm[0][h], L = sm.sel.wl[0][h], O = sm.sel.wo[0][h][e];
@@ -921,9 +1030,9 @@ __device__ __forceinline__ void item_sel(const FusedArgs &a, int u, int s, Smem<
     // loads so both travel together.
     constexpr int NPR = G * kHeadDim / 2;
     constexpr int PPT = (NPR + kThreads - 1) / kThreads;
-    constexpr int XB = 16 / PPT;
-    const float *mlb = a.part_ml + (int64_t)u * a.n_splits * G * 2;
-    const uint64_t *ob = reinterpret_cast<const uint64_t *>(a.part_o + (int64_t)u * a.n_splits * G * kHeadDim);
+    constexpr int XB = 32 / PPT;
+    const float *mlb = a.part_ml + (int64_t)u * a.n_chunks * G * 2;
+    const uint64_t *ob = reinterpret_cast<const uint64_t *>(a.part_o + (int64_t)u * a.n_chunks * G * kHeadDim);
     const int n = n_splits_u;
     uint64_t ov[PPT][XB];
 #pragma unroll
@@ -994,51 +1103,41 @@ __device__ __forceinline__ void item_sel(const FusedArgs &a, int u, int s, Smem<
 // ---------------------------------------------------------------- item order
 
 struct Item {
-    int kind;  // 0 PRO, 1 SCAN, 2 SEL
+    int kind;  // 0 PRO, 1 WORK
     int u, i;
 };
 
-// PRO(u, p) for every unit and part; then for x = 0 .. U + lag - 1 the
-// SCAN(x, *) items if x < U followed by the SEL(x - lag, *) items if
-// x >= lag.  The dispatcher starts workgroups in this order as slots free
-// up, so the scan front moves through the units in order and the
-// selection of unit u runs while the units after u + lag are scanned.
+// PRO(u, p) for every unit and part, then WORK(u, c) unit by unit.
 __device__ __forceinline__ Item item_of(const FusedArgs &a, int tk) {
-    const int U = a.B * a.Hkv, C = a.n_chunks, S = a.n_splits;
-    const int lag = a.lag < U ? a.lag : U;
+    const int U = a.B * a.Hkv;
     Item it;
     if (tk < kProParts * U) {
         it.kind = 0; it.u = tk / kProParts; it.i = tk % kProParts;
         return it;
     }
-    int r = tk - kProParts * U;
-    if (r < lag * C) {
-        it.kind = 1; it.u = r / C; it.i = r % C;
-        return it;
-    }
-    r -= lag * C;
-    const int mid = U - lag;
-    if (r < mid * (C + S)) {
-        const int blk = r / (C + S), off = r % (C + S);
-        if (off < C) {
-            it.kind = 1; it.u = lag + blk; it.i = off;
-        } else {
-            it.kind = 2; it.u = blk; it.i = off - C;
-        }
-        return it;
-    }
-    r -= mid * (C + S);
-    it.kind = 2; it.u = mid + r / S; it.i = r % S;
+    tk -= kProParts * U;
+    it.kind = 1; it.u = tk / a.n_chunks; it.i = tk % a.n_chunks;
     return it;
 }
 
+// WORK(u, c): scan the span, wait for the unit, select, gather, attend.
 template <int G>
-__global__ __launch_bounds__(kThreads) void k_decode_fused(FusedArgs a) {
+__device__ __forceinline__ void item_work(const FusedArgs &a, int u, int c, Smem<G> &sm) {
+    const Slot cur = slot_of(a, u, c);
+    if (cur.p0 >= cur.p1) return;
+    scan_phase<G>(a, cur, sm);
+    __syncthreads();  // the LDS histograms and the selection state share memory
+    sel_phase<G>(a, cur, sm);
+}
+
+// Three workgroups per CU (two for G = 8): the register budget the
+// compiler must meet.
+template <int G>
+__global__ __launch_bounds__(kThreads, G <= 4 ? 3 : 2) void k_decode_fused(FusedArgs a) {
     __shared__ Smem<G> sm;
     const Item it = item_of(a, blockIdx.x);
     if (it.kind == 0) item_pro<G>(a, it.u, it.i, sm);
-    else if (it.kind == 1) item_scan<G>(a, it.u, it.i, sm);
-    else item_sel<G>(a, it.u, it.i, sm);
+    else item_work<G>(a, it.u, it.i, sm);
     __syncthreads();
     if (threadIdx.x == 0) unit_finish(a, it.u);
 }
@@ -1060,20 +1159,15 @@ bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, DecodePlan *p) {
     d.G = G;
     d.NB = G * kBits + 1;
     d.max_ctx = max_ctx;
-    d.chunk = kChunk;
-    const int64_t C = max_ctx > 0 ? (max_ctx + kChunk - 1) / kChunk : 1;
-    // selection splits: kMinCps chunks each, more when a unit would get
-    // more than kMaxSplits of them
-    int64_t cps = (C + kMaxSplits - 1) / kMaxSplits;
-    if (cps < kMinCps) cps = kMinCps;
-    if (cps > C) cps = C;
-    const int64_t NS = (C + cps - 1) / cps;
-    const int64_t items = units * (kProParts + C + NS);
+    // work items: spans of a multiple of kSpanUnit keys, at most kMaxSplits
+    // per unit (all of a unit's items must fit on the chip together)
+    const int64_t ctx = max_ctx > 0 ? max_ctx : 1;
+    const int64_t per = (ctx + (int64_t)kMaxSplits * kSpanUnit - 1) / ((int64_t)kMaxSplits * kSpanUnit);
+    d.span = per * kSpanUnit;
+    const int64_t C = (ctx + d.span - 1) / d.span;
+    const int64_t items = units * (kProParts + C);
     if (items > INT32_MAX / 2) return false;
     d.n_chunks = (int)C;
-    d.cps = (int)cps;
-    d.n_splits = (int)NS;
-    d.lag = kSelLag;
     d.n_items = (int)items;
     d.sstride = ((max_ctx + 63) / 64) * 64;
     size_t off = 0;
@@ -1084,9 +1178,9 @@ bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, DecodePlan *p) {
     d.off_chunk_hist = off;
     off = align256(off + (size_t)units * d.n_chunks * d.NB * 4);
     d.off_part_ml = off;
-    off = align256(off + (size_t)units * d.n_splits * G * 2 * 4);
+    off = align256(off + (size_t)units * d.n_chunks * G * 2 * 4);
     d.off_part_o = off;
-    off = align256(off + (size_t)units * d.n_splits * G * kHeadDim * 4);
+    off = align256(off + (size_t)units * d.n_chunks * G * kHeadDim * 4);
     d.off_scores = off;
     off = align256(off + (size_t)units * d.sstride * 2);
     d.total = off;
@@ -1132,10 +1226,8 @@ hipError_t launch_decode(const DecodePlan &p, uint16_t *k_cache, uint16_t *v_cac
     a.B = p.B;
     a.Hkv = p.Hkv;
     a.k_max = k_max;
+    a.span = p.span;
     a.n_chunks = p.n_chunks;
-    a.cps = p.cps;
-    a.n_splits = p.n_splits;
-    a.lag = p.lag;
     a.n_items = p.n_items;
     switch (p.G) {
         case 1: return launch_g<1>(p, a, s);

@@ -26,11 +26,8 @@ constexpr int kCtrlUnitBase = 16;
 struct DecodePlan {
     int B = 0, Hq = 0, Hkv = 0, G = 0, NB = 0;
     int64_t max_ctx = 0;
-    int chunk = 0;       // keys per scan item
-    int n_chunks = 0;    // scan items per unit: ceil(max_ctx / chunk)
-    int cps = 0;         // scan chunks per selection split
-    int n_splits = 0;    // selection splits per unit: ceil(n_chunks / cps)
-    int lag = 0;         // SEL items of unit u are placed after the SCAN items of unit u + lag
+    int64_t span = 0;    // keys per work item (scan and selection of one span)
+    int n_chunks = 0;    // work items per unit: ceil(max_ctx / span)
     int n_items = 0;     // workgroups of the launch
     int64_t sstride = 0; // score row stride (elements) in the workspace
     size_t off_qcodes = 0, off_unit_hist = 0, off_chunk_hist = 0, off_part_ml = 0,
