@@ -498,28 +498,42 @@ __device__ __forceinline__ void slot_score(const FusedArgs &a, const Slot &s, in
                                            const uvec4 (&buf)[kSub], const uint32_t (&qc)[G][4],
                                            const uint64_t (&app)[2], Smem<G> &sm) {
     const int t = threadIdx.x, wv = t >> 6;
-    const int64_t app_row = s.sl.app ? s.sl.l0 : -1;
-    const uvec4 appv = {(uint32_t)app[0], (uint32_t)(app[0] >> 32), (uint32_t)app[1],
-                        (uint32_t)(app[1] >> 32)};
     constexpr int HPW = SmemScan<G>::NH / 4;  // sub-histograms per wave
     uint32_t *wh = sm.scan.hist[wv * HPW + (t & (HPW - 1))];
-    uint16_t *sc = a.scores + (int64_t)s.u * a.sstride;
-    uint16_t *sd = a.scores_dbg ? a.scores_dbg + (int64_t)s.u * a.max_ctx : nullptr;
     const bool in_lds = a.span <= kSpanUnit;
+    const int n_span = (int)(s.p1 - s.p0);
+    const int sub_lo = kSub * sb * kThreads;
+    const int app_ii = s.sl.app ? (int)(s.sl.l0 - s.p0) : -1;
+    if (in_lds && !a.scores_dbg && sub_lo + kSub * kThreads <= n_span &&
+        (app_ii < sub_lo || app_ii >= sub_lo + kSub * kThreads)) {
+        // a whole sub-batch of ordinary keys
+#pragma unroll
+        for (int r = 0; r < kSub; ++r) {
+            const int ii = sub_lo + r * kThreads + t;
+            const int sv = group_hamming<G>(buf[r], qc);
+            atomicAdd(&wh[sv], 1u);
+            sm.scan.scores[ii] = (uint16_t)sv;
+        }
+        return;
+    }
+    const uvec4 appv = {(uint32_t)app[0], (uint32_t)(app[0] >> 32), (uint32_t)app[1],
+                        (uint32_t)(app[1] >> 32)};
+    uint16_t *sc = a.scores + (int64_t)s.u * a.sstride + s.p0;
+    uint16_t *sd = a.scores_dbg ? a.scores_dbg + (int64_t)s.u * a.max_ctx + s.p0 : nullptr;
 #pragma unroll
     for (int r = 0; r < kSub; ++r) {
-        const int64_t i = s.p0 + (int64_t)(kSub * sb + r) * kThreads + t;
+        const int ii = sub_lo + r * kThreads + t;
         uint32_t sv = kNoScore;
-        if (i < s.p1) {
-            const uvec4 k = (i == app_row) ? appv : buf[r];
+        if (ii < n_span) {
+            const uvec4 k = (ii == app_ii) ? appv : buf[r];
             sv = (uint32_t)group_hamming<G>(k, qc);
             atomicAdd(&wh[sv], 1u);
-            if (sd) sd[i] = (uint16_t)sv;
-            if (in_lds) sm.scan.scores[i - s.p0] = (uint16_t)sv;
+            if (sd) sd[ii] = (uint16_t)sv;
+            if (in_lds) sm.scan.scores[ii] = (uint16_t)sv;
         }
         if (!in_lds) {
             const uint32_t nb = (uint32_t)__shfl_xor((int)sv, 1, 64);
-            if (!(t & 1) && i < s.p1) st_dev(reinterpret_cast<uint32_t *>(sc + i), sv | (nb << 16));
+            if (!(t & 1) && ii < n_span) st_dev(reinterpret_cast<uint32_t *>(sc + ii), sv | (nb << 16));
         }
     }
 }
@@ -772,6 +786,26 @@ __device__ __forceinline__ int wave_sum64(int v) {
     return tot;
 }
 
+// Bit masks over eight packed u16 scores (bit e: score e): le8 of the scores
+// <= T, lt8 of the scores < T.  Per 16-bit half, with x <= 0x7FFF:
+// (0x8000 + T) - x has bit 15 set iff x <= T, and no borrow crosses halves.
+// kNoScore (0xFFFF) is first folded to 0x7FFF, still above every T.
+__device__ __forceinline__ void cut_masks(const uint4 &v, int T, uint32_t &le8, uint32_t &lt8) {
+    const uint32_t hle = (uint32_t)(0x8000 + T) * 0x10001u;
+    const uint32_t hlt = (uint32_t)(0x8000 + T - 1) * 0x10001u;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t le = 0, lt = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t x = w[k] & 0x7FFF7FFFu;
+        const uint32_t a = hle - x, b = hlt - x;
+        le |= (((a >> 15) & 1u) << (2 * k)) | ((a >> 31) << (2 * k + 1));
+        lt |= (((b >> 15) & 1u) << (2 * k)) | ((b >> 31) << (2 * k + 1));
+    }
+    le8 = le;
+    lt8 = lt;
+}
+
 // Score e (0..7) of eight packed u16 scores.
 __device__ __forceinline__ int score_at(const uint4 &v, int e) {
     const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
@@ -900,17 +934,17 @@ __device__ __forceinline__ void sel_phase(const FusedArgs &a, const Slot &cur, S
     for (int h = 0; h < G; ++h) o[h][0] = o[h][1] = 0.f;
     int64_t ties_acc = 0;
     for (int64_t rb = s0; rb < s1; rb += kListCap) {
-        // pass 1: this wave's score-T and below-T counts (past s1 the words
-        // read as kNoScore, which is above every T)
+        // pass 1: this lane's keys below T and up to T as bit masks (bit e of
+        // slot d: key woff + 512 d + e; past s1 the words read as kNoScore,
+        // which is above every T), and the wave's counts
+        uint32_t lt8[D], le8[D];
         int n_eq = 0, n_lt = 0;
 #pragma unroll
-        for (int d = 0; d < D; ++d)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int sv = score_at(pf[d], e);
-                n_eq += sv == T;
-                n_lt += sv < T;
-            }
+        for (int d = 0; d < D; ++d) {
+            cut_masks(pf[d], T, le8[d], lt8[d]);
+            n_eq += __popc(le8[d] & ~lt8[d]);
+            n_lt += __popc(lt8[d]);
+        }
         {
             const int weq = wave_sum64(n_eq), wlt = wave_sum64(n_lt);
             if (lane == 0) {
@@ -936,33 +970,33 @@ __device__ __forceinline__ void sel_phase(const FusedArgs &a, const Slot &cur, S
             batch_eq += e2;
             batch_sel += sw;
         }
-        // pass 2: select in index order (d, lane, e) and write the list
+        // pass 2: select in index order (d, lane, e) and write the list.  The
+        // score-T keys are taken in index order while the split's tie count
+        // is below rem_quota: a lane takes all or none of its ties, except
+        // the one lane where the quota runs out, which takes the lowest ones.
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            int ne = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ne += score_at(pf[d], e) == T;
+            const uint32_t eq8 = le8[d] & ~lt8[d];
+            const int ne = __popc(eq8);
             int ne_tot;
-            int64_t tr = tie_base + wave_excl_scan16(ne, &ne_tot);
-            unsigned selmask = 0;
-            int n_sel = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int sv = score_at(pf[d], e);
-                bool take = sv < T;
-                if (sv == T) {
-                    take = tr < rem_quota;
-                    ++tr;
+            const int64_t tr = tie_base + wave_excl_scan16(ne, &ne_tot);
+            uint32_t sel8;
+            if (tr + ne <= rem_quota) {
+                sel8 = le8[d];
+            } else if (tr >= rem_quota) {
+                sel8 = lt8[d];
+            } else {
+                uint32_t take = 0, rest = eq8;
+                for (int q = (int)(rem_quota - tr); q > 0; --q) {
+                    take |= rest & (0u - rest);  // lowest remaining tie
+                    rest &= rest - 1u;
                 }
-                selmask |= (take ? 1u : 0u) << e;
-                n_sel += take;
+                sel8 = lt8[d] | take;
             }
             int ns_tot;
-            int p = sel_base + wave_excl_scan16(n_sel, &ns_tot);
+            int p = sel_base + wave_excl_scan16(__popc(sel8), &ns_tot);
             const int o0 = (int)woff + d * 512;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (selmask & (1u << e)) sm.sel.list[p++] = (uint16_t)(o0 + e);
+            for (uint32_t mm = sel8; mm; mm &= mm - 1u) sm.sel.list[p++] = (uint16_t)(o0 + __builtin_ctz(mm));
             tie_base += ne_tot;
             sel_base += ns_tot;
         }

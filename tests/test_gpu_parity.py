@@ -131,6 +131,42 @@ def test_fused_matches_two_calls(gpu):
     assert int(a.cache.ctrl[1:].abs().sum().item()) == 0
 
 
+FAST = [synth.config(1), FUZZ[2], FUZZ[3],
+        synth.custom("g4 long", 2, 8, 2, [40000, 17000], [625, 265], [40, 17], seed=21)]
+
+
+@pytest.mark.parametrize("spec", FAST, ids=[s.name for s in FAST])
+def test_step_without_debug_outputs_matches(gpu, spec):
+    # Without the optional debug outputs the kernel takes its fast scoring
+    # path; results must be bit-identical to the run that writes them.
+    a = GpuWorkload(spec, gpu, extra_ctx=2)
+    b = GpuWorkload(spec, gpu, extra_ctx=2)
+    oa, _, _ = a.step(debug=True)
+    ob, _, _ = b.step(debug=False)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+    assert torch.equal(a.cache.codes, b.cache.codes)
+    assert torch.equal(a.cache.k, b.cache.k) and torch.equal(a.cache.v, b.cache.v)
+    assert torch.equal(a.cache.seq_len, b.cache.seq_len)
+    assert a.cache.status() == 0 and b.cache.status() == 0
+
+
+def test_config3_step_without_debug_outputs(gpu):
+    # The benchmarked call (no debug outputs) at full size, outputs against
+    # the oracle on sampled units.
+    spec = synth.config(3)
+    wl = GpuWorkload(spec, gpu, extra_ctx=2)
+    out, _, _ = wl.step(debug=False)
+    torch.cuda.synchronize()
+    assert wl.cache.status() == 0
+    G = spec.G
+    for (b, kv) in [(0, 0), (1, 6), (3, 3)]:
+        _say(f"[parity] cfg3 no-debug: oracle unit {(b, kv)}")
+        ref = oracle_unit(spec, wl, b, kv)
+        o = out[b, kv * G:(kv + 1) * G].float().cpu().numpy().astype(np.float64)
+        assert np.abs(o - ref["out"]).max() <= OUT_TOL
+
+
 def test_many_units_dense_and_sparse(gpu):
     # 512 units, so each unit has a single split of up to 3000 keys; half the
     # sequences select everything (dense), which overflows the LDS index
