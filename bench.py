@@ -182,6 +182,32 @@ def main():
         print(f"[bench] device status flags set: {status}", file=sys.stderr)
         sys.exit(1)
 
+    # The prefill encode of the same workload (hata_append over the N - 1
+    # prefilled rows of every sequence, codes computed in place): events
+    # around each call, after one warm-up.
+    enc_ms = []
+    for r in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        base.encode_prefill()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if r > 0:
+            enc_ms.append(e0.elapsed_time(e1))
+    enc_rows = B * Hkv * (N - 1)
+    enc_s = statistics.mean(enc_ms) * 1e-3
+    prefill = {
+        "what": "hata_append encoding the N - 1 prefilled rows of every (sequence, KV head) "
+                "in place (one launch)",
+        "rows": enc_rows,
+        "ms": enc_s * 1e3,
+        "Mrows_per_s": enc_rows / enc_s / 1e6,
+        "hbm_GBps": enc_rows * (256 + 16) / enc_s / 1e9,
+        "useful_TFLOPs": enc_rows * 2 * 128 * 128 / enc_s / 1e12,
+        "mfma_TFLOPs": enc_rows * 2 * 2 * 128 * 128 / enc_s / 1e12,
+        "mfma_peak_TFLOPs": 2500.0,
+    }
+
     n_ctx = ctx0 + (args.steps // L) / 2.0  # mean context over the timed steps
     step_bytes = algorithmic_bytes(B, Hq, Hkv, n_ctx, K)
     achieved = step_bytes / (dec_ms * 1e-3) / 1e9
@@ -220,6 +246,7 @@ def main():
             "traffic": None,
             "launch_us": dec_ms * 1e3,
         },
+        "prefill_encode": prefill,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libhata.so")
 
-SOURCES = ["api.cpp", "encode_exact.hip", "decode.hip"]
+SOURCES = ["api.cpp", "encode_exact.hip", "encode_mfma.hip", "decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -50,8 +50,14 @@ hata_status hata_encode_keys(const uint16_t *keys, int64_t n_rows, int32_t n_hea
     if (!keys || !w_h || !codes_out) return HATA_ERR_INVALID_ARG;
     if (row_stride < 0 || head_stride < 0) return HATA_ERR_INVALID_ARG;
     if (n_heads > 1 && head_stride < kHeadDim && row_stride < kHeadDim) return HATA_ERR_INVALID_ARG;
-    hipError_t e = launch_encode_exact(keys, n_rows, n_heads, row_stride, head_stride, w_h,
-                                       codes_out, static_cast<hipStream_t>(stream));
+    // Bulk calls on the matrix cores (16-byte row pieces), small ones exact;
+    // both give the same bits.
+    const bool mfma = n_rows >= kMfmaMinRows && aligned16(keys) && row_stride % 8 == 0 &&
+                      head_stride % 8 == 0;
+    hipError_t e = mfma ? launch_encode_mfma(keys, n_rows, n_heads, row_stride, head_stride, w_h,
+                                             codes_out, static_cast<hipStream_t>(stream))
+                        : launch_encode_exact(keys, n_rows, n_heads, row_stride, head_stride, w_h,
+                                              codes_out, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
 }
 
@@ -62,9 +68,13 @@ hata_status hata_append(const hata_cache *c, const uint16_t *k_new, const uint16
     if (t_max < 0 || !n_new || !w_h) return HATA_ERR_INVALID_ARG;
     if ((k_new == nullptr) != (v_new == nullptr)) return HATA_ERR_INVALID_ARG;
     if (t_max == 0) return HATA_OK;
-    hipError_t e = launch_append_exact(c->k, c->v, c->codes, c->seq_len, c->ctrl, c->batch,
-                                       c->n_kv_heads, c->max_ctx, k_new, v_new, n_new, t_max,
-                                       w_h, static_cast<hipStream_t>(stream));
+    const bool mfma = t_max >= kMfmaMinRows && (k_new == nullptr || (aligned16(k_new) && aligned16(v_new)));
+    hipError_t e = mfma ? launch_append_mfma(c->k, c->v, c->codes, c->seq_len, c->ctrl, c->batch,
+                                             c->n_kv_heads, c->max_ctx, k_new, v_new, n_new, t_max,
+                                             w_h, static_cast<hipStream_t>(stream))
+                        : launch_append_exact(c->k, c->v, c->codes, c->seq_len, c->ctrl, c->batch,
+                                              c->n_kv_heads, c->max_ctx, k_new, v_new, n_new, t_max,
+                                              w_h, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
 }
 

@@ -44,6 +44,19 @@ hipError_t launch_append_exact(uint16_t *k_cache, uint16_t *v_cache, uint32_t *c
                                const int32_t *n_new, int t_max, const float *w,
                                hipStream_t s);
 
+// Bulk encoder on the matrix cores (identical bits; rows read as 16-byte
+// pieces, so keys / k_new / v_new 16-byte aligned and strides multiples of
+// 8 elements).  Used from kMfmaMinRows rows on.
+constexpr int kMfmaMinRows = 64;
+
+hipError_t launch_append_mfma(uint16_t *k_cache, uint16_t *v_cache, uint32_t *codes,
+                              int32_t *seq_len, int32_t *ctrl, int B, int Hkv, int64_t max_ctx,
+                              const uint16_t *k_new, const uint16_t *v_new,
+                              const int32_t *n_new, int t_max, const float *w, hipStream_t s);
+
+hipError_t launch_encode_mfma(const uint16_t *keys, int64_t n_rows, int n_heads, int64_t row_stride,
+                              int64_t head_stride, const float *w, uint32_t *codes, hipStream_t s);
+
 hipError_t launch_encode_exact(const uint16_t *keys, int64_t n_rows, int n_heads,
                                int64_t row_stride, int64_t head_stride, const float *w,
                                uint32_t *codes, hipStream_t s);

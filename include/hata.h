@@ -113,7 +113,11 @@ typedef struct {
  *   n_rows    >= 0 rows; n_heads >= 1 heads, each with its own W_H.
  *   w_h       device fp32 [n_heads][128 (d)][128 (bit)].
  *   codes_out device u32 [n_rows][n_heads][4], fully overwritten.
- * Every bit is the exact sign of the code convention above.
+ * Every bit is the exact sign of the code convention above.  From 64 rows
+ * on (with keys 16-byte aligned and strides multiples of 8 elements) the
+ * products run on the matrix cores, and every bit inside their error band is
+ * recomputed; smaller or unaligned calls take the exact kernel.  The bits are
+ * the same either way.
  * Errors: HATA_ERR_INVALID_ARG for null pointers (with n_rows > 0),
  * negative sizes or strides smaller than a row; HATA_ERR_HIP on launch
  * failure.
@@ -139,6 +143,8 @@ hata_status hata_encode_keys(const uint16_t *keys, int64_t n_rows, int32_t n_hea
  * [0, t_max] sets HATA_DEV_BAD_NEW and the entry is skipped.
  * Host errors: HATA_ERR_INVALID_ARG (null cache fields, exactly one of
  * k_new / v_new null, t_max < 0), HATA_ERR_UNSUPPORTED (shape).
+ * From t_max >= 64 the codes are computed on the matrix cores (as in
+ * hata_encode_keys; same bits).
  */
 hata_status hata_append(const hata_cache *c, const uint16_t *k_new, const uint16_t *v_new,
                         const int32_t *n_new, int32_t t_max, const float *w_h, void *stream);
