@@ -18,9 +18,12 @@ Prints one JSON line.  value = decode steps per second on one GPU.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -33,6 +36,10 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 HBM_PEAK_GBS = 8000.0
 LAYERS = 8
 QUERIES = 7  # distinct step queries, coprime with LAYERS: 56 (layer, query) pairs
+COPY_PROBE_BYTES = 256 << 20
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_decode_fused_cfg3_hbm_traffic.md")
+DECODE_SOURCES = ("decode.hip", "device_util.h", "hata_internal.h")
+DECODE_KERNEL = "k_decode_fused<4>"
 
 
 def parse():
@@ -43,6 +50,13 @@ def parse():
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=2)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="end with 4 plain 256 MiB device-to-device copies (the "
+                         "calibration kernel for HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM traffic block from two rocprofv3 --pmc "
+                         "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of "
+                         "'bench.py --copy-probe' runs, then exit")
     return ap.parse_args()
 
 
@@ -53,6 +67,69 @@ def algorithmic_bytes(B, Hq, Hkv, n_ctx, k):
     K and V row and one code per sequence and KV head)."""
     return (16 * B * Hkv * n_ctx + 512 * B * Hkv * k + 4 * Hkv * 128 * 128 +
             2 * 2 * B * Hq * 128 + B * Hkv * (512 + 16))
+
+
+def decode_sources_digest():
+    """sha256 over the decode kernel's sources: a traffic figure taken from
+    counters is only reported for the kernel it was measured on."""
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "hash_top_sparse_encode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _pmc_per_dispatch(path):
+    """{kernel name: [counter value per dispatch, in dispatch order]}."""
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+    out = {}
+    for r in rows:
+        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def pmc_summary(fetch_csv, write_csv):
+    """Key: value lines for the traffic profile.  The decode kernel's
+    counters are averaged over its dispatches; the calibration copy is the
+    last 4 __amd_rocclr_copyBuffer dispatches (bench.py --copy-probe ends
+    with 4 copies of COPY_PROBE_BYTES)."""
+    vals = {}
+    for counter, path in (("fetch", fetch_csv), ("write", write_csv)):
+        per = _pmc_per_dispatch(path)
+        dec = [v for k, v in per.items() if DECODE_KERNEL in k]
+        cp = [v for k, v in per.items() if "copyBuffer" in k]
+        if len(dec) != 1 or len(cp) != 1 or len(cp[0]) < 4:
+            raise SystemExit(f"{path}: expected one decode kernel and >= 4 copies")
+        vals[f"decode_{counter}_kib_per_dispatch"] = statistics.mean(dec[0])
+        vals[f"decode_{counter}_dispatches"] = len(dec[0])
+        vals[f"copy_{counter}_kib"] = statistics.mean(cp[0][-4:])
+    lines = [f"decode_sources_sha256: {decode_sources_digest()}",
+             f"copy_bytes: {COPY_PROBE_BYTES}"]
+    lines += [f"{k}: {v}" for k, v in vals.items()]
+    return "\n".join(lines)
+
+
+def measured_traffic_bytes():
+    """HBM bytes per decode launch from the committed counter summary:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) each scaled by copy_bytes
+    over what the same counter reads for the calibration copy.  None when
+    the summary is missing or the decode sources changed since."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^([a-z0-9_]+): (\S+)$", text, flags=re.M))
+    try:
+        if vals["decode_sources_sha256"] != decode_sources_digest():
+            return None
+        cb = float(vals["copy_bytes"])
+        total = 0.0
+        for c in ("fetch", "write"):
+            scale = cb / (float(vals[f"copy_{c}_kib"]) * 1024.0)
+            total += float(vals[f"decode_{c}_kib_per_dispatch"]) * 1024.0 * scale
+        return total
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
 
 
 def cpu_baseline(spec, reps):
@@ -101,6 +178,9 @@ def cpu_baseline(spec, reps):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        print(pmc_summary(*args.pmc_summary))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path "
               "has no multi-GPU mode.", file=sys.stderr)
@@ -211,6 +291,7 @@ def main():
     n_ctx = ctx0 + (args.steps // L) / 2.0  # mean context over the timed steps
     step_bytes = algorithmic_bytes(B, Hq, Hkv, n_ctx, K)
     achieved = step_bytes / (dec_ms * 1e-3) / 1e9
+    traffic_bytes = measured_traffic_bytes()
 
     result = {
         "metric": "decode steps/sec & HBM GB/s fraction, hashed top-k attn @128K ctx, 1 GPU",
@@ -243,11 +324,21 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": (traffic_bytes / (dec_ms * 1e-3) / 1e9
+                        if traffic_bytes is not None else None),
+            "traffic_bytes_per_launch": traffic_bytes,
+            "alg_bytes_per_launch": step_bytes,
             "launch_us": dec_ms * 1e3,
         },
         "prefill_encode": prefill,
     }
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(spec, args.cpu_reps)

@@ -9,31 +9,41 @@
 //              bits each: exact codes of the G query heads and of the step's
 //              appended token; part 0 also appends the K/V row and clears
 //              the unit histogram.
-//   SCAN(u,c)  chunk c of up to 8192 keys, in passes of 4096: 16-byte code
-//              loads issued before anything else, G x (XOR + popcount) against query codes held in scalar
-//              registers, scores stored four to a 64-bit word, per-wave LDS
-//              histograms of the 0..128G range, the chunk's cumulative
-//              histogram, its counts added into the unit histogram.
-//              The last chunk of a unit to finish derives the selection plan
-//              from the unit and chunk histograms: the cut
-//              score T, the quota of score-T keys, and per split the score-T
-//              and below-T counts of the chunks before it.
-//   SEL(u,s)   split s (a run of chunks): reads its plan entries, re-reads
-//              its scores (four rounds prefetched),
-//              compact the selected indices in index order into LDS, gather
-//              bf16 K/V rows (32 lanes x 8 bytes per row, 8 rows per lane
-//              group in flight) with an online softmax; one (m, l, o)
-//              partial per query head.  The last split of a unit merges the
-//              partials in split order into the bf16 output.
-// The item order is PRO for every unit, then SCAN items unit by unit, then
-// SEL items unit by unit (the order also allows SEL items of unit u right
-// after the SCAN items of unit u + lag).
+//   WORK(u,c)  span c of the unit's keys (8192 keys, or a multiple of 8192
+//              when a unit would need more than 64 items), in two phases:
+//     scan     16-byte code loads in 16 KB sub-batches, two in flight (the
+//              wait for the query codes sits behind the first two);
+//              G x (XOR + popcount) against query codes held in scalar
+//              registers; scores kept in LDS (or the workspace for longer
+//              spans) and counted into 16 LDS sub-histograms of the 0..128G
+//              range; the span's cumulative histogram published and its
+//              counts added into the unit histogram; the unit's scan
+//              counter bumped.
+//     select   once every WORK item of the unit has scanned: the cut score
+//              T (first bin whose cumulative count reaches k_eff) from the
+//              unit histogram, the below-T and score-T counts of the spans
+//              before c from their cumulative histograms (which fixes how
+//              many score-T keys this span keeps: the lowest indices win),
+//              then the span's selected keys compacted in index order into
+//              an LDS list by packed 16-bit compare masks and ballots;
+//     attend   gather of the selected bf16 K/V rows, logits of 16-key tiles
+//              on the matrix cores, an online softmax in base 2, P.V on the
+//              vector units; one (m, l, o) partial per query head.  The
+//              last item of a unit to finish merges the partials in item
+//              order into the bf16 output.
 //
-// Ordering: an item waits only for items of its own unit with smaller block
-// indices (SCAN on PRO, SEL on all SCANs).  Workgroups of a grid are started
-// in block order within each XCD, and a finished workgroup frees its slot, so
-// the smallest unfinished index can always start.  Every wait also gives up
-// after a bound (HATA_DEV_STALL), so the kernel always terminates.
+// Ordering: a PRO part waits for nothing; a WORK item's scan waits for the
+// PRO parts of its unit (smaller block indices), and its selection for the
+// scans of every WORK item of its unit.  Workgroups of a grid are started in
+// block order within each XCD, and a finished workgroup frees its slot.  Take
+// the smallest unfinished block X: every PRO part is done, so if X is
+// WORK(u, c), every workgroup that started after the finished ones holds an
+// item of unit u or a later one, and the unit's unstarted items (at most 63)
+// are the next in line on their XCDs; an XCD holds at least 64 of these
+// workgroups at once (32 CUs x 2 or 3), so they all start, all scan, and
+// unit u completes.  Every
+// wait also gives up after a bound (HATA_DEV_STALL), so the kernel always
+// terminates.
 //
 // Coherence across the eight XCDs without cache flushes: every value one
 // workgroup produces for another (query codes, the appended row and code,
