@@ -217,11 +217,13 @@ def hata_decode_workspace_bytes(cache: HataCache, k_max: int) -> int:
 
 
 def alloc_workspace(cache: HataCache, k_max: int) -> torch.Tensor:
-    """A device byte tensor of the required size (torch allocations are 256-byte aligned)."""
+    """A zero-filled device byte tensor of the required size (torch
+    allocations are 256-byte aligned).  It may be shared by caches whose
+    calls are ordered on one stream."""
     n = hata_decode_workspace_bytes(cache, k_max)
     if n == 0:
         raise ValueError("unsupported cache shape")
-    return torch.empty(n, dtype=torch.uint8, device=cache.k.device)
+    return torch.zeros(n, dtype=torch.uint8, device=cache.k.device)
 
 
 def hata_decode_attn(cache: HataCache, q: torch.Tensor, w_h: torch.Tensor, topk: torch.Tensor,

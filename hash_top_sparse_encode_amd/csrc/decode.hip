@@ -7,30 +7,33 @@
 // Work items, one per workgroup, in block-index order:
 //   PRO(u,p)   per unit u = (batch b, KV head g), four parts of 32 code
 //              bits each: exact codes of the G query heads and of the step's
-//              appended token; part 0 also appends the K/V row and clears
-//              the unit histogram.
+//              appended token, published as words tagged with the launch's
+//              tag; part 0 also appends the K/V row and clears the unit
+//              histogram (before any of the unit's words is published).
 //   WORK(u,c)  span c of the unit's keys (8192 keys, or a multiple of 8192
 //              when a unit would need more than 64 items), in two phases:
-//     scan     16-byte code loads in 16 KB sub-batches, two in flight (the
-//              wait for the query codes sits behind the first two);
-//              G x (XOR + popcount) against query codes held in scalar
-//              registers; scores kept in LDS (or the workspace for longer
-//              spans) and counted into 16 LDS sub-histograms of the 0..128G
-//              range; the span's cumulative histogram published and its
-//              counts added into the unit histogram; the unit's scan
-//              counter bumped.
-//     select   once every WORK item of the unit has scanned: the cut score
-//              T (first bin whose cumulative count reaches k_eff) from the
-//              unit histogram, the below-T and score-T counts of the spans
-//              before c from their cumulative histograms (which fixes how
-//              many score-T keys this span keeps: the lowest indices win),
-//              then the span's selected keys compacted in index order into
-//              an LDS list by packed 16-bit compare masks and ballots;
+//     scan     wave 0 polls the unit's tagged code words while waves 1-3
+//              start the span's code stream (16-byte loads in 16 KB
+//              sub-batches, four in flight); the group score of each key
+//              from bit planes of the summed query codes (held in scalar
+//              registers); scores kept in LDS (or the workspace for longer
+//              spans) and counted into LDS sub-histograms of the 0..128G
+//              range; the span's cumulative histogram published (tagged)
+//              and its counts added into the unit histogram.
+//     select   the span's candidates (scores up to a cut read off its own
+//              histogram) are listed while the unit's other items finish;
+//              once the unit histogram is complete (its counts sum to the
+//              context length), the cut score T (first bin whose cumulative
+//              count reaches k_eff) and, from the earlier spans' cumulative
+//              histograms, the below-T and score-T keys before this span
+//              (which fixes how many score-T keys it keeps: the lowest
+//              indices win); the selection is then taken from the
+//              candidates (or, if T lies above their cut, from all scores);
 //     attend   gather of the selected bf16 K/V rows, logits of 16-key tiles
 //              on the matrix cores, an online softmax in base 2, P.V on the
 //              vector units; one (m, l, o) partial per query head.  The
 //              last item of a unit to finish merges the partials in item
-//              order into the bf16 output.
+//              order into the bf16 output and resets the unit's state.
 //
 // Ordering: a PRO part waits for nothing; a WORK item's scan waits for the
 // PRO parts of its unit (smaller block indices), and its selection for the
@@ -41,18 +44,21 @@
 // item of unit u or a later one, and the unit's unstarted items (at most 63)
 // are the next in line on their XCDs; an XCD holds at least 64 of these
 // workgroups at once (32 CUs x 2 or 3), so they all start, all scan, and
-// unit u completes.  Every
-// wait also gives up after a bound (HATA_DEV_STALL), so the kernel always
-// terminates.
+// unit u completes.  Every wait also gives up after a bound
+// (HATA_DEV_STALL), so the kernel always terminates.
 //
 // Coherence across the eight XCDs without cache flushes: every value one
-// workgroup produces for another (query codes, the appended row and code,
-// histograms, scores, partials, counters) is written with a device-scope
-// relaxed atomic store (write-through, "sc1") or atomic add, the producer
-// waits for its stores to complete (s_waitcnt) before bumping a counter, and
-// the consumer reads those values with device-scope atomic loads ("sc1"),
-// which are served by the device-coherent level.  An agent-scope fence would
-// write back / invalidate whole L2s instead, which costs more than the step.
+// workgroup produces for another is written with a device-scope relaxed
+// atomic store (write-through, "sc1") or atomic add and read with
+// device-scope atomic loads ("sc1"), which are served by the
+// device-coherent level.  Readers need no separate "ready" counter: the
+// PRO code words and the per-span cumulative histograms carry a tag (the
+// unit's launch count on this workspace, plus one), so a reader re-reads
+// until every word it uses carries this launch's tag, and the unit
+// histogram is complete exactly when its counts sum to the context length.
+// Only the split partials are published behind a counter (stores drained,
+// then one atomic add), for the merge.  An agent-scope fence would write
+// back / invalidate whole L2s instead, which costs more than the step.
 #include "device_util.h"
 #include "hata_internal.h"
 #include "../../include/hata.h"
@@ -62,11 +68,13 @@ namespace hata {
 constexpr int kThreads = 256;
 constexpr int kSpanUnit = 8192;    // a work item's span of keys is a multiple of this
 constexpr int kSub = 4;            // keys per thread in one sub-batch of code loads (1024 per workgroup)
+constexpr int kScanDepth = 4;      // sub-batches of code loads in flight per workgroup
 constexpr int kMaxSplits = 64;     // work items per unit, at most (the merge width)
 constexpr int kSelRound = 2048;    // 8 scores per thread per selection round
 constexpr int kSelRounds = 4;      // selection rounds per batch (scores prefetched together)
 constexpr int kListCap = kSelRounds * kSelRound;  // selected indices buffered in LDS
 constexpr int kSpinLimit = 1 << 22;
+constexpr int kPollLimit = 1 << 18;  // block-wide polls (each a full re-read)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint16_t kNoScore = 0xFFFF;
 
@@ -79,7 +87,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kProParts = 4;
 
 // per-unit counter words
-constexpr int kPro = 0, kScan = 1, kAttn = 2, kFin = 3, kNumCtr = 4;
+constexpr int kAttn = 0, kNumCtr = 1;
+// Bins of every earlier item's cumulative histogram read, ending at the
+// candidate cut, along with the unit histogram.
+constexpr int kWin = 8;
 constexpr int kUnitWords = 64;  // one 256-byte line per unit (and per batch entry)
 
 struct FusedArgs {
@@ -97,9 +108,10 @@ struct FusedArgs {
     int32_t *sel_out;        // optional debug output
     uint16_t *scores_dbg;    // optional debug output, row stride max_ctx
     uint16_t *scores;        // workspace, row stride sstride
-    uint32_t *qcodes;
+    uint32_t *gen;           // per unit: launches completed on this workspace (tags are gen + 1)
+    uint64_t *qtag;          // per unit: (G + 1) x 4 tagged code words (query heads, appended key)
     uint32_t *unit_hist;     // per unit: 128 G + 2 words (bins in pairs)
-    uint32_t *chunk_hist;    // per unit and scan slot: cumulative counts, 128 G + 1 bins
+    uint64_t *chunk_hist;    // per unit and work item: tagged cumulative counts, 128 G + 1 bins
     float *part_ml;
     float *part_o;
     int64_t max_ctx;
@@ -181,21 +193,6 @@ __device__ __forceinline__ int32_t *batch_ctr(const FusedArgs &a, int b) {
     return a.ctrl + kCtrlUnitBase + kUnitWords * (a.B * a.Hkv + b);
 }
 
-// Thread 0 polls until *p >= target; the workgroup continues together.
-__device__ __forceinline__ void wg_wait_geq(const FusedArgs &a, int32_t *p, int target) {
-    if (threadIdx.x == 0) {
-        int spins = 0;
-        while (ld_dev(p) < target) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++spins > kSpinLimit) {
-                atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_STALL);
-                break;
-            }
-        }
-    }
-    __syncthreads();
-}
-
 // Every thread's device-scope stores complete, then thread 0 counts.
 // Returns the counter's previous value (in thread 0).
 __device__ __forceinline__ int wg_signal(int32_t *p) {
@@ -228,6 +225,10 @@ struct SmemScan {
     uint16_t scores[kSpanUnit];
     uint32_t hist[NH][NB];
     int scan[4];
+    uint32_t qc[G * kWords];  // the unit's query codes, fetched by wave 0
+    uint32_t app[kWords];     // the appended key's code (when in this span)
+    int tc;                   // candidate cut of the span (see slot_publish)
+    uint32_t gen;             // the unit's launch generation
 };
 
 template <int G>
@@ -293,6 +294,7 @@ __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Sm
             wq[r] = *reinterpret_cast<const fvec4 *>(wk + (f >> 3) * kBits + 4 * (f & 7));
         }
     }
+    const uint32_t tag = ld_dev(a.gen + u) + 1u;
     const int64_t raw = a.seq_len[b];
     const StepLen sl = step_len(a, b);
     const int nvec = G + (sl.app ? 1 : 0);
@@ -376,6 +378,9 @@ __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Sm
             }
         }
     }
+    // Part 0's clearing of the unit histogram is complete before any code
+    // word of the unit is published.
+    if (part == 0) drain_memory();
     __syncthreads();
     // Decide bit (v, col) for v = t >> 5 (and v = 8 + (t >> 5) on a second
     // pass for G = 8): tree over the four waves, then the sign test.
@@ -398,26 +403,112 @@ __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Sm
             }
         }
         const uint64_t mb = __ballot(bit);
-        if ((t & 31) == 0 && v < nvec) {
-            const uint32_t word = (uint32_t)(((t >> 5) & 1) ? (mb >> 32) : mb);
-            if (v < G) st_dev(a.qcodes + ((int64_t)b * Hq + kv * G + v) * kWords + part, word);
-            else st_dev(a.codes + ((int64_t)u * a.max_ctx + sl.l0) * kWords + part, word);
+        if ((t & 31) == 0 && v < NV && sl.len > 0) {
+            const uint32_t word = v < nvec ? (uint32_t)(((t >> 5) & 1) ? (mb >> 32) : mb) : 0u;
+            st_dev(a.qtag + ((int64_t)u * NV + v) * kWords + part, ((uint64_t)tag << 32) | word);
+            if (v == G && sl.app) st_dev(a.codes + ((int64_t)u * a.max_ctx + sl.l0) * kWords + part, word);
         }
     }
-    if (sl.len > 0) wg_signal(unit_ctr(a, u, kPro));
-    __syncthreads();
 }
 
 // ---------------------------------------------------------------- scanners
 
+// The group score of a key, sum over the G query heads of
+// popcount(qcode_h XOR kcode), from the query codes summed bit by bit.  For
+// code bit j let c_j (0..G) count the heads with bit j set: the key adds
+// k_j ? G - c_j : c_j.  With G = 2^m, that per-bit value d_j has the bit
+// planes
+//   d_0 = c_0                                  (G - c and c share parity),
+//   d_i = c_i ^ (k & (c_0 | .. | c_{i-1}))    for 0 < i < m (negation flips
+//                                              the bits above the lowest set one),
+//   d_m = k ? [c_j == 0] : c_m,
+// so the score is popcount(c_0) + sum_i 2^i popcount(d_i).  For G = 4 that
+// is five lane operations per code word instead of eight.
 template <int G>
-__device__ __forceinline__ int group_hamming(const uvec4 &k, const uint32_t (&qc)[G][4]) {
-    int s = 0;
+struct QPlanes {
+    static constexpr int M = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;  // G = 2^M
+    static constexpr int NP = G == 1 ? 1 : G == 2 ? 2 : G == 4 ? 4 : 6;
+    uint32_t p[NP][4];  // per code word; see query_planes
+    int c0sum;          // popcount of the c_0 plane over the code
+};
+
+// Planes of the query codes (uniform values, kept in scalar registers):
+//   G = 1: {q}              G = 2: {c_1, z}
+//   G = 4: {c_0, c_1, c_2, z}     G = 8: {c_0, c_1, c_0 | c_1, c_2, c_3, z}
+// with z the bits where no head is set.
+template <int G>
+__device__ __forceinline__ void query_planes(const uint32_t (&qc)[G][4], QPlanes<G> &qp) {
+    constexpr int M = QPlanes<G>::M;
+    qp.c0sum = 0;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-        s += __popc(k.x ^ qc[h][0]) + __popc(k.y ^ qc[h][1]) + __popc(k.z ^ qc[h][2]) +
-             __popc(k.w ^ qc[h][3]);
-    return s;
+    for (int w = 0; w < 4; ++w) {
+        uint32_t c[M + 1];
+#pragma unroll
+        for (int i = 0; i <= M; ++i) c[i] = 0u;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {  // ripple-carry add of head h's bits
+            uint32_t carry = qc[h][w];
+#pragma unroll
+            for (int i = 0; i <= M; ++i) {
+                const uint32_t nc = c[i] ^ carry;
+                carry &= c[i];
+                c[i] = nc;
+            }
+        }
+        uint32_t any = 0u;
+#pragma unroll
+        for (int i = 0; i <= M; ++i) any |= c[i];
+        const uint32_t z = ~any;
+        if constexpr (G == 1) {
+            qp.p[0][w] = c[0];
+        } else {
+            qp.c0sum += __popc(c[0]);
+            if constexpr (G == 2) {
+                qp.p[0][w] = c[1];
+                qp.p[1][w] = z;
+            } else if constexpr (G == 4) {
+                qp.p[0][w] = c[0];
+                qp.p[1][w] = c[1];
+                qp.p[2][w] = c[2];
+                qp.p[3][w] = z;
+            } else {
+                qp.p[0][w] = c[0];
+                qp.p[1][w] = c[1];
+                qp.p[2][w] = c[0] | c[1];
+                qp.p[3][w] = c[2];
+                qp.p[4][w] = c[3];
+                qp.p[5][w] = z;
+            }
+        }
+    }
+}
+
+template <int G>
+__device__ __forceinline__ int group_hamming(const uvec4 &k, const QPlanes<G> &qp) {
+    const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+    if constexpr (G == 1) {
+        int s = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) s += __popc(kw[w] ^ qp.p[0][w]);
+        return s;
+    } else {
+        int p1 = 0, p2 = 0, p3 = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t x = kw[w];
+            if constexpr (G == 2) {
+                p1 += __popc((x & qp.p[1][w]) | (~x & qp.p[0][w]));
+            } else if constexpr (G == 4) {
+                p1 += __popc(qp.p[1][w] ^ (x & qp.p[0][w]));
+                p2 += __popc((x & qp.p[3][w]) | (~x & qp.p[2][w]));
+            } else {
+                p1 += __popc(qp.p[1][w] ^ (x & qp.p[0][w]));
+                p2 += __popc(qp.p[3][w] ^ (x & qp.p[2][w]));
+                p3 += __popc((x & qp.p[5][w]) | (~x & qp.p[4][w]));
+            }
+        }
+        return qp.c0sum + 2 * p1 + 4 * p2 + 8 * p3;
+    }
 }
 
 // Work item c of unit u: keys [c span, min((c + 1) span, len)).
@@ -451,53 +542,38 @@ __device__ __forceinline__ void slot_issue(const FusedArgs &a, const Slot &s, in
     }
 }
 
-// Wait for the unit's PRO parts (the prefetched poll usually settles it),
-// then issue the loads of the query codes and, where the slot holds the key
-// appended in this launch, of its code.  Nothing waits for these loads here.
+// Wave 0 only: the unit's generation and its PRO parts' tagged code words
+// (query heads, then the appended key), re-read until every word carries
+// this launch's tag (generation + 1), into LDS.  Loads complete in order
+// within a wave, so this runs in a wave with no code loads outstanding; the
+// other waves' code streams are already in flight.
 template <int G>
-__device__ __forceinline__ void slot_begin(const FusedArgs &a, const Slot &s, uint64_t (&qraw)[G][2],
-                                           uint64_t (&app)[2]) {
-    if (threadIdx.x == 0 && ld_dev(unit_ctr(a, s.u, kPro)) < kProParts) {
-        int spins = 0;
-        while (ld_dev(unit_ctr(a, s.u, kPro)) < kProParts) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++spins > kSpinLimit) {
-                atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_STALL);
-                break;
-            }
+__device__ __forceinline__ void slot_fetch_qcodes(const FusedArgs &a, const Slot &s, Smem<G> &sm) {
+    constexpr int NW = (G + 1) * kWords;
+    const int lane = threadIdx.x & 63;
+    const uint64_t *src = a.qtag + (int64_t)s.u * NW;
+    const uint32_t tag = ld_dev(a.gen + s.u) + 1u;
+    uint64_t v = lane < NW ? ld_dev(src + lane) : (uint64_t)tag << 32;
+    for (int spins = 0; __ballot((uint32_t)(v >> 32) != tag) != 0; ++spins) {
+        if (spins > kSpinLimit) {
+            if (lane == 0) atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_STALL);
+            break;
         }
+        __builtin_amdgcn_s_sleep(1);
+        if ((uint32_t)(v >> 32) != tag) v = ld_dev(src + lane);
     }
-    __syncthreads();
-    const int b = s.u / a.Hkv, kv = s.u % a.Hkv;
-    const uint64_t *qsrc =
-        reinterpret_cast<const uint64_t *>(a.qcodes + ((int64_t)b * a.Hkv * G + kv * G) * kWords);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        qraw[h][0] = ld_dev(qsrc + 2 * h);
-        qraw[h][1] = ld_dev(qsrc + 2 * h + 1);
-    }
-    app[0] = app[1] = 0;
-    if (s.sl.app && s.sl.l0 >= s.p0 && s.sl.l0 < s.p1) {
-        const int64_t off = s.sl.l0 - s.p0;
-        if (threadIdx.x == (int)(off % kThreads)) {
-            const uint64_t *p = reinterpret_cast<const uint64_t *>(
-                reinterpret_cast<const uvec4 *>(a.codes) + (int64_t)s.u * a.max_ctx + s.sl.l0);
-            app[0] = ld_dev(p);
-            app[1] = ld_dev(p + 1);
-        }
-    }
+    if (lane < G * kWords) sm.scan.qc[lane] = (uint32_t)v;
+    else if (lane < NW) sm.scan.app[lane - G * kWords] = (uint32_t)v;
+    if (lane == 0) sm.scan.gen = tag;
 }
 
-// Query codes from their (uniform) loaded words into scalar registers.
+// Query codes from LDS into scalar registers.
 template <int G>
-__device__ __forceinline__ void qcodes_sgpr(const uint64_t (&qraw)[G][2], uint32_t (&qc)[G][4]) {
+__device__ __forceinline__ void qcodes_sgpr(const Smem<G> &sm, uint32_t (&qc)[G][4]) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        qc[h][0] = __builtin_amdgcn_readfirstlane((uint32_t)qraw[h][0]);
-        qc[h][1] = __builtin_amdgcn_readfirstlane((uint32_t)(qraw[h][0] >> 32));
-        qc[h][2] = __builtin_amdgcn_readfirstlane((uint32_t)qraw[h][1]);
-        qc[h][3] = __builtin_amdgcn_readfirstlane((uint32_t)(qraw[h][1] >> 32));
-    }
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) qc[h][w] = __builtin_amdgcn_readfirstlane(sm.scan.qc[h * kWords + w]);
 }
 
 // Scores of sub-batch sb, counted into the LDS sub-histograms and kept in
@@ -505,8 +581,8 @@ __device__ __forceinline__ void qcodes_sgpr(const uint64_t (&qraw)[G][2], uint32
 // word.
 template <int G>
 __device__ __forceinline__ void slot_score(const FusedArgs &a, const Slot &s, int sb,
-                                           const uvec4 (&buf)[kSub], const uint32_t (&qc)[G][4],
-                                           const uint64_t (&app)[2], Smem<G> &sm) {
+                                           const uvec4 (&buf)[kSub], const QPlanes<G> &qp,
+                                           Smem<G> &sm) {
     const int t = threadIdx.x, wv = t >> 6;
     constexpr int HPW = SmemScan<G>::NH / 4;  // sub-histograms per wave
     uint32_t *wh = sm.scan.hist[wv * HPW + (t & (HPW - 1))];
@@ -520,14 +596,13 @@ __device__ __forceinline__ void slot_score(const FusedArgs &a, const Slot &s, in
 #pragma unroll
         for (int r = 0; r < kSub; ++r) {
             const int ii = sub_lo + r * kThreads + t;
-            const int sv = group_hamming<G>(buf[r], qc);
+            const int sv = group_hamming<G>(buf[r], qp);
             atomicAdd(&wh[sv], 1u);
             sm.scan.scores[ii] = (uint16_t)sv;
         }
         return;
     }
-    const uvec4 appv = {(uint32_t)app[0], (uint32_t)(app[0] >> 32), (uint32_t)app[1],
-                        (uint32_t)(app[1] >> 32)};
+    const uvec4 appv = {sm.scan.app[0], sm.scan.app[1], sm.scan.app[2], sm.scan.app[3]};
     uint16_t *sc = a.scores + (int64_t)s.u * a.sstride + s.p0;
     uint16_t *sd = a.scores_dbg ? a.scores_dbg + (int64_t)s.u * a.max_ctx + s.p0 : nullptr;
 #pragma unroll
@@ -536,7 +611,7 @@ __device__ __forceinline__ void slot_score(const FusedArgs &a, const Slot &s, in
         uint32_t sv = kNoScore;
         if (ii < n_span) {
             const uvec4 k = (ii == app_ii) ? appv : buf[r];
-            sv = (uint32_t)group_hamming<G>(k, qc);
+            sv = (uint32_t)group_hamming<G>(k, qp);
             atomicAdd(&wh[sv], 1u);
             if (sd) sd[ii] = (uint16_t)sv;
             if (in_lds) sm.scan.scores[ii] = (uint16_t)sv;
@@ -548,11 +623,15 @@ __device__ __forceinline__ void slot_score(const FusedArgs &a, const Slot &s, in
     }
 }
 
-// The chunk's histogram: its cumulative counts (bin by bin) go to the
-// chunk's row of chunk_hist, and its counts are added into the unit
-// histogram two bins per 64-bit atomic.
+// The item's histogram: its cumulative counts (bin by bin, tagged with the
+// unit's launch generation in the upper 32 bits) go to the item's row of
+// chunk_hist, and its counts are added into the unit histogram two bins per
+// 64-bit atomic.  Nothing waits for these writes: a reader knows the unit
+// histogram is complete when its counts sum to the context length, and a
+// row's entries are this launch's when they carry its tag.  Returns the
+// span's candidate cut.
 template <int G>
-__device__ __forceinline__ void slot_publish(const FusedArgs &a, const Slot &s, Smem<G> &sm) {
+__device__ __forceinline__ int slot_publish(const FusedArgs &a, const Slot &s, uint32_t gen, Smem<G> &sm) {
     constexpr int NB = G * kBits + 1;
     constexpr int NP = (NB + 1) / 2;
     constexpr int PER = (NB + kThreads - 1) / kThreads;
@@ -572,15 +651,25 @@ __device__ __forceinline__ void slot_publish(const FusedArgs &a, const Slot &s, 
         loc[e] = v;
         tsum += (int)v;
     }
+    if (t == 0) sm.scan.tc = NB - 1;
     int tot;
     int run = block_excl_scan_256(tsum, sm.scan.scan, &tot);  // its barriers publish hist[0]
-    uint32_t *ch = a.chunk_hist + ((int64_t)s.u * a.n_chunks + s.c) * NB;
+    // The candidate cut: the first bin at which the span's cumulative count
+    // reaches 1.5 times its proportional share of k_eff, plus 32.
+    const int n_span = (int)(s.p1 - s.p0);
+    const int64_t k_eff = step_keff(a, s.u / a.Hkv, s.sl.len);
+    const int64_t share = (k_eff * n_span + s.sl.len - 1) / s.sl.len;
+    const int64_t target = share + share / 2 + 32 < n_span ? share + share / 2 + 32 : n_span;
+    uint64_t *ch = a.chunk_hist + ((int64_t)s.u * a.n_chunks + s.c) * NB;
+    const uint64_t tag = (uint64_t)gen << 32;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
         const int bin = t * PER + e;
         if (bin < NB) {
+            const int before = run;
             run += (int)loc[e];
-            st_dev(ch + bin, (uint32_t)run);
+            st_dev(ch + bin, tag | (uint32_t)run);
+            if (before < target && run >= target) sm.scan.tc = bin;
         }
     }
     uint64_t *uh = reinterpret_cast<uint64_t *>(a.unit_hist) + (int64_t)s.u * NP;
@@ -591,19 +680,19 @@ __device__ __forceinline__ void slot_publish(const FusedArgs &a, const Slot &s, 
             __hip_atomic_fetch_add(uh + pr, (uint64_t)lo | ((uint64_t)hi << 32), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
     }
+    __syncthreads();
+    return sm.scan.tc;
 }
 
-// Thread 0 only: count one item of unit u finished.  The last item of a
-// unit resets the unit's counters and counts the unit done for its batch
-// entry; the last unit of an entry publishes the new length and resets the
-// entry counter.
-__device__ __forceinline__ void unit_finish(const FusedArgs &a, int u) {
-    drain_memory();
-    const int per_unit = kProParts + a.n_chunks;
-    if (add_dev(unit_ctr(a, u, kFin), 1) != per_unit - 1) return;
-    const int b = u / a.Hkv;
+// Thread 0 of the unit's last WORK item, after its merge: every item of the
+// unit is past its waits, so the unit's counters are reset for the next
+// launch and its generation advances; the last unit of a batch entry
+// publishes the entry's new length (no item of the entry reads it any
+// more).  Nothing here needs to complete before the kernel ends.
+__device__ __forceinline__ void unit_done(const FusedArgs &a, int u) {
     for (int w = 0; w < kNumCtr; ++w) st_dev(unit_ctr(a, u, w), 0);
-    drain_memory();
+    __hip_atomic_fetch_add(a.gen + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int b = u / a.Hkv;
     if (add_dev(batch_ctr(a, b), 1) != a.Hkv - 1) return;
     const StepLen sl = step_len(a, b);
     if (sl.app) st_dev(a.seq_len + b, (int32_t)(sl.l0 + 1));
@@ -611,29 +700,35 @@ __device__ __forceinline__ void unit_finish(const FusedArgs &a, int u) {
 }
 
 // Scan phase of work item (u, c): its span's codes in sub-batches of 16 KB,
-// two in flight at a time; the wait for the unit's query codes sits behind
-// the first two.  Scores go to the workspace, the histograms are published
-// and the unit's scan counter is bumped.
+// kScanDepth in flight; wave 0 fetches the unit's code words first (see
+// slot_fetch_qcodes) while the other waves' first sub-batches are on their
+// way.  Scores go to LDS (or the workspace), the histograms are published.
+// Returns the span's candidate cut; *gen gets the launch's tag.
 template <int G>
-__device__ __forceinline__ void scan_phase(const FusedArgs &a, const Slot &cur, Smem<G> &sm) {
+__device__ __forceinline__ int scan_phase(const FusedArgs &a, const Slot &cur, uint32_t &gen, Smem<G> &sm) {
     constexpr int NB = G * kBits + 1;
     const int n_sub = (int)((cur.p1 - cur.p0 + kSub * kThreads - 1) / (kSub * kThreads));
-    uvec4 bufA[kSub], bufB[kSub];
-    slot_issue(a, cur, 0, bufA);
-    slot_issue(a, cur, 1, bufB);
+    constexpr int D = kScanDepth;
+    const int wv = threadIdx.x >> 6;
+    uvec4 buf[D][kSub];
     for (int i = threadIdx.x; i < SmemScan<G>::NH * NB; i += kThreads) (&sm.scan.hist[0][0])[i] = 0u;
-    uint64_t qraw[G][2], app[2];
-    slot_begin<G>(a, cur, qraw, app);  // its barrier also orders the clearing
+    if (wv == 0) slot_fetch_qcodes<G>(a, cur, sm);
+#pragma unroll
+    for (int d = 0; d < D; ++d) slot_issue(a, cur, d, buf[d]);
+    __syncthreads();
+    gen = sm.scan.gen;
     uint32_t qc[G][4];
-    qcodes_sgpr<G>(qraw, qc);
-    for (int sb = 0; sb < n_sub; sb += 2) {
-        slot_score<G>(a, cur, sb, bufA, qc, app, sm);
-        if (sb + 2 < n_sub) slot_issue(a, cur, sb + 2, bufA);
-        slot_score<G>(a, cur, sb + 1, bufB, qc, app, sm);
-        if (sb + 3 < n_sub) slot_issue(a, cur, sb + 3, bufB);
+    qcodes_sgpr<G>(sm, qc);
+    QPlanes<G> qp;
+    query_planes<G>(qc, qp);
+    for (int sb = 0; sb < n_sub; sb += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            slot_score<G>(a, cur, sb + d, buf[d], qp, sm);
+            if (sb + d + D < n_sub) slot_issue(a, cur, sb + d + D, buf[d]);
+        }
     }
-    slot_publish<G>(a, cur, sm);
-    wg_signal(unit_ctr(a, cur.u, kScan));
+    return slot_publish<G>(a, cur, gen, sm);
 }
 
 // ---------------------------------------------------------------- selection phase
@@ -847,6 +942,157 @@ __device__ __forceinline__ uint4 load_scores8(const uint16_t *su, int64_t i0, in
     return make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
 }
 
+// Bit mask over eight packed u16 scores of those <= T (bit e: score e),
+// as in cut_masks.
+__device__ __forceinline__ uint32_t le_mask8(const uint4 &v, int T) {
+    const uint32_t hle = (uint32_t)(0x8000 + T) * 0x10001u;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t le = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t a = hle - (w[k] & 0x7FFF7FFFu);
+        le |= (((a >> 15) & 1u) << (2 * k)) | ((a >> 31) << (2 * k + 1));
+    }
+    return le;
+}
+
+// The span's keys with score <= tc (keys woff + 512 d + e, scores in pf),
+// as offsets in index order into sm.sel.list.  Returns their count; the
+// list is complete after the caller's next barrier.
+template <int G>
+__device__ __forceinline__ int list_candidates(const uint4 (&pf)[kSelRounds], int tc, int woff,
+                                               Smem<G> &sm) {
+    constexpr int D = kSelRounds;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    uint32_t le8[D];
+    int n = 0;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        le8[d] = le_mask8(pf[d], tc);
+        n += __popc(le8[d]);
+    }
+    const int wn = wave_sum64(n);
+    if (lane == 0) sm.sel.wlt[wv] = wn;
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+        const int c = sm.sel.wlt[w2];
+        base += w2 < wv ? c : 0;
+        total += c;
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        int tot;
+        int p = base + wave_excl_scan16(__popc(le8[d]), &tot);
+        const int o0 = woff + d * 512;
+        for (uint32_t mm = le8[d]; mm; mm &= mm - 1u) sm.sel.list[p++] = (uint16_t)(o0 + __builtin_ctz(mm));
+        base += tot;
+    }
+    return total;
+}
+
+// One selection batch (keys rb + woff + 512 d + e, scores in pf): the keys
+// below Tsel, and the score-Tsel keys while the split's running tie count
+// (ties_acc before the batch) is below rem_quota, written to sm.sel.list in
+// index order.  Returns the batch's selected count; *n_eq gets its count of
+// score-Tsel keys.  Ends with the list written by every thread but no
+// barrier after it.
+template <int G>
+__device__ __forceinline__ int select_batch(const uint4 (&pf)[kSelRounds], int Tsel, int64_t rem_quota,
+                                            int64_t ties_acc, int woff, Smem<G> &sm, int *n_eq) {
+    constexpr int D = kSelRounds;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    // pass 1: this lane's keys below Tsel and up to Tsel as bit masks (bit e
+    // of slot d: key woff + 512 d + e; past the end the words read as
+    // kNoScore, which is above every Tsel), and the wave's counts
+    uint32_t lt8[D], le8[D];
+    int n_e = 0, n_l = 0;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        cut_masks(pf[d], Tsel, le8[d], lt8[d]);
+        n_e += __popc(le8[d] & ~lt8[d]);
+        n_l += __popc(lt8[d]);
+    }
+    {
+        const int weq = wave_sum64(n_e), wlt = wave_sum64(n_l);
+        if (lane == 0) {
+            sm.sel.weq[wv] = weq;
+            sm.sel.wlt[wv] = wlt;
+        }
+    }
+    __syncthreads();
+    // this wave's place in the batch: ties and selections of the waves before it
+    int64_t tie_base = ties_acc;
+    int sel_base = 0, batch_sel = 0, batch_eq = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+        const int e2 = sm.sel.weq[w2], l2 = sm.sel.wlt[w2];
+        const int64_t tb = ties_acc + batch_eq;
+        int64_t take = rem_quota - tb;
+        take = take < 0 ? 0 : (take > e2 ? e2 : take);
+        const int sw = l2 + (int)take;
+        if (w2 < wv) {
+            tie_base += e2;
+            sel_base += sw;
+        }
+        batch_eq += e2;
+        batch_sel += sw;
+    }
+    // pass 2: select in index order (d, lane, e) and write the list.  The
+    // score-Tsel keys are taken in index order while the split's tie count
+    // is below rem_quota: a lane takes all or none of its ties, except the
+    // one lane where the quota runs out, which takes the lowest ones.
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        const uint32_t eq8 = le8[d] & ~lt8[d];
+        const int ne = __popc(eq8);
+        int ne_tot;
+        const int64_t tr = tie_base + wave_excl_scan16(ne, &ne_tot);
+        uint32_t sel8;
+        if (tr + ne <= rem_quota) {
+            sel8 = le8[d];
+        } else if (tr >= rem_quota) {
+            sel8 = lt8[d];
+        } else {
+            uint32_t take = 0, rest = eq8;
+            for (int q = (int)(rem_quota - tr); q > 0; --q) {
+                take |= rest & (0u - rest);  // lowest remaining tie
+                rest &= rest - 1u;
+            }
+            sel8 = lt8[d] | take;
+        }
+        int ns_tot;
+        int p = sel_base + wave_excl_scan16(__popc(sel8), &ns_tot);
+        const int o0 = woff + d * 512;
+        for (uint32_t mm = sel8; mm; mm &= mm - 1u) sm.sel.list[p++] = (uint16_t)(o0 + __builtin_ctz(mm));
+        tie_base += ne_tot;
+        sel_base += ns_tot;
+    }
+    *n_eq = batch_eq;
+    return batch_sel;
+}
+
+// Exclusive prefix count of a 0/1 flag over the 256 threads in thread
+// order; *total gets the count.  Two barriers; tmp holds four ints.
+__device__ __forceinline__ int block_excl_count(bool f, int *tmp, int *total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const uint64_t m = __ballot(f);
+    const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+    if (lane == 0) tmp[wv] = __popcll(m);
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+        const int c = tmp[w2];
+        base += w2 < wv ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + pre;
+}
+
 // Selection phase of work item (u, c), once every item of the unit has
 // scanned: the cut T from the unit histogram, the score-T and below-T keys
 // of the items before it from their cumulative histograms, then the span's
@@ -854,7 +1100,8 @@ __device__ __forceinline__ uint4 load_scores8(const uint16_t *su, int64_t i0, in
 // gathered and attended; the (m, l, o) partials of the items are merged in
 // item order by the last one.
 template <int G>
-__device__ __forceinline__ void sel_phase(const FusedArgs &a, const Slot &cur, Smem<G> &sm) {
+__device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, int tc, uint32_t gen,
+                                          Smem<G> &sm) {
     constexpr int D = kSelRounds;  // selection rounds of scores in flight
     constexpr int NB = G * kBits + 1;
     constexpr int PER = (NB + kThreads - 1) / kThreads;
@@ -865,62 +1112,129 @@ __device__ __forceinline__ void sel_phase(const FusedArgs &a, const Slot &cur, S
     const int64_t len = sl.len;
     const int64_t k_eff = step_keff(a, b, len);
     const int64_t s0 = cur.p0, s1 = cur.p1;
-    if (k_eff == 0) return;
     const int n_splits_u = (int)((len + a.span - 1) / a.span);
+    if (k_eff == 0) {  // the outputs are zero (written by PRO part 0)
+        const int prev = wg_signal(unit_ctr(a, u, kAttn));
+        if (t == 0) sm.sel.last = (prev == n_splits_u - 1);
+        __syncthreads();
+        return sm.sel.last;
+    }
 
     // the query heads as MFMA operands
     bf16x8 qa[4];
     load_q_operand<G>(a.q + ((int64_t)b * Hq + kv * G) * kHeadDim, qa);
-    wg_wait_geq(a, unit_ctr(a, u, kScan), n_splits_u);
 
-    // ---- the unit histogram and the first D rounds of this split's scores
     const uint16_t *su = a.scores + (int64_t)u * a.sstride;
     // batch layout: wave w holds keys [rb + 2048 w, rb + 2048 (w + 1)), lane
     // `lane` of it keys rb + 2048 w + 512 d + 8 lane + e (d < D, e < 8)
-    const int64_t woff = (int64_t)wv * (kSelRounds * kSelRound / 4) + 8 * lane;
+    const int woff = wv * (kSelRounds * kSelRound / 4) + 8 * lane;
     const bool in_lds = a.span <= kSpanUnit;
     uint4 pf[D];
 #pragma unroll
     for (int d = 0; d < D; ++d)
         pf[d] = in_lds ? lds_scores8(sm.sel.scores, woff + d * 512, s1 - s0)
                        : load_scores8(su, s0 + woff + (int64_t)d * 512, s1);
-    {
-        const uint32_t *uhr = a.unit_hist + (int64_t)u * (NB + 1);
-        uint32_t loc[PER];
-        int tsum = 0;
+    // ---- the unit histogram and a window of the earlier items' cumulative
+    // histograms (bins tc - kWin + 1 .. tc), requested before the candidate
+    // pass and read again until complete
+    const uint32_t *uhr = a.unit_hist + (int64_t)u * (NB + 1);
+    const uint64_t *chu = a.chunk_hist + (int64_t)u * a.n_chunks * NB;
+    const uint64_t tag = (uint64_t)gen << 32;
+    const int wlo = tc - (kWin - 1);
+    constexpr int WPT = kMaxSplits * kWin / kThreads;
+    uint32_t loc[PER];
+    uint64_t win[WPT];
+    auto read_state = [&]() {
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
             const int bin = t * PER + e;
             loc[e] = bin < NB ? ld_dev(uhr + bin) : 0u;
-            tsum += (int)loc[e];
         }
+#pragma unroll
+        for (int k = 0; k < WPT; ++k) {
+            const int i = t + k * kThreads, cc = i / kWin, bin = wlo + i % kWin;
+            win[k] = (cc < s && bin >= 0) ? ld_dev(chu + (int64_t)cc * NB + bin) : tag;
+        }
+    };
+    read_state();
+    // ---- meanwhile the span's candidates: every key up to the candidate
+    // cut tc, in index order (spans kept in LDS)
+    const int n_cand = in_lds ? list_candidates<G>(pf, tc, woff, sm) : -1;
+    // ---- the cut T, once every item of the unit has added its counts
+    // (they then sum to len)
+    for (int spins = 0;; ++spins) {
+        int tsum = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) tsum += (int)loc[e];
         if (t == 0) {
             sm.sel.T = NB - 1;
             sm.sel.below = 0;
         }
         int tot;
         int run = block_excl_scan_256(tsum, sm.sel.scan, &tot);
-        // the cut T: first bin whose cumulative count reaches k_eff (the
-        // counts sum to len >= k_eff); below: the count under T
+        if ((int64_t)tot >= len) {
+            // T: first bin whose cumulative count reaches k_eff; below: the
+            // count under T
 #pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int nxt = run + (int)loc[e];
-            if ((int64_t)run < k_eff && (int64_t)nxt >= k_eff) {
-                sm.sel.T = t * PER + e;
-                sm.sel.below = run;
+            for (int e = 0; e < PER; ++e) {
+                const int nxt = run + (int)loc[e];
+                if ((int64_t)run < k_eff && (int64_t)nxt >= k_eff) {
+                    sm.sel.T = t * PER + e;
+                    sm.sel.below = run;
+                }
+                run = nxt;
             }
-            run = nxt;
+            break;
         }
-        __syncthreads();
+        if (spins > kPollLimit) {
+            if (t == 0) atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_STALL);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        read_state();
     }
+    __syncthreads();
     const int T = sm.sel.T;
-    // ---- score-T and below-T keys in the chunks before this split
+    // ---- score-T and below-T keys in the items before this one: from the
+    // window when it holds bins T - 1 and T, else read (again) until every
+    // entry carries this launch's tag
     long long tie = 0, lo = 0;
-    for (int cc = t; cc < s; cc += kThreads) {
-        const uint32_t *chc = a.chunk_hist + ((int64_t)u * a.n_chunks + cc) * NB;
-        const uint32_t l = T > 0 ? ld_dev(chc + T - 1) : 0u;
-        tie += (long long)ld_dev(chc + T) - l;
-        lo += l;
+    const bool in_win = T <= tc && (T == 0 ? wlo <= 0 : T - 1 >= wlo);
+    int bad = 0;
+    if (in_win) {
+#pragma unroll
+        for (int k = 0; k < WPT; ++k) {
+            const int i = t + k * kThreads, cc = i / kWin, bin = wlo + i % kWin;
+            if (cc < s) {
+                bad |= (win[k] & ~0xFFFFFFFFull) != tag;
+                const long long cum = (uint32_t)win[k];
+                if (bin == T) tie += cum;
+                if (bin == T - 1) {
+                    tie -= cum;
+                    lo += cum;
+                }
+            }
+        }
+    }
+    if (!in_win || __syncthreads_or(bad)) {
+        for (int spins = 0;; ++spins) {
+            tie = lo = 0;
+            bad = 0;
+            for (int cc = t; cc < s; cc += kThreads) {
+                const uint64_t *chc = chu + (int64_t)cc * NB;
+                const uint64_t h = ld_dev(chc + T);
+                const uint64_t l = T > 0 ? ld_dev(chc + T - 1) : tag;
+                bad |= ((h & ~0xFFFFFFFFull) != tag) | ((l & ~0xFFFFFFFFull) != tag);
+                tie += (long long)(uint32_t)h - (long long)(uint32_t)l;
+                lo += (uint32_t)l;
+            }
+            if (!__syncthreads_or(bad)) break;
+            if (spins > kPollLimit) {
+                if (t == 0) atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_STALL);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
     }
     const int64_t ties_b = block_sum_256(tie, sm.sel.red);
     const int64_t below_b = block_sum_256(lo, sm.sel.red);
@@ -942,93 +1256,79 @@ __device__ __forceinline__ void sel_phase(const FusedArgs &a, const Slot &cur, S
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) o[h][0] = o[h][1] = 0.f;
-    int64_t ties_acc = 0;
-    for (int64_t rb = s0; rb < s1; rb += kListCap) {
-        // pass 1: this lane's keys below T and up to T as bit masks (bit e of
-        // slot d: key woff + 512 d + e; past s1 the words read as kNoScore,
-        // which is above every T), and the wave's counts
-        uint32_t lt8[D], le8[D];
-        int n_eq = 0, n_lt = 0;
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            cut_masks(pf[d], T, le8[d], lt8[d]);
-            n_eq += __popc(le8[d] & ~lt8[d]);
-            n_lt += __popc(lt8[d]);
-        }
-        {
-            const int weq = wave_sum64(n_eq), wlt = wave_sum64(n_lt);
+    if (n_cand >= 0 && T <= tc) {
+        // ---- the selection is among the candidates: keep those below T and
+        // the first rem_quota of score T (index order), compacting the list
+        // in place (a kept entry moves to a position <= its own)
+        int n_sel = 0;
+        int64_t ties_acc = 0;
+        for (int i0 = 0; i0 < n_cand; i0 += kThreads) {
+            const int i = i0 + t;
+            const int off = i < n_cand ? (int)sm.sel.list[i] : 0;
+            const int sc = i < n_cand ? (int)sm.sel.scores[off] : 0x7FFF;
+            const uint64_t mlt = __ballot(sc < T), meq = __ballot(sc == T);
+            const int lt_pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(mlt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mlt, 0));
+            const int eq_pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(meq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)meq, 0));
             if (lane == 0) {
-                sm.sel.weq[wv] = weq;
-                sm.sel.wlt[wv] = wlt;
+                sm.sel.wlt[wv] = __popcll(mlt);
+                sm.sel.weq[wv] = __popcll(meq);
             }
-        }
-        __syncthreads();
-        // this wave's place in the batch: ties and selections of the waves before it
-        int64_t tie_base = ties_acc;
-        int sel_base = 0, batch_sel = 0, batch_eq = 0;
+            __syncthreads();
+            int lt_b = 0, eq_b = 0, lt_tot = 0, eq_tot = 0;
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-            const int e2 = sm.sel.weq[w2], l2 = sm.sel.wlt[w2];
-            const int64_t tb = ties_acc + batch_eq;
-            int64_t take = rem_quota - tb;
-            take = take < 0 ? 0 : (take > e2 ? e2 : take);
-            const int sw = l2 + (int)take;
-            if (w2 < wv) {
-                tie_base += e2;
-                sel_base += sw;
+            for (int w2 = 0; w2 < 4; ++w2) {
+                const int cl = sm.sel.wlt[w2], ce = sm.sel.weq[w2];
+                lt_b += w2 < wv ? cl : 0;
+                eq_b += w2 < wv ? ce : 0;
+                lt_tot += cl;
+                eq_tot += ce;
             }
-            batch_eq += e2;
-            batch_sel += sw;
-        }
-        // pass 2: select in index order (d, lane, e) and write the list.  The
-        // score-T keys are taken in index order while the split's tie count
-        // is below rem_quota: a lane takes all or none of its ties, except
-        // the one lane where the quota runs out, which takes the lowest ones.
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const uint32_t eq8 = le8[d] & ~lt8[d];
-            const int ne = __popc(eq8);
-            int ne_tot;
-            const int64_t tr = tie_base + wave_excl_scan16(ne, &ne_tot);
-            uint32_t sel8;
-            if (tr + ne <= rem_quota) {
-                sel8 = le8[d];
-            } else if (tr >= rem_quota) {
-                sel8 = lt8[d];
-            } else {
-                uint32_t take = 0, rest = eq8;
-                for (int q = (int)(rem_quota - tr); q > 0; --q) {
-                    take |= rest & (0u - rest);  // lowest remaining tie
-                    rest &= rest - 1u;
-                }
-                sel8 = lt8[d] | take;
-            }
-            int ns_tot;
-            int p = sel_base + wave_excl_scan16(__popc(sel8), &ns_tot);
-            const int o0 = (int)woff + d * 512;
-            for (uint32_t mm = sel8; mm; mm &= mm - 1u) sm.sel.list[p++] = (uint16_t)(o0 + __builtin_ctz(mm));
-            tie_base += ne_tot;
-            sel_base += ns_tot;
-        }
-        // the next batch's scores are on their way during this one's attention
-        if (rb + kListCap < s1) {
-#pragma unroll
-            for (int d = 0; d < D; ++d) pf[d] = load_scores8(su, rb + kListCap + woff + (int64_t)d * 512, s1);
+            const int64_t room = rem_quota - ties_acc > 0 ? rem_quota - ties_acc : 0;  // score-T keys still to take
+            const int eq_before = eq_b + eq_pre;
+            const bool take = sc < T || (sc == T && eq_before < room);
+            const int pos = n_sel + lt_b + lt_pre + (int)(eq_before < room ? eq_before : room);
+            __syncthreads();  // every entry of this round read, the counts too
+            if (take) sm.sel.list[pos] = (uint16_t)off;
+            n_sel += lt_tot + (int)(eq_tot < room ? eq_tot : room);
+            ties_acc += eq_tot;
         }
         __syncthreads();
         if (sel_u) {
-            for (int i = t; i < batch_sel; i += kThreads) {
+            for (int i = t; i < n_sel; i += kThreads) {
                 const int64_t gp = out_pos + i;
-                if (gp >= 0 && gp < a.k_max) sel_u[gp] = (int32_t)(rb + sm.sel.list[i]);
+                if (gp >= 0 && gp < a.k_max) sel_u[gp] = (int32_t)(s0 + sm.sel.list[i]);
             }
         }
-        out_pos += batch_sel;
-        ties_acc += batch_eq;
-        // the batch's selections through the attention
-        const int app_off = (app_row >= rb && app_row < rb + kListCap) ? (int)(app_row - rb) : -1;
-        attend_mfma<G>(Ku + rb * kHeadDim, Vu + rb * kHeadDim, kapp, vapp, app_off, sm.sel.list,
-                       batch_sel, qa, sm.sel.pb[wv], m, l, o);
+        const int app_off = (app_row >= s0 && app_row < s1) ? (int)(app_row - s0) : -1;
+        attend_mfma<G>(Ku + s0 * kHeadDim, Vu + s0 * kHeadDim, kapp, vapp, app_off, sm.sel.list,
+                       n_sel, qa, sm.sel.pb[wv], m, l, o);
         __syncthreads();
+    } else {
+        if (n_cand >= 0) __syncthreads();  // the candidate list is read no further
+        int64_t ties_acc = 0;
+        for (int64_t rb = s0; rb < s1; rb += kListCap) {
+            int batch_eq;
+            const int batch_sel = select_batch<G>(pf, T, rem_quota, ties_acc, woff, sm, &batch_eq);
+            // the next batch's scores are on their way during this one's attention
+            if (rb + kListCap < s1) {
+#pragma unroll
+                for (int d = 0; d < D; ++d) pf[d] = load_scores8(su, rb + kListCap + woff + (int64_t)d * 512, s1);
+            }
+            __syncthreads();
+            if (sel_u) {
+                for (int i = t; i < batch_sel; i += kThreads) {
+                    const int64_t gp = out_pos + i;
+                    if (gp >= 0 && gp < a.k_max) sel_u[gp] = (int32_t)(rb + sm.sel.list[i]);
+                }
+            }
+            out_pos += batch_sel;
+            ties_acc += batch_eq;
+            // the batch's selections through the attention
+            const int app_off = (app_row >= rb && app_row < rb + kListCap) ? (int)(app_row - rb) : -1;
+            attend_mfma<G>(Ku + rb * kHeadDim, Vu + rb * kHeadDim, kapp, vapp, app_off, sm.sel.list,
+                           batch_sel, qa, sm.sel.pb[wv], m, l, o);
+            __syncthreads();
+        }
     }
 
     // ---- the waves' states into LDS, then combined per output
@@ -1066,7 +1366,7 @@ __device__ __forceinline__ void sel_phase(const FusedArgs &a, const Slot &cur, S
     const int prev = wg_signal(unit_ctr(a, u, kAttn));
     if (t == 0) sm.sel.last = (prev == n_splits_u - 1);
     __syncthreads();
-    if (!sm.sel.last) return;
+    if (!sm.sel.last) return false;
     // Per split x and head h: weight w = exp2(m_x - M) with M the maximum
     // over splits; out = sum_x w o_x / sum_x w l_x.  Output pair pr (floats
     // 2 pr, 2 pr + 1 of the G x 128 block) is thread pr's; its partials are
@@ -1141,7 +1441,7 @@ __device__ __forceinline__ void sel_phase(const FusedArgs &a, const Slot &cur, S
             o[1] = L > 0.f ? f32_to_bf16(O[k][1] / L) : (uint16_t)0;
         }
     }
-    __syncthreads();
+    return true;
 }
 
 // ---------------------------------------------------------------- item order
@@ -1169,9 +1469,10 @@ template <int G>
 __device__ __forceinline__ void item_work(const FusedArgs &a, int u, int c, Smem<G> &sm) {
     const Slot cur = slot_of(a, u, c);
     if (cur.p0 >= cur.p1) return;
-    scan_phase<G>(a, cur, sm);
+    uint32_t gen;
+    const int tc = scan_phase<G>(a, cur, gen, sm);
     __syncthreads();  // the LDS histograms and the selection state share memory
-    sel_phase<G>(a, cur, sm);
+    if (sel_phase<G>(a, cur, tc, gen, sm) && threadIdx.x == 0) unit_done(a, u);
 }
 
 // Three workgroups per CU (two for G = 8): the register budget the
@@ -1182,8 +1483,6 @@ __global__ __launch_bounds__(kThreads, G <= 4 ? 3 : 2) void k_decode_fused(Fused
     const Item it = item_of(a, blockIdx.x);
     if (it.kind == 0) item_pro<G>(a, it.u, it.i, sm);
     else item_work<G>(a, it.u, it.i, sm);
-    __syncthreads();
-    if (threadIdx.x == 0) unit_finish(a, it.u);
 }
 
 // ---------------------------------------------------------------- plan + launch
@@ -1215,12 +1514,14 @@ bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, DecodePlan *p) {
     d.n_items = (int)items;
     d.sstride = ((max_ctx + 63) / 64) * 64;
     size_t off = 0;
-    d.off_qcodes = off;
-    off = align256(off + (size_t)B * Hq * kWords * 4);
+    d.off_gen = off;
+    off = align256(off + (size_t)units * 4);
+    d.off_qtag = off;
+    off = align256(off + (size_t)units * (G + 1) * kWords * 8);
     d.off_unit_hist = off;
     off = align256(off + (size_t)units * (d.NB + 1) * 4);
     d.off_chunk_hist = off;
-    off = align256(off + (size_t)units * d.n_chunks * d.NB * 4);
+    off = align256(off + (size_t)units * d.n_chunks * d.NB * 8);
     d.off_part_ml = off;
     off = align256(off + (size_t)units * d.n_chunks * G * 2 * 4);
     d.off_part_o = off;
@@ -1245,7 +1546,7 @@ hipError_t launch_decode(const DecodePlan &p, uint16_t *k_cache, uint16_t *v_cac
                          const float *w, const int32_t *topk, int k_max, uint16_t *out, void *ws,
                          int32_t *sel_idx_out, uint16_t *scores_out, hipStream_t s) {
     char *base = static_cast<char *>(ws);
-    FusedArgs a;
+    FusedArgs a{};
     a.k_cache = k_cache;
     a.v_cache = v_cache;
     a.codes = codes;
@@ -1261,9 +1562,10 @@ hipError_t launch_decode(const DecodePlan &p, uint16_t *k_cache, uint16_t *v_cac
     a.scores_dbg = scores_out;
     a.scores = reinterpret_cast<uint16_t *>(base + p.off_scores);
     a.sstride = p.sstride;
-    a.qcodes = reinterpret_cast<uint32_t *>(base + p.off_qcodes);
+    a.gen = reinterpret_cast<uint32_t *>(base + p.off_gen);
+    a.qtag = reinterpret_cast<uint64_t *>(base + p.off_qtag);
     a.unit_hist = reinterpret_cast<uint32_t *>(base + p.off_unit_hist);
-    a.chunk_hist = reinterpret_cast<uint32_t *>(base + p.off_chunk_hist);
+    a.chunk_hist = reinterpret_cast<uint64_t *>(base + p.off_chunk_hist);
     a.part_ml = reinterpret_cast<float *>(base + p.off_part_ml);
     a.part_o = reinterpret_cast<float *>(base + p.off_part_o);
     a.max_ctx = p.max_ctx;

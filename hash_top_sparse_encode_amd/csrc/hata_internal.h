@@ -30,7 +30,7 @@ struct DecodePlan {
     int n_chunks = 0;    // work items per unit: ceil(max_ctx / span)
     int n_items = 0;     // workgroups of the launch
     int64_t sstride = 0; // score row stride (elements) in the workspace
-    size_t off_qcodes = 0, off_unit_hist = 0, off_chunk_hist = 0, off_part_ml = 0,
+    size_t off_gen = 0, off_qtag = 0, off_unit_hist = 0, off_chunk_hist = 0, off_part_ml = 0,
            off_part_o = 0, off_scores = 0, total = 0;
 };
 

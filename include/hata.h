@@ -174,7 +174,12 @@ size_t hata_decode_workspace_bytes(const hata_cache *c, int32_t k_max);
  *   k_max      host upper bound of the budget, >= 0.
  *   out        device bf16 [batch][n_q_heads][128]; zero where k_eff = 0.
  *   workspace  device, >= hata_decode_workspace_bytes(c, k_max) bytes,
- *              256-byte aligned; contents need no initialisation.
+ *              256-byte aligned, zero-filled by the caller before its first
+ *              use (and again after a call that set HATA_DEV_STALL).  It
+ *              holds per-(sequence, KV head) launch counters that tag each
+ *              call's intermediate results, so one workspace may serve
+ *              several caches (layers) whose calls are ordered; the caller
+ *              does not write it after the zero fill.
  *   sel_idx_out optional device int32 [batch][n_kv_heads][k_max]: the
  *              selected indices in ascending order, -1 after k_eff.
  *   scores_out optional device u16 [batch][n_kv_heads][max_ctx]: the

@@ -129,6 +129,28 @@ def test_fused_matches_two_calls(gpu):
     assert a.cache.status() == 0 and b.cache.status() == 0
     # counters are back at zero after each call
     assert int(a.cache.ctrl[1:].abs().sum().item()) == 0
+    assert int(b.cache.ctrl[1:].abs().sum().item()) == 0
+
+
+def test_workspace_shared_by_caches(gpu):
+    # Caches (layers) whose calls are ordered may share one workspace: call
+    # after call, alternating between two caches, the results equal those of
+    # the same caches each with a workspace of its own.
+    specs = [synth.custom(f"ws {i}", 2, 8, 2, [9000, 3100], [140, 48], [9, 3], seed=31 + i)
+             for i in range(2)]
+    own = [GpuWorkload(s, gpu, extra_ctx=4) for s in specs]
+    shared = [GpuWorkload(s, gpu, extra_ctx=4) for s in specs]
+    for w in shared[1:]:
+        w.ws = shared[0].ws
+    for r in range(3):
+        for i in range(2):
+            oa, sa, ca = own[i].step(debug=(r == 1))
+            ob, sb, cb = shared[i].step(debug=(r == 1))
+            torch.cuda.synchronize()
+            assert torch.equal(oa.view(torch.int16), ob.view(torch.int16)), (r, i)
+            if r == 1:
+                assert torch.equal(sa, sb) and torch.equal(ca, cb), (r, i)
+            assert own[i].cache.status() == 0 and shared[i].cache.status() == 0
 
 
 FAST = [synth.config(1), FUZZ[2], FUZZ[3],
