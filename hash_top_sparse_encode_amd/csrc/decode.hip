@@ -231,14 +231,23 @@ struct SmemScan {
     uint32_t gen;             // the unit's launch generation
 };
 
+// A wave's staged V rows: 64 dims (128 B) of each of 32 keys, rows 144 B
+// apart so that the transposed reads of four rows fall in distinct banks.
+constexpr int kVRow = 72;
+
 template <int G>
 struct SmemSel {
-    uint16_t scores[kSpanUnit];
+    union {
+        uint16_t scores[kSpanUnit];    // the span's scores, until the selection is made
+        uint16_t vst[4][32][kVRow];    // attention: each wave's V rows, half a row at a time
+        struct {
+            float wm[4][G];
+            float wl[4][G];
+            float wo[4][G][kHeadDim];
+        } cb;                          // after the attention: each wave's (m, l, o)
+    };
     uint16_t list[kListCap];  // selected keys of a batch, as offsets from its first key
-    float pb[4][32 * G];      // per wave: softmax numerators of its 32 keys of a round
-    float wm[4][G];
-    float wl[4][G];
-    float wo[4][G][kHeadDim];
+    uint16_t pb[4][2][G][32]; // per wave: softmax numerators as bf16 high and low parts
     float mw[kMaxSplits][G];  // merge: per-split maxima, then weights
     float lv[kMaxSplits][G];  // merge: per-split sums
     float ml[G];
@@ -771,22 +780,37 @@ __device__ __forceinline__ void load_q_operand(const uint16_t *qg, bf16x8 (&qa)[
     }
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Four 16-bit values of four consecutive rows of a staged V tile, transposed
+// by the LDS (ds_read_b64_tr_b16): within each 16-lane group, lane i
+// receives element i % 4 of the 64-bit pieces addressed by lanes i / 4,
+// i / 4 + 4, i / 4 + 8 and i / 4 + 12.
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(p));
+}
+
 // Attention over the rows Kb / Vb + list[0..n) (offsets from a batch's first
 // key; the row at offset app_off is this step's appended key, read from
 // kapp / vapp).  Each wave takes 32 keys of every 128: logits of two 16-key
 // tiles by MFMA (lane (g, c) brings dims 32 g .. 32 g + 32 of key c of a
 // tile; its accumulator holds heads 4 g .. 4 g + 3 of key c), an online
 // softmax in base 2 per head (running m, l per lane for its four heads), and
-// P.V on the vector units with every lane holding dims 2 lane, 2 lane + 1 of
-// each row.  Loads of a round are all issued before any is used.
+// P.V by MFMA as well: P (heads x 32 keys) in bf16 high and low parts
+// through LDS as the A operand, V staged in LDS half a row at a time and
+// read back transposed as the B operand (lane (g, n) gets keys 8 g .. 8 g + 7
+// of dim n of a 16-dim block).  oacc[blk] holds O[4 g + i][16 blk + n] in
+// lane (g, n).  Loads of a round are all issued before any is used.
 template <int G>
 __device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
                                             const uint16_t *__restrict__ Vb,
                                             const uint16_t *__restrict__ kapp,
                                             const uint16_t *__restrict__ vapp, int app_off,
                                             const uint16_t *list, int n, const bf16x8 (&qa)[4],
-                                            float *pw, float (&m)[4], float (&lsum)[4],
-                                            float (&o)[G][2]) {
+                                            uint16_t (*vst)[kVRow], uint16_t (*pb)[G][32],
+                                            float (&m)[4], float (&lsum)[4], f32x4 (&oacc)[8]) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, grp = lane >> 4, c = lane & 15;
     constexpr float kScale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
     for (int base = 32 * wv; base < n; base += 128) {
@@ -804,17 +828,16 @@ __device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
                 if (off >= 0) kr[tau][j] = *reinterpret_cast<const uvec4 *>(row + 32 * grp + 8 * j);
             }
         }
-        // V rows: dims 2 lane, 2 lane + 1 of each of the kc keys
-        const int offl = lane < kc ? (int)list[base + lane] : -1;
-        uint32_t vr[32];
+        // V rows in 16-byte pieces: piece r of lane l is key (l >> 3) + 8 (r >> 1),
+        // dims 8 (l & 7) + 64 (r & 1) .. + 8
+        uvec4 vv[8];
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
-            vr[k] = 0u;
-            const int off = __builtin_amdgcn_readlane(offl, k);
-            if (k < kc) {
-                const uint16_t *row = off == app_off ? vapp : Vb + off * kHeadDim;
-                vr[k] = *reinterpret_cast<const uint32_t *>(row + 2 * lane);
-            }
+        for (int r = 0; r < 8; ++r) {
+            const int key = (lane >> 3) + 8 * (r >> 1);
+            const int off = key < kc ? (int)list[base + key] : -1;
+            const uint16_t *row = off == app_off ? vapp : Vb + off * kHeadDim;
+            vv[r] = uvec4{0u, 0u, 0u, 0u};
+            if (off >= 0) vv[r] = *reinterpret_cast<const uvec4 *>(row + 8 * (lane & 7) + 64 * (r & 1));
         }
         // logits
         f32x4 acc[2];
@@ -826,8 +849,8 @@ __device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
                 acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], __builtin_bit_cast(bf16x8, kr[tau][j]),
                                                                    acc[tau], 0, 0, 0);
         }
-        // online softmax for this lane's heads 4 grp + i
-        float alv[4];
+        // online softmax for this lane's heads 4 grp + i; P to LDS as bf16
+        // high and low parts ([head][key])
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bool hv = 4 * grp + i < G;
@@ -838,32 +861,41 @@ __device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
             const float p0 = (z0 == -INFINITY) ? 0.f : exp2f(z0 - M);
             const float p1 = (z1 == -INFINITY) ? 0.f : exp2f(z1 - M);
             lsum[i] = lsum[i] * al + row16_sum(p0 + p1);
+            // the accumulators are zero until the wave has seen a key
+            if (__ballot(m[i] != -INFINITY) != 0) {
+#pragma unroll
+                for (int blk = 0; blk < 8; ++blk) oacc[blk][i] *= al;
+            }
             m[i] = M;
-            alv[i] = al;
             if (hv) {
-                pw[c * G + 4 * grp + i] = p0;
-                pw[(16 + c) * G + 4 * grp + i] = p1;
+                const int h = (4 * grp + i) % G;
+                const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;  // round to nearest even
+                pb[0][h][c] = __builtin_bit_cast(uint16_t, h0);
+                pb[0][h][16 + c] = __builtin_bit_cast(uint16_t, h1);
+                pb[1][h][c] = __builtin_bit_cast(uint16_t, (__bf16)(p0 - (float)h0));
+                pb[1][h][16 + c] = __builtin_bit_cast(uint16_t, (__bf16)(p1 - (float)h1));
             }
         }
-        // rescale the accumulators (head h's factor lives in lane 16 (h / 4))
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float al =
-                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alv[h & 3]), 16 * (h >> 2)));
-            o[h][0] *= al;
-            o[h][1] *= al;
+        // P as the A operand: lane l holds head l % 16, keys 8 (l >> 4) .. + 8
+        uvec4 pa[2] = {uvec4{0u, 0u, 0u, 0u}, uvec4{0u, 0u, 0u, 0u}};
+        if (c < G) {
+            pa[0] = *reinterpret_cast<const uvec4 *>(&pb[0][c][8 * grp]);
+            pa[1] = *reinterpret_cast<const uvec4 *>(&pb[1][c][8 * grp]);
         }
-        // P.V
+        const bf16x8 ph = __builtin_bit_cast(bf16x8, pa[0]), pl = __builtin_bit_cast(bf16x8, pa[1]);
+        // P.V, half a V row at a time through LDS
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
-            if (k < kc) {
-                const float v0 = __uint_as_float(vr[k] << 16), v1 = __uint_as_float(vr[k] & 0xFFFF0000u);
+        for (int half = 0; half < 2; ++half) {
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float pk = pw[k * G + h];
-                    o[h][0] = fmaf(pk, v0, o[h][0]);
-                    o[h][1] = fmaf(pk, v1, o[h][1]);
-                }
+            for (int rr = 0; rr < 4; ++rr)
+                *reinterpret_cast<uvec4 *>(&vst[(lane >> 3) + 8 * rr][8 * (lane & 7)]) = vv[2 * rr + half];
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                const uint16_t *src = &vst[8 * grp + (c >> 2)][16 * blk + 4 * (c & 3)];
+                const s16x4 b0 = lds_read_tr16(src), b1 = lds_read_tr16(src + 4 * kVRow);
+                const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[4 * half + blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, oacc[4 * half + blk], 0, 0, 0);
+                oacc[4 * half + blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, oacc[4 * half + blk], 0, 0, 0);
             }
         }
     }
@@ -1248,14 +1280,15 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     const int64_t app_row = sl.app ? sl.l0 : -1;
     const uint16_t *kapp = sl.app ? a.k_new + ((int64_t)b * a.Hkv + kv) * kHeadDim : nullptr;
     const uint16_t *vapp = sl.app ? a.v_new + ((int64_t)b * a.Hkv + kv) * kHeadDim : nullptr;
-    float m[4], l[4], o[G][2];
+    float m[4], l[4];
+    f32x4 o[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         m[i] = -INFINITY;
         l[i] = 0.f;
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) o[h][0] = o[h][1] = 0.f;
+    for (int blk = 0; blk < 8; ++blk) o[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (n_cand >= 0 && T <= tc) {
         // ---- the selection is among the candidates: keep those below T and
         // the first rem_quota of score T (index order), compacting the list
@@ -1301,7 +1334,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
         }
         const int app_off = (app_row >= s0 && app_row < s1) ? (int)(app_row - s0) : -1;
         attend_mfma<G>(Ku + s0 * kHeadDim, Vu + s0 * kHeadDim, kapp, vapp, app_off, sm.sel.list,
-                       n_sel, qa, sm.sel.pb[wv], m, l, o);
+                       n_sel, qa, sm.sel.vst[wv], sm.sel.pb[wv], m, l, o);
         __syncthreads();
     } else {
         if (n_cand >= 0) __syncthreads();  // the candidate list is read no further
@@ -1326,7 +1359,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
             // the batch's selections through the attention
             const int app_off = (app_row >= rb && app_row < rb + kListCap) ? (int)(app_row - rb) : -1;
             attend_mfma<G>(Ku + rb * kHeadDim, Vu + rb * kHeadDim, kapp, vapp, app_off, sm.sel.list,
-                           batch_sel, qa, sm.sel.pb[wv], m, l, o);
+                           batch_sel, qa, sm.sel.vst[wv], sm.sel.pb[wv], m, l, o);
             __syncthreads();
         }
     }
@@ -1335,24 +1368,33 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         if (lane == 16 * (h >> 2)) {
-            sm.sel.wm[wv][h] = m[h & 3];
-            sm.sel.wl[wv][h] = l[h & 3];
+            sm.sel.cb.wm[wv][h] = m[h & 3];
+            sm.sel.cb.wl[wv][h] = l[h & 3];
         }
-        sm.sel.wo[wv][h][2 * lane] = o[h][0];
-        sm.sel.wo[wv][h][2 * lane + 1] = o[h][1];
+    }
+    // lane (g, n) holds O[4 g + i][16 blk + n]
+    if ((lane >> 4) < (G + 3) / 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * (lane >> 4) + i;
+            if (h < G) {
+#pragma unroll
+                for (int blk = 0; blk < 8; ++blk) sm.sel.cb.wo[wv][h][16 * blk + (lane & 15)] = o[blk][i];
+            }
+        }
     }
     __syncthreads();
     float *pml = a.part_ml + ((int64_t)u * a.n_chunks + s) * G * 2;
     float *po = a.part_o + ((int64_t)u * a.n_chunks + s) * G * kHeadDim;
     for (int pr = t; pr < G * kHeadDim; pr += kThreads) {
         const int h = pr / kHeadDim, e = pr % kHeadDim;
-        float M = sm.sel.wm[0][h], L = sm.sel.wl[0][h], O = sm.sel.wo[0][h][e];
+        float M = sm.sel.cb.wm[0][h], L = sm.sel.cb.wl[0][h], O = sm.sel.cb.wo[0][h][e];
 #pragma unroll
         for (int w2 = 1; w2 < 4; ++w2) {
             float Mn, a1, a2;
-            lse_weights(M, sm.sel.wm[w2][h], &Mn, &a1, &a2);
-            L = L * a1 + sm.sel.wl[w2][h] * a2;
-            O = O * a1 + sm.sel.wo[w2][h][e] * a2;
+            lse_weights(M, sm.sel.cb.wm[w2][h], &Mn, &a1, &a2);
+            L = L * a1 + sm.sel.cb.wl[w2][h] * a2;
+            O = O * a1 + sm.sel.cb.wo[w2][h][e] * a2;
             M = Mn;
         }
         st_dev(po + pr, O);
