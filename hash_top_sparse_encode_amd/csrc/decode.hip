@@ -231,15 +231,11 @@ struct SmemScan {
     uint32_t gen;             // the unit's launch generation
 };
 
-// A wave's staged V rows: 64 dims (128 B) of each of 32 keys, rows 144 B
-// apart so that the transposed reads of four rows fall in distinct banks.
-constexpr int kVRow = 72;
-
 template <int G>
 struct SmemSel {
     union {
         uint16_t scores[kSpanUnit];    // the span's scores, until the selection is made
-        uint16_t vst[4][32][kVRow];    // attention: each wave's V rows, half a row at a time
+        uint16_t vst[4][32][kHeadDim]; // attention: each wave's V rows of a round
         struct {
             float wm[4][G];
             float wl[4][G];
@@ -799,7 +795,7 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
 // tile; its accumulator holds heads 4 g .. 4 g + 3 of key c), an online
 // softmax in base 2 per head (running m, l per lane for its four heads), and
 // P.V by MFMA as well: P (heads x 32 keys) in bf16 high and low parts
-// through LDS as the A operand, V staged in LDS half a row at a time and
+// through LDS as the A operand, the V rows staged in LDS as they arrive and
 // read back transposed as the B operand (lane (g, n) gets keys 8 g .. 8 g + 7
 // of dim n of a 16-dim block).  oacc[blk] holds O[4 g + i][16 blk + n] in
 // lane (g, n).  Loads of a round are all issued before any is used.
@@ -809,7 +805,7 @@ __device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
                                             const uint16_t *__restrict__ kapp,
                                             const uint16_t *__restrict__ vapp, int app_off,
                                             const uint16_t *list, int n, const bf16x8 (&qa)[4],
-                                            uint16_t (*vst)[kVRow], uint16_t (*pb)[G][32],
+                                            uint16_t (*vst)[kHeadDim], uint16_t (*pb)[G][32],
                                             float (&m)[4], float (&lsum)[4], f32x4 (&oacc)[8]) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, grp = lane >> 4, c = lane & 15;
     constexpr float kScale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
@@ -828,16 +824,21 @@ __device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
                 if (off >= 0) kr[tau][j] = *reinterpret_cast<const uvec4 *>(row + 32 * grp + 8 * j);
             }
         }
-        // V rows in 16-byte pieces: piece r of lane l is key (l >> 3) + 8 (r >> 1),
-        // dims 8 (l & 7) + 64 (r & 1) .. + 8
-        uvec4 vv[8];
+        // V rows in 16-byte pieces: piece r of lane l is key (l >> 4) + 4 r,
+        // dims 8 (l & 15) .. + 8; staged in LDS as they arrive
+        {
+            uvec4 vv[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int key = (lane >> 3) + 8 * (r >> 1);
-            const int off = key < kc ? (int)list[base + key] : -1;
-            const uint16_t *row = off == app_off ? vapp : Vb + off * kHeadDim;
-            vv[r] = uvec4{0u, 0u, 0u, 0u};
-            if (off >= 0) vv[r] = *reinterpret_cast<const uvec4 *>(row + 8 * (lane & 7) + 64 * (r & 1));
+            for (int r = 0; r < 8; ++r) {
+                const int key = (lane >> 4) + 4 * r;
+                const int off = key < kc ? (int)list[base + key] : -1;
+                const uint16_t *row = off == app_off ? vapp : Vb + off * kHeadDim;
+                vv[r] = uvec4{0u, 0u, 0u, 0u};
+                if (off >= 0) vv[r] = *reinterpret_cast<const uvec4 *>(row + 8 * (lane & 15));
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                *reinterpret_cast<uvec4 *>(&vst[(lane >> 4) + 4 * r][8 * (lane & 15)]) = vv[r];
         }
         // logits
         f32x4 acc[2];
@@ -883,20 +884,14 @@ __device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
             pa[1] = *reinterpret_cast<const uvec4 *>(&pb[1][c][8 * grp]);
         }
         const bf16x8 ph = __builtin_bit_cast(bf16x8, pa[0]), pl = __builtin_bit_cast(bf16x8, pa[1]);
-        // P.V, half a V row at a time through LDS
+        // P.V: the B operand of 16-dim block blk, transposed from the staged rows
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                *reinterpret_cast<uvec4 *>(&vst[(lane >> 3) + 8 * rr][8 * (lane & 7)]) = vv[2 * rr + half];
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                const uint16_t *src = &vst[8 * grp + (c >> 2)][16 * blk + 4 * (c & 3)];
-                const s16x4 b0 = lds_read_tr16(src), b1 = lds_read_tr16(src + 4 * kVRow);
-                const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[4 * half + blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, oacc[4 * half + blk], 0, 0, 0);
-                oacc[4 * half + blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, oacc[4 * half + blk], 0, 0, 0);
-            }
+        for (int blk = 0; blk < 8; ++blk) {
+            const uint16_t *src = &vst[8 * grp + (c >> 2)][16 * blk + 4 * (c & 3)];
+            const s16x4 b0 = lds_read_tr16(src), b1 = lds_read_tr16(src + 4 * kHeadDim);
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, oacc[blk], 0, 0, 0);
+            oacc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, oacc[blk], 0, 0, 0);
         }
     }
 }
