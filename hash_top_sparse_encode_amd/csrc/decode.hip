@@ -157,6 +157,16 @@ __device__ __forceinline__ int add_dev(int32_t *p, int v) {
 // Wait until this thread's memory operations have completed.
 __device__ __forceinline__ void drain_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
+// A value known to be the same in every lane, moved to a scalar register
+// (values read from LDS or reduced across the block are otherwise kept per
+// lane).
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // ---------------------------------------------------------------- small helpers
 
 __device__ __forceinline__ int64_t clamp_len(int64_t v, int64_t hi) {
@@ -776,6 +786,11 @@ __device__ __forceinline__ void load_q_operand(const uint16_t *qg, bf16x8 (&qa)[
     }
 }
 
+// s_waitcnt immediates (gfx9 encoding): wait for LDS operations only, or
+// for vector memory loads only.
+constexpr int kWaitLgkm0 = 0xC07F;  // vmcnt(63) expcnt(7) lgkmcnt(0)
+constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0) expcnt(7) lgkmcnt(15)
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
@@ -795,8 +810,8 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
 // tile; its accumulator holds heads 4 g .. 4 g + 3 of key c), an online
 // softmax in base 2 per head (running m, l per lane for its four heads), and
 // P.V by MFMA as well: P (heads x 32 keys) in bf16 high and low parts
-// through LDS as the A operand, the V rows staged in LDS as they arrive and
-// read back transposed as the B operand (lane (g, n) gets keys 8 g .. 8 g + 7
+// through LDS as the A operand, the V rows loaded straight into LDS
+// (global_load_lds) and read back transposed as the B operand (lane (g, n) gets keys 8 g .. 8 g + 7
 // of dim n of a 16-dim block).  oacc[blk] holds O[4 g + i][16 blk + n] in
 // lane (g, n).  Loads of a round are all issued before any is used.
 template <int G>
@@ -824,22 +839,25 @@ __device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
                 if (off >= 0) kr[tau][j] = *reinterpret_cast<const uvec4 *>(row + 32 * grp + 8 * j);
             }
         }
-        // V rows in 16-byte pieces: piece r of lane l is key (l >> 4) + 4 r,
-        // dims 8 (l & 15) .. + 8; staged in LDS as they arrive
-        {
-            uvec4 vv[8];
+        // V rows straight into LDS: 16 bytes per lane, and one instruction
+        // fills four consecutive 256-byte rows (lane l writes piece l), so
+        // piece l of instruction r is key (l >> 4) + 4 r, dims 8 (l & 15) .. + 8.
+        // Keys past kc repeat the round's first key (their P is zero).  The
+        // previous round's reads of the staging rows have completed first.
+        // (The row offsets are all read from the list first: an LDS read after
+        // one of these loads would have to wait for it.)
+        const uint16_t *vrow[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int key = (lane >> 4) + 4 * r;
-                const int off = key < kc ? (int)list[base + key] : -1;
-                const uint16_t *row = off == app_off ? vapp : Vb + off * kHeadDim;
-                vv[r] = uvec4{0u, 0u, 0u, 0u};
-                if (off >= 0) vv[r] = *reinterpret_cast<const uvec4 *>(row + 8 * (lane & 15));
-            }
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                *reinterpret_cast<uvec4 *>(&vst[(lane >> 4) + 4 * r][8 * (lane & 15)]) = vv[r];
+        for (int r = 0; r < 8; ++r) {
+            const int key = (lane >> 4) + 4 * r;
+            const int off = (int)list[base + (key < kc ? key : 0)];
+            vrow[r] = (off == app_off ? vapp : Vb + off * kHeadDim) + 8 * (lane & 15);
         }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            __builtin_amdgcn_global_load_lds(vrow[r], (__attribute__((address_space(3))) void *)&vst[4 * r][0],
+                                             16, 0, 0);
         // logits
         f32x4 acc[2];
 #pragma unroll
@@ -884,7 +902,9 @@ __device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
             pa[1] = *reinterpret_cast<const uvec4 *>(&pb[1][c][8 * grp]);
         }
         const bf16x8 ph = __builtin_bit_cast(bf16x8, pa[0]), pl = __builtin_bit_cast(bf16x8, pa[1]);
-        // P.V: the B operand of 16-dim block blk, transposed from the staged rows
+        // P.V: the B operand of 16-dim block blk, transposed from the staged
+        // rows once their loads have landed
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
             const uint16_t *src = &vst[8 * grp + (c >> 2)][16 * blk + 4 * (c & 3)];
@@ -1186,7 +1206,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     read_state();
     // ---- meanwhile the span's candidates: every key up to the candidate
     // cut tc, in index order (spans kept in LDS)
-    const int n_cand = in_lds ? list_candidates<G>(pf, tc, woff, sm) : -1;
+    const int n_cand = in_lds ? uni(list_candidates<G>(pf, tc, woff, sm)) : -1;
     // ---- the cut T, once every item of the unit has added its counts
     // (they then sum to len)
     for (int spins = 0;; ++spins) {
@@ -1221,7 +1241,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
         read_state();
     }
     __syncthreads();
-    const int T = sm.sel.T;
+    const int T = uni(sm.sel.T);
     // ---- score-T and below-T keys in the items before this one: from the
     // window when it holds bins T - 1 and T, else read (again) until every
     // entry carries this launch's tag
@@ -1263,9 +1283,9 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
             __builtin_amdgcn_s_sleep(1);
         }
     }
-    const int64_t ties_b = block_sum_256(tie, sm.sel.red);
-    const int64_t below_b = block_sum_256(lo, sm.sel.red);
-    const int64_t quota = k_eff - sm.sel.below;  // keys of score T to take, lowest index first
+    const int64_t ties_b = uni((int64_t)block_sum_256(tie, sm.sel.red));
+    const int64_t below_b = uni((int64_t)block_sum_256(lo, sm.sel.red));
+    const int64_t quota = k_eff - uni(sm.sel.below);  // keys of score T to take, lowest index first
     const int64_t rem_quota = quota - ties_b > 0 ? quota - ties_b : 0;
     int64_t out_pos = below_b + (ties_b < quota ? ties_b : quota);
 
@@ -1317,8 +1337,8 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
             const int pos = n_sel + lt_b + lt_pre + (int)(eq_before < room ? eq_before : room);
             __syncthreads();  // every entry of this round read, the counts too
             if (take) sm.sel.list[pos] = (uint16_t)off;
-            n_sel += lt_tot + (int)(eq_tot < room ? eq_tot : room);
-            ties_acc += eq_tot;
+            n_sel = uni(n_sel + lt_tot + (int)(eq_tot < room ? eq_tot : room));
+            ties_acc = uni(ties_acc + eq_tot);
         }
         __syncthreads();
         if (sel_u) {
@@ -1509,7 +1529,7 @@ __device__ __forceinline__ void item_work(const FusedArgs &a, int u, int c, Smem
     uint32_t gen;
     const int tc = scan_phase<G>(a, cur, gen, sm);
     __syncthreads();  // the LDS histograms and the selection state share memory
-    if (sel_phase<G>(a, cur, tc, gen, sm) && threadIdx.x == 0) unit_done(a, u);
+    if (sel_phase<G>(a, cur, uni(tc), (uint32_t)uni((int)gen), sm) && threadIdx.x == 0) unit_done(a, u);
 }
 
 // Three workgroups per CU (two for G = 8): the register budget the
