@@ -699,11 +699,12 @@ __device__ __forceinline__ int slot_publish(const FusedArgs &a, const Slot &s, u
     return sm.scan.tc;
 }
 
-// Thread 0 of the unit's last WORK item, after its merge: every item of the
-// unit is past its waits, so the unit's counters are reset for the next
-// launch and its generation advances; the last unit of a batch entry
-// publishes the entry's new length (no item of the entry reads it any
-// more).  Nothing here needs to complete before the kernel ends.
+// Thread 0 of the unit's last WORK item, once it knows it is the last: every
+// item of the unit is past its waits and past reading the length, so the
+// unit's counters are reset for the next launch and its generation
+// advances; the last unit of a batch entry publishes the entry's new length
+// (no item of the entry reads it any more).  Nothing here needs to complete
+// before the kernel ends.
 __device__ __forceinline__ void unit_done(const FusedArgs &a, int u) {
     for (int w = 0; w < kNumCtr; ++w) st_dev(unit_ctr(a, u, w), 0);
     __hip_atomic_fetch_add(a.gen + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1164,6 +1165,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
         const int prev = wg_signal(unit_ctr(a, u, kAttn));
         if (t == 0) sm.sel.last = (prev == n_splits_u - 1);
         __syncthreads();
+        if (sm.sel.last && t == 0) unit_done(a, u);
         return sm.sel.last;
     }
 
@@ -1447,6 +1449,8 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
         sm.sel.mw[i / G][i % G] = ld_dev(mlb + 2 * i);
         sm.sel.lv[i / G][i % G] = ld_dev(mlb + 2 * i + 1);
     }
+    // the unit's bookkeeping, its round trip overlapping these loads
+    if (t == 0) unit_done(a, u);
     __syncthreads();
     if (t < G) {
         float M = -INFINITY;
@@ -1529,7 +1533,7 @@ __device__ __forceinline__ void item_work(const FusedArgs &a, int u, int c, Smem
     uint32_t gen;
     const int tc = scan_phase<G>(a, cur, gen, sm);
     __syncthreads();  // the LDS histograms and the selection state share memory
-    if (sel_phase<G>(a, cur, uni(tc), (uint32_t)uni((int)gen), sm) && threadIdx.x == 0) unit_done(a, u);
+    sel_phase<G>(a, cur, uni(tc), (uint32_t)uni((int)gen), sm);
 }
 
 // Three workgroups per CU (two for G = 8): the register budget the
