@@ -237,26 +237,23 @@ def main():
         step(s)
     torch.cuda.synchronize()
     ctx0 = int(layers[args.warmup % L].cache.seq_len[0].item()) + 1
+    # HIP events on the launch stream bracket the timed region: the decode
+    # kernel is the only work in it, one launch per step, so their interval
+    # over the step count is the kernel's average launch duration (with the
+    # gaps between back-to-back launches).
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record(stream)
     for s in range(args.steps):
         step(args.warmup + s)
+    ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
     ms_per_step = wall * 1e3 / args.steps
     steps_per_s = args.steps / wall
-
-    # Second pass with HIP events around each step's kernel (same stream) for
-    # the kernel-level roofline figure.
-    stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for s in range(args.steps):
-        evs[s][0].record(stream)
-        step(args.warmup + args.steps + s)
-        evs[s][1].record(stream)
-    torch.cuda.synchronize()
-    dec_ms = statistics.mean(a.elapsed_time(b) for a, b in evs)
+    dec_ms = ev0.elapsed_time(ev1) / args.steps
     status = [ly.cache.status() for ly in layers]
     if any(status):
         print(f"[bench] device status flags set: {status}", file=sys.stderr)

@@ -29,11 +29,12 @@
 //              (which fixes how many score-T keys it keeps: the lowest
 //              indices win); the selection is then taken from the
 //              candidates (or, if T lies above their cut, from all scores);
-//     attend   gather of the selected bf16 K/V rows, logits of 16-key tiles
-//              on the matrix cores, an online softmax in base 2, P.V on the
-//              vector units; one (m, l, o) partial per query head.  The
-//              last item of a unit to finish merges the partials in item
-//              order into the bf16 output and resets the unit's state.
+//     attend   gather of the selected bf16 K/V rows (V straight into LDS),
+//              logits of 16-key tiles on the matrix cores, an online softmax
+//              in base 2, P.V on the matrix cores as well; one (m, l, o)
+//              partial per query head.  The last item of a unit to finish
+//              merges the partials in item order into the bf16 output and
+//              resets the unit's state.
 //
 // Ordering: a PRO part waits for nothing; a WORK item's scan waits for the
 // PRO parts of its unit (smaller block indices), and its selection for the
@@ -812,8 +813,8 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
 // softmax in base 2 per head (running m, l per lane for its four heads), and
 // P.V by MFMA as well: P (heads x 32 keys) in bf16 high and low parts
 // through LDS as the A operand, the V rows loaded straight into LDS
-// (global_load_lds) and read back transposed as the B operand (lane (g, n) gets keys 8 g .. 8 g + 7
-// of dim n of a 16-dim block).  oacc[blk] holds O[4 g + i][16 blk + n] in
+// (global_load_lds) and read back transposed as the B operand (lane (g, n)
+// gets keys 8 g .. 8 g + 7 of dim n of a 16-dim block).  oacc[blk] holds O[4 g + i][16 blk + n] in
 // lane (g, n).  Loads of a round are all issued before any is used.
 template <int G>
 __device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
