@@ -255,9 +255,6 @@ struct SmemSel {
     };
     uint16_t list[kListCap];  // selected keys of a batch, as offsets from its first key
     uint16_t pb[4][2][G][32]; // per wave: softmax numerators as bf16 high and low parts
-    float mw[kMaxSplits][G];  // merge: per-split maxima, then weights
-    float lv[kMaxSplits][G];  // merge: per-split sums
-    float ml[G];
     int scan[8];
     int weq[4], wlt[4];  // per-wave counts of score-T and below-T keys in a batch
     long long red[4];
@@ -702,16 +699,21 @@ __device__ __forceinline__ int slot_publish(const FusedArgs &a, const Slot &s, u
 
 // Thread 0 of the unit's last WORK item, once it knows it is the last: every
 // item of the unit is past its waits and past reading the length, so the
-// unit's counters are reset for the next launch and its generation
-// advances; the last unit of a batch entry publishes the entry's new length
-// (no item of the entry reads it any more).  Nothing here needs to complete
-// before the kernel ends.
-__device__ __forceinline__ void unit_done(const FusedArgs &a, int u) {
+// unit's counters are reset for the next launch, its generation advances,
+// and the unit is counted as finished in its batch entry.  Returns the
+// entry's count before this unit, for entry_done (its round trip can overlap
+// other work first).  Nothing here needs to complete before the kernel ends.
+__device__ __forceinline__ int unit_done(const FusedArgs &a, int u) {
     for (int w = 0; w < kNumCtr; ++w) st_dev(unit_ctr(a, u, w), 0);
     __hip_atomic_fetch_add(a.gen + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int b = u / a.Hkv;
-    if (add_dev(batch_ctr(a, b), 1) != a.Hkv - 1) return;
-    const StepLen sl = step_len(a, b);
+    return add_dev(batch_ctr(a, u / a.Hkv), 1);
+}
+
+// After unit_done: the last unit of batch entry b to finish publishes the
+// entry's new length (no item of the entry reads it any more) and clears the
+// entry's count.  sl is the entry's length state of this launch.
+__device__ __forceinline__ void entry_done(const FusedArgs &a, int b, const StepLen &sl, int prev) {
+    if (prev != a.Hkv - 1) return;
     if (sl.app) st_dev(a.seq_len + b, (int32_t)(sl.l0 + 1));
     st_dev(batch_ctr(a, b), 0);
 }
@@ -776,14 +778,14 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 // The query heads as the A operand of v_mfma_f32_16x16x32_bf16: lane l holds
 // row l % 16 (head; zero for heads >= G) and, for MFMA j, dims
-// 32 (l / 16) + 8 j .. + 8 (the same dims its B operand brings for a key).
+// 32 j + 8 (l / 16) .. + 8 (the same dims its B operand brings for a key).
 template <int G>
 __device__ __forceinline__ void load_q_operand(const uint16_t *qg, bf16x8 (&qa)[4]) {
     const int lane = threadIdx.x & 63, h = lane & 15, grp = lane >> 4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         uvec4 v = {0u, 0u, 0u, 0u};
-        if (h < G) v = *reinterpret_cast<const uvec4 *>(qg + h * kHeadDim + 32 * grp + 8 * j);
+        if (h < G) v = *reinterpret_cast<const uvec4 *>(qg + h * kHeadDim + 32 * j + 8 * grp);
         qa[j] = __builtin_bit_cast(bf16x8, v);
     }
 }
@@ -808,8 +810,9 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
 // Attention over the rows Kb / Vb + list[0..n) (offsets from a batch's first
 // key; the row at offset app_off is this step's appended key, read from
 // kapp / vapp).  Each wave takes 32 keys of every 128: logits of two 16-key
-// tiles by MFMA (lane (g, c) brings dims 32 g .. 32 g + 32 of key c of a
-// tile; its accumulator holds heads 4 g .. 4 g + 3 of key c), an online
+// tiles by MFMA (for MFMA j, lane (g, c) brings dims 32 j + 8 g .. + 8 of key
+// c of a tile, so each load instruction reads whole 64-byte pieces of 16
+// rows; its accumulator holds heads 4 g .. 4 g + 3 of key c), an online
 // softmax in base 2 per head (running m, l per lane for its four heads), and
 // P.V by MFMA as well: P (heads x 32 keys) in bf16 high and low parts
 // through LDS as the A operand, the V rows loaded straight into LDS
@@ -828,7 +831,7 @@ __device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
     constexpr float kScale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
     for (int base = 32 * wv; base < n; base += 128) {
         const int kc = n - base < 32 ? n - base : 32;
-        // K rows: key 16 tau + c, dims 32 grp .. +32
+        // K rows: key 16 tau + c, dims 32 j + 8 grp .. + 8 for MFMA j
         uvec4 kr[2][4];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
@@ -838,7 +841,7 @@ __device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 kr[tau][j] = uvec4{0u, 0u, 0u, 0u};
-                if (off >= 0) kr[tau][j] = *reinterpret_cast<const uvec4 *>(row + 32 * grp + 8 * j);
+                if (off >= 0) kr[tau][j] = *reinterpret_cast<const uvec4 *>(row + 32 * j + 8 * grp);
             }
         }
         // V rows straight into LDS: 16 bytes per lane, and one instruction
@@ -1166,7 +1169,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
         const int prev = wg_signal(unit_ctr(a, u, kAttn));
         if (t == 0) sm.sel.last = (prev == n_splits_u - 1);
         __syncthreads();
-        if (sm.sel.last && t == 0) unit_done(a, u);
+        if (sm.sel.last && t == 0) entry_done(a, b, sl, unit_done(a, u));
         return sm.sel.last;
     }
 
@@ -1428,13 +1431,19 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     __syncthreads();
     if (!sm.sel.last) return false;
     // Per split x and head h: weight w = exp2(m_x - M) with M the maximum
-    // over splits; out = sum_x w o_x / sum_x w l_x.  Output pair pr (floats
-    // 2 pr, 2 pr + 1 of the G x 128 block) is thread pr's; its partials are
-    // loaded for up to XB splits at a time, the first batch before the (m, l)
-    // loads so both travel together.
+    // over splits; out = sum_x w o_x / sum_x w l_x.  Thread 0 first does the
+    // unit's bookkeeping (its count returns with the loads below and is used
+    // at the end).  Output pair pr (floats 2 pr, 2 pr + 1 of the G x 128
+    // block, head pr / 64) is thread pr's (and pr + 256's), so each wave
+    // covers whole heads: it loads every split's (m, l) of its heads into its
+    // lanes (split x in lane x), forms the weights and sums by lane
+    // reductions and reads weight x back with a lane read, with no exchange
+    // between waves.  Partials are loaded for up to XB splits at a time.
+    int entry_prev = 0;
+    if (t == 0) entry_prev = unit_done(a, u);
     constexpr int NPR = G * kHeadDim / 2;
     constexpr int PPT = (NPR + kThreads - 1) / kThreads;
-    constexpr int XB = 32 / PPT;
+    constexpr int XB = 24 / PPT;
     const float *mlb = a.part_ml + (int64_t)u * a.n_chunks * G * 2;
     const uint64_t *ob = reinterpret_cast<const uint64_t *>(a.part_o + (int64_t)u * a.n_chunks * G * kHeadDim);
     const int n = n_splits_u;
@@ -1446,26 +1455,23 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
             const int pr = t + k * kThreads;
             ov[k][x] = (pr < NPR && x < n) ? ld_dev(ob + (int64_t)x * NPR + pr) : 0ull;
         }
-    for (int i = t; i < n * G; i += kThreads) {
-        sm.sel.mw[i / G][i % G] = ld_dev(mlb + 2 * i);
-        sm.sel.lv[i / G][i % G] = ld_dev(mlb + 2 * i + 1);
-    }
-    // the unit's bookkeeping, its round trip overlapping these loads
-    if (t == 0) unit_done(a, u);
-    __syncthreads();
-    if (t < G) {
-        float M = -INFINITY;
-        for (int x = 0; x < n; ++x) M = fmaxf(M, sm.sel.mw[x][t]);
-        float L = 0.f;
-        for (int x = 0; x < n; ++x) {
-            const float ms = sm.sel.mw[x][t];
-            const float wx = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-            sm.sel.mw[x][t] = wx;
-            L = fmaf(sm.sel.lv[x][t], wx, L);
+    float wk[PPT], Lk[PPT];
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int h = wv + 4 * k;  // the head of this wave's pairs t + 256 k
+        float mx = -INFINITY, lx = 0.f;
+        if (h < G && lane < n) {
+            mx = ld_dev(mlb + 2 * (lane * G + h));
+            lx = ld_dev(mlb + 2 * (lane * G + h) + 1);
         }
-        sm.sel.ml[t] = L;
+        float M = row16_max(mx);
+        M = fmaxf(M, __shfl_xor(M, 16, 64));
+        M = fmaxf(M, __shfl_xor(M, 32, 64));
+        wk[k] = (mx == -INFINITY) ? 0.f : exp2f(mx - M);
+        float L = row16_sum(lx * wk[k]);
+        L += __shfl_xor(L, 16, 64);
+        Lk[k] = L + __shfl_xor(L, 32, 64);
     }
-    __syncthreads();
     float O[PPT][2];
 #pragma unroll
     for (int k = 0; k < PPT; ++k) O[k][0] = O[k][1] = 0.f;
@@ -1480,12 +1486,11 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
                 }
         }
 #pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-            const int h = (2 * (t + k * kThreads)) / kHeadDim;
+        for (int x = 0; x < XB; ++x) {
+            if (x0 + x < n) {
 #pragma unroll
-            for (int x = 0; x < XB; ++x) {
-                if (x0 + x < n && t + k * kThreads < NPR) {
-                    const float wx = sm.sel.mw[x0 + x][h];
+                for (int k = 0; k < PPT; ++k) {
+                    const float wx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk[k]), x0 + x));
                     O[k][0] = fmaf(__uint_as_float((uint32_t)ov[k][x]), wx, O[k][0]);
                     O[k][1] = fmaf(__uint_as_float((uint32_t)(ov[k][x] >> 32)), wx, O[k][1]);
                 }
@@ -1496,13 +1501,13 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     for (int k = 0; k < PPT; ++k) {
         const int pr = t + k * kThreads;
         if (pr < NPR) {
-            const int h = (2 * pr) / kHeadDim;
-            const float L = sm.sel.ml[h];
+            const float L = Lk[k];
             uint16_t *o = a.out + ((int64_t)b * Hq + kv * G) * kHeadDim + 2 * pr;
             o[0] = L > 0.f ? f32_to_bf16(O[k][0] / L) : (uint16_t)0;
             o[1] = L > 0.f ? f32_to_bf16(O[k][1] / L) : (uint16_t)0;
         }
     }
+    if (t == 0) entry_done(a, b, sl, entry_prev);
     return true;
 }
 
