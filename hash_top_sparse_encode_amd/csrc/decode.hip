@@ -752,13 +752,6 @@ __device__ __forceinline__ int scan_phase(const FusedArgs &a, const Slot &cur, u
 
 // ---------------------------------------------------------------- selection phase
 
-__device__ __forceinline__ void lse_weights(float m1, float m2, float *M, float *a1, float *a2) {
-    const float mm = fmaxf(m1, m2);
-    *M = mm;
-    *a1 = (m1 == -INFINITY) ? 0.f : exp2f(m1 - mm);
-    *a2 = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mm);
-}
-
 // All-reduce over the 16 lanes of a row (lanes 16 g .. 16 g + 15): xor-1 and
 // xor-2 quad permutes, then the half-row and row mirrors.
 __device__ __forceinline__ float row16_max(float v) {
@@ -1405,20 +1398,29 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
         }
     }
     __syncthreads();
+    // Output pair pr (floats 2 pr, 2 pr + 1 of the G x 128 block) is thread
+    // pr's: with M the maximum of the waves' m for its head, wave w's state
+    // weighs a_w = exp2(m_w - M).
     float *pml = a.part_ml + ((int64_t)u * a.n_chunks + s) * G * 2;
-    float *po = a.part_o + ((int64_t)u * a.n_chunks + s) * G * kHeadDim;
-    for (int pr = t; pr < G * kHeadDim; pr += kThreads) {
-        const int h = pr / kHeadDim, e = pr % kHeadDim;
-        float M = sm.sel.cb.wm[0][h], L = sm.sel.cb.wl[0][h], O = sm.sel.cb.wo[0][h][e];
+    uint64_t *po = reinterpret_cast<uint64_t *>(a.part_o + ((int64_t)u * a.n_chunks + s) * G * kHeadDim);
+    for (int pr = t; pr < G * kHeadDim / 2; pr += kThreads) {
+        const int h = pr / (kHeadDim / 2), e = 2 * (pr % (kHeadDim / 2));
+        float mw[4], M = -INFINITY;
 #pragma unroll
-        for (int w2 = 1; w2 < 4; ++w2) {
-            float Mn, a1, a2;
-            lse_weights(M, sm.sel.cb.wm[w2][h], &Mn, &a1, &a2);
-            L = L * a1 + sm.sel.cb.wl[w2][h] * a2;
-            O = O * a1 + sm.sel.cb.wo[w2][h][e] * a2;
-            M = Mn;
+        for (int w2 = 0; w2 < 4; ++w2) {
+            mw[w2] = sm.sel.cb.wm[w2][h];
+            M = fmaxf(M, mw[w2]);
         }
-        st_dev(po + pr, O);
+        float L = 0.f, O0 = 0.f, O1 = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+            const float aw = (mw[w2] == -INFINITY) ? 0.f : exp2f(mw[w2] - M);
+            const float2 ow = *reinterpret_cast<const float2 *>(&sm.sel.cb.wo[w2][h][e]);
+            L = fmaf(sm.sel.cb.wl[w2][h], aw, L);
+            O0 = fmaf(ow.x, aw, O0);
+            O1 = fmaf(ow.y, aw, O1);
+        }
+        st_dev(po + pr, (uint64_t)__float_as_uint(O0) | ((uint64_t)__float_as_uint(O1) << 32));
         if (e == 0) {
             st_dev(pml + 2 * h, M);
             st_dev(pml + 2 * h + 1, L);
