@@ -45,8 +45,11 @@
 // item of unit u or a later one, and the unit's unstarted items (at most 63)
 // are the next in line on their XCDs; an XCD holds at least 64 of these
 // workgroups at once (32 CUs x 2 or 3), so they all start, all scan, and
-// unit u completes.  Every wait also gives up after a bound
-// (HATA_DEV_STALL), so the kernel always terminates.
+// unit u completes.  (When every unit's last item is moved to the end of the
+// grid, see item_of, the host has checked that every workgroup of the launch
+// is resident at once, so no wait depends on a workgroup yet to start.)
+// Every wait also gives up after a bound (HATA_DEV_STALL), so the kernel
+// always terminates.
 //
 // Coherence across the eight XCDs without cache flushes: every value one
 // workgroup produces for another is written with a device-scope relaxed
@@ -120,6 +123,7 @@ struct FusedArgs {
     int B, Hkv, k_max;
     int64_t span;            // keys per work item
     int n_chunks;            // work items per unit
+    int tails_last;          // every unit's last work item after all the others (see item_of)
     int n_items;
 };
 
@@ -1520,7 +1524,13 @@ struct Item {
     int u, i;
 };
 
-// PRO(u, p) for every unit and part, then WORK(u, c) unit by unit.
+// PRO(u, p) for every unit and part, then WORK(u, c) unit by unit.  With
+// tails_last (set by the host only when the whole grid is resident at once),
+// each unit's last item, which often holds just the few keys past a multiple
+// of the span, comes after every other item instead: blocks are dealt to the
+// XCDs in turn and to their CUs in order, so the grid's last blocks are the
+// ones that land as a third workgroup on a CU, and the light items are then
+// the ones sharing a CU with two full ones.
 __device__ __forceinline__ Item item_of(const FusedArgs &a, int tk) {
     const int U = a.B * a.Hkv;
     Item it;
@@ -1529,7 +1539,15 @@ __device__ __forceinline__ Item item_of(const FusedArgs &a, int tk) {
         return it;
     }
     tk -= kProParts * U;
-    it.kind = 1; it.u = tk / a.n_chunks; it.i = tk % a.n_chunks;
+    it.kind = 1;
+    const int full = U * (a.n_chunks - 1);
+    if (a.tails_last && tk >= full) {
+        it.u = tk - full; it.i = a.n_chunks - 1;
+    } else if (a.tails_last) {
+        it.u = tk / (a.n_chunks - 1); it.i = tk % (a.n_chunks - 1);
+    } else {
+        it.u = tk / a.n_chunks; it.i = tk % a.n_chunks;
+    }
     return it;
 }
 
@@ -1602,9 +1620,18 @@ bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, DecodePlan *p) {
     return true;
 }
 
+// The last-items-last order gives up the unit-by-unit order that lets a grid
+// larger than the chip make progress, so it is only used when every
+// workgroup of the launch can be resident at once.
 template <int G>
 static hipError_t launch_g(const DecodePlan &p, FusedArgs &a, hipStream_t s) {
     (void)p;
+    int dev = 0, n_cu = 0, per_cu = 0;
+    a.tails_last = 0;
+    if (a.n_chunks > 1 && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_fused<G>, kThreads, 0) == hipSuccess)
+        a.tails_last = (int64_t)a.n_items <= (int64_t)per_cu * n_cu;
     hipLaunchKernelGGL(k_decode_fused<G>, dim3(a.n_items), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
