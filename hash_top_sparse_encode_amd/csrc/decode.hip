@@ -261,7 +261,7 @@ struct SmemSel {
     uint16_t pb[4][2][G][32]; // per wave: softmax numerators as bf16 high and low parts
     int scan[8];
     int weq[4], wlt[4];  // per-wave counts of score-T and below-T keys in a batch
-    long long red[4];
+    int red[8];
     int T, below, last;
 };
 
@@ -1286,8 +1286,9 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
             __builtin_amdgcn_s_sleep(1);
         }
     }
-    const int64_t ties_b = uni((int64_t)block_sum_256(tie, sm.sel.red));
-    const int64_t below_b = uni((int64_t)block_sum_256(lo, sm.sel.red));
+    int ties_s, below_s;  // both at most the context length
+    block_sum2_256((int)tie, (int)lo, sm.sel.red, &ties_s, &below_s);
+    const int64_t ties_b = uni(ties_s), below_b = uni(below_s);
     const int64_t quota = k_eff - uni(sm.sel.below);  // keys of score T to take, lowest index first
     const int64_t rem_quota = quota - ties_b > 0 ? quota - ties_b : 0;
     int64_t out_pos = below_b + (ties_b < quota ? ties_b : quota);

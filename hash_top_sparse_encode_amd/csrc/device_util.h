@@ -18,16 +18,33 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// DPP controls (GFX9 encoding): row_shr:n is kDppRowShr + n; row_bcast:15 and
+// row_bcast:31 pass lane 15 (31) of a group of rows on to the following rows.
+constexpr int kDppRowShr = 0x110, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes of a wave: a shift-and-add scan
+// within each row of 16 lanes, then each row adds the totals of the rows
+// before it (row_bcast:15 for rows 1 and 3, row_bcast:31 for rows 2 and 3).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 1, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 2, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 4, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 8, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast15, 0xA, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast31, 0xC, 0xF, false);
+    return x;
+}
+
+// Sum over the lanes of a wave, in a scalar register.
+__device__ __forceinline__ int wave_sum(int x) {
+    return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
+}
+
 // Exclusive prefix sum over the 256 threads of a workgroup (4 waves of 64).
 // Every thread must call it; `tmp` is 4 ints of LDS.  *total gets the sum.
 __device__ __forceinline__ int block_excl_scan_256(int v, int *tmp, int *total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        int y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
-    }
+    const int x = wave_incl_scan(v);
     if (lane == 63) tmp[w] = x;
     __syncthreads();
     int pre = 0, tot = 0;
@@ -42,46 +59,19 @@ __device__ __forceinline__ int block_excl_scan_256(int v, int *tmp, int *total) 
     return pre + x - v;
 }
 
-// Exclusive prefix sum over the 256 threads of a workgroup for small values
-// (0 <= v < 16): per wave, bit-plane ballots counted below each lane
-// (mbcnt); across the 4 waves, one LDS exchange.  `tmp` is 8 ints of LDS
-// used as two alternating halves (`phase` 0/1), so consecutive calls with
-// alternating phases need only one barrier each.  Every thread must call it.
-__device__ __forceinline__ int block_excl_scan_small(int v, int *tmp, int phase, int *total) {
+// Sums over the 256 threads of a workgroup of two values at once (each sum
+// must fit in an int); `tmp` is 8 ints of LDS, written here and read after
+// one barrier.  Every thread must call it.
+__device__ __forceinline__ void block_sum2_256(int a, int b, int *tmp, int *sa, int *sb) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int pre = 0, wtot = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const uint64_t m = __ballot((v >> b) & 1);
-        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        pre += below << b;
-        wtot += __popcll(m) << b;
+    const int wa = wave_sum(a), wb = wave_sum(b);
+    if (lane == 0) {
+        tmp[w] = wa;
+        tmp[4 + w] = wb;
     }
-    int *slot = tmp + 4 * phase;
-    if (lane == 0) slot[w] = wtot;
     __syncthreads();
-    int base = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int x = slot[i];
-        base += (i < w) ? x : 0;
-        tot += x;
-    }
-    *total = tot;
-    return base + pre;
-}
-
-// Sum over the 256 threads of a workgroup (64-bit).
-__device__ __forceinline__ long long block_sum_256(long long v, long long *tmp) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-    if (lane == 0) tmp[w] = v;
-    __syncthreads();
-    long long t = tmp[0] + tmp[1] + tmp[2] + tmp[3];
-    __syncthreads();
-    return t;
+    *sa = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+    *sb = tmp[4] + tmp[5] + tmp[6] + tmp[7];
 }
 
 // Column j of W (W[t][j], t = 0..127, column stride 128) into registers, all
