@@ -677,28 +677,50 @@ __device__ __forceinline__ int slot_publish(const FusedArgs &a, const Slot &s, u
     const int64_t k_eff = step_keff(a, s.u / a.Hkv, s.sl.len);
     const int64_t share = (k_eff * n_span + s.sl.len - 1) / s.sl.len;
     const int64_t target = share + share / 2 + 32 < n_span ? share + share / 2 + 32 : n_span;
-    uint64_t *ch = a.chunk_hist + ((int64_t)s.u * a.n_chunks + s.c) * NB;
-    const uint64_t tag = (uint64_t)gen << 32;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
         const int bin = t * PER + e;
         if (bin < NB) {
             const int before = run;
             run += (int)loc[e];
-            st_dev(ch + bin, tag | (uint32_t)run);
+            sm.scan.hist[1][bin] = (uint32_t)run;  // the cumulative row, published below
             if (before < target && run >= target) sm.scan.tc = bin;
         }
     }
-    uint64_t *uh = reinterpret_cast<uint64_t *>(a.unit_hist) + (int64_t)s.u * NP;
-    for (int pr = t; pr < NP; pr += kThreads) {
-        const uint32_t lo = sm.scan.hist[0][2 * pr];
-        const uint32_t hi = 2 * pr + 1 < NB ? sm.scan.hist[0][2 * pr + 1] : 0u;
-        if (lo | hi)
-            __hip_atomic_fetch_add(uh + pr, (uint64_t)lo | ((uint64_t)hi << 32), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-    }
     __syncthreads();
-    return sm.scan.tc;
+    // Wave 3 alone publishes, with every store a whole 512-byte line run: on
+    // this architecture stores count against the issuing wave's memory
+    // counter, and waves 0-2 poll next (a poll's wait would include them).
+    // Its values come out of LDS before the barrier that frees the memory.
+    constexpr int CW = (NB + 63) / 64, PW = (NP + 63) / 64;
+    uint32_t cum[CW], cnt[PW][2];
+    const int l = t & 63;
+    if (t >= 3 * 64) {
+#pragma unroll
+        for (int k = 0; k < CW; ++k) cum[k] = l + 64 * k < NB ? sm.scan.hist[1][l + 64 * k] : 0u;
+#pragma unroll
+        for (int k = 0; k < PW; ++k) {
+            const int pr = l + 64 * k;
+            cnt[k][0] = pr < NP ? sm.scan.hist[0][2 * pr] : 0u;
+            cnt[k][1] = 2 * pr + 1 < NB ? sm.scan.hist[0][2 * pr + 1] : 0u;
+        }
+    }
+    const int tc = sm.scan.tc;
+    __syncthreads();
+    if (t >= 3 * 64) {
+        uint64_t *ch = a.chunk_hist + ((int64_t)s.u * a.n_chunks + s.c) * NB;
+        const uint64_t tag = (uint64_t)gen << 32;
+#pragma unroll
+        for (int k = 0; k < CW; ++k)
+            if (l + 64 * k < NB) st_dev(ch + l + 64 * k, tag | cum[k]);
+        uint64_t *uh = reinterpret_cast<uint64_t *>(a.unit_hist) + (int64_t)s.u * NP;
+#pragma unroll
+        for (int k = 0; k < PW; ++k)
+            if (cnt[k][0] | cnt[k][1])
+                __hip_atomic_fetch_add(uh + l + 64 * k, (uint64_t)cnt[k][0] | ((uint64_t)cnt[k][1] << 32),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return tc;
 }
 
 // Thread 0 of the unit's last WORK item, once it knows it is the last: every
@@ -1153,7 +1175,12 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
                                           Smem<G> &sm) {
     constexpr int D = kSelRounds;  // selection rounds of scores in flight
     constexpr int NB = G * kBits + 1;
-    constexpr int PER = (NB + kThreads - 1) / kThreads;
+    // Waves 0-2 poll the unit's histograms (PER bins and WPT window entries
+    // per thread); wave 3 published this item's histograms, and its stores
+    // would hold up a poll's wait behind them.
+    constexpr int kPoll = 3 * 64;
+    constexpr int PER = (NB + kPoll - 1) / kPoll;
+    constexpr int WPT = (kMaxSplits * kWin + kPoll - 1) / kPoll;
     const int u = cur.u, s = cur.c;
     const int b = u / a.Hkv, kv = u % a.Hkv, Hq = a.Hkv * G;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -1191,19 +1218,18 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     const uint64_t *chu = a.chunk_hist + (int64_t)u * a.n_chunks * NB;
     const uint64_t tag = (uint64_t)gen << 32;
     const int wlo = tc - (kWin - 1);
-    constexpr int WPT = kMaxSplits * kWin / kThreads;
     uint32_t loc[PER];
     uint64_t win[WPT];
     auto read_state = [&]() {
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
             const int bin = t * PER + e;
-            loc[e] = bin < NB ? ld_dev(uhr + bin) : 0u;
+            loc[e] = (t < kPoll && bin < NB) ? ld_dev(uhr + bin) : 0u;
         }
 #pragma unroll
         for (int k = 0; k < WPT; ++k) {
-            const int i = t + k * kThreads, cc = i / kWin, bin = wlo + i % kWin;
-            win[k] = (cc < s && bin >= 0) ? ld_dev(chu + (int64_t)cc * NB + bin) : tag;
+            const int i = t + k * kPoll, cc = i / kWin, bin = wlo + i % kWin;
+            win[k] = (t < kPoll && cc < s && bin >= 0) ? ld_dev(chu + (int64_t)cc * NB + bin) : tag;
         }
     };
     read_state();
@@ -1254,8 +1280,8 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     if (in_win) {
 #pragma unroll
         for (int k = 0; k < WPT; ++k) {
-            const int i = t + k * kThreads, cc = i / kWin, bin = wlo + i % kWin;
-            if (cc < s) {
+            const int i = t + k * kPoll, cc = i / kWin, bin = wlo + i % kWin;
+            if (t < kPoll && cc < s) {
                 bad |= (win[k] & ~0xFFFFFFFFull) != tag;
                 const long long cum = (uint32_t)win[k];
                 if (bin == T) tie += cum;
