@@ -14,16 +14,17 @@
 // same quantity (Higham, Accuracy and Stability of Numerical Algorithms,
 // ch. 3-4).  A bit with |y'| > 2^-14 ||x|| ||W_:j|| + 2^-100 is therefore the
 // sign of y'.  Every other bit is recomputed by the wave: a double-precision
-// dot product over 64 lanes (two exact products per lane, a six-step
-// butterfly) decides it when |s| > 2^-44 sum |p|; otherwise lane 0 runs the
-// sequential double loop itself.
+// dot product over 64 lanes (two exact products per lane, then a lane sum
+// with eight rounding levels, so within gamma_8 sum |p| of the exact sum)
+// decides it when |s| > 2^-44 sum |p|; otherwise lane 0 runs the sequential
+// double loop itself.
 //
 // Work split: grid.y = head; each workgroup keeps its head's W operands in
 // registers (wave w: columns 32 w .. 32 w + 31, i.e. code word w) and W_H
 // transposed in LDS for the recomputations, and walks 64-row tiles.  Lane
-// (g, c) of a wave loads row c of each 16-row M tile, dims 32 g .. 32 g + 31
-// (64 contiguous bytes), which is the MFMA A operand when MFMA j takes dims
-// 32 g + 8 j .. + 8 from lane group g (the B operand uses the same map).
+// (g, c) of a wave loads, for MFMA j, dims 32 j + 8 g .. + 8 of row c of each
+// 16-row M tile (the A operand), so each load instruction reads whole
+// 64-byte pieces of 16 rows; the B operand uses the same map of dims.
 #include "device_util.h"
 #include "hata_internal.h"
 #include "../../include/hata.h"
@@ -68,10 +69,35 @@ __device__ __forceinline__ bool append_ok(int64_t len, int n, int t_max, int64_t
     return n >= 0 && n <= t_max && len >= 0 && len + n <= max_ctx;
 }
 
+// Sum over the 64 lanes of a wave, in every lane: within each row of 16
+// lanes by DPP (xor 1, xor 2, half-row mirror, row mirror: four additions),
+// then the four row sums, read from lanes 0, 16, 32, 48, added in order
+// (three more): eight rounding levels with the caller's pair sum.
+__device__ __forceinline__ double dpp_f64(double v, int ctrl_id) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+    switch (ctrl_id) {
+        case 0: lo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false);
+                hi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, false); break;
+        case 1: lo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, false);
+                hi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, false); break;
+        case 2: lo = __builtin_amdgcn_update_dpp(0, lo, 0x141, 0xF, 0xF, false);
+                hi = __builtin_amdgcn_update_dpp(0, hi, 0x141, 0xF, 0xF, false); break;
+        default: lo = __builtin_amdgcn_update_dpp(0, lo, 0x140, 0xF, 0xF, false);
+                 hi = __builtin_amdgcn_update_dpp(0, hi, 0x140, 0xF, 0xF, false); break;
+    }
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ double lane_f64(double v, int l) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ double dsum64(double v) {
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-    return v;
+    for (int k = 0; k < 4; ++k) v += dpp_f64(v, k);
+    return ((lane_f64(v, 0) + lane_f64(v, 16)) + lane_f64(v, 32)) + lane_f64(v, 48);
 }
 
 // The exact bit (row R of the tile, column col): see the header comment.
@@ -108,7 +134,7 @@ __global__ __launch_bounds__(kEThreads, 2) void k_encode_mfma(EncArgs a) {
     const float *W = a.w + (int64_t)h * kHeadDim * kBits;
 
     // ---- W_H transposed into LDS, and this wave's B operands (columns
-    // 32 wv + 16 nt + c, rows 32 g + 8 j + e) split into bf16 hi / lo terms
+    // 32 wv + 16 nt + c, rows 32 j + 8 g + e) split into bf16 hi / lo terms
     for (int i = t; i < kHeadDim * kBits / 4; i += kEThreads) {
         // consecutive threads take consecutive rows: the LDS writes hit
         // consecutive banks
@@ -129,7 +155,7 @@ __global__ __launch_bounds__(kEThreads, 2) void k_encode_mfma(EncArgs a) {
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float wf = W[(32 * g + 8 * j + e) * kBits + col];
+                const float wf = W[(32 * j + 8 * g + e) * kBits + col];
                 const uint16_t hb = f32_to_bf16(wf);  // nearest even; NaN stays NaN
                 const float hf = __uint_as_float((uint32_t)hb << 16);
                 const uint16_t lb = f32_to_bf16(wf - hf);
@@ -145,6 +171,10 @@ __global__ __launch_bounds__(kEThreads, 2) void k_encode_mfma(EncArgs a) {
     __syncthreads();
 
     const int64_t n_tiles = a.tiles_per_seg * a.n_seg;
+    // the batch entry's length and row count, read again only when a tile
+    // belongs to another entry (consecutive tiles mostly share one)
+    int s_cur = -1;
+    int64_t l0_cur = 0, rows_cur = 0;
     for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
         const int s = (int)(tile / a.tiles_per_seg);
         const int64_t r0 = (tile % a.tiles_per_seg) * kERows;
@@ -152,9 +182,14 @@ __global__ __launch_bounds__(kEThreads, 2) void k_encode_mfma(EncArgs a) {
         if (a.mode == 0) {
             rows = a.n_rows;
         } else {
-            l0 = a.seq_len[s];
-            const int n = a.n_new[s];
-            rows = append_ok(l0, n, a.t_max, a.max_ctx) ? n : 0;
+            if (s != s_cur) {
+                s_cur = s;
+                l0_cur = a.seq_len[s];
+                const int n = a.n_new[s];
+                rows_cur = append_ok(l0_cur, n, a.t_max, a.max_ctx) ? n : 0;
+            }
+            l0 = l0_cur;
+            rows = rows_cur;
         }
         if (r0 >= rows) continue;
         const int nr = rows - r0 < kERows ? (int)(rows - r0) : kERows;
@@ -174,7 +209,7 @@ __global__ __launch_bounds__(kEThreads, 2) void k_encode_mfma(EncArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 xa[mt][j] = uvec4{0u, 0u, 0u, 0u};
-                if (src) xa[mt][j] = *reinterpret_cast<const uvec4 *>(src + 32 * g + 8 * j);
+                if (src) xa[mt][j] = *reinterpret_cast<const uvec4 *>(src + 32 * j + 8 * g);
             }
         }
         if (a.mode == 1 && a.k_new) {
@@ -187,9 +222,9 @@ __global__ __launch_bounds__(kEThreads, 2) void k_encode_mfma(EncArgs a) {
                     const int64_t nrow = (((int64_t)s * a.t_max + r) * a.Hkv + h) * kHeadDim;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        *reinterpret_cast<uvec4 *>(a.k_cache + crow + 32 * g + 8 * j) = xa[mt][j];
-                        *reinterpret_cast<uvec4 *>(a.v_cache + crow + 32 * g + 8 * j) =
-                            *reinterpret_cast<const uvec4 *>(a.v_new + nrow + 32 * g + 8 * j);
+                        *reinterpret_cast<uvec4 *>(a.k_cache + crow + 32 * j + 8 * g) = xa[mt][j];
+                        *reinterpret_cast<uvec4 *>(a.v_cache + crow + 32 * j + 8 * g) =
+                            *reinterpret_cast<const uvec4 *>(a.v_new + nrow + 32 * j + 8 * g);
                     }
                 }
             }
@@ -199,7 +234,7 @@ __global__ __launch_bounds__(kEThreads, 2) void k_encode_mfma(EncArgs a) {
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<uvec4 *>(&sm.xs[16 * mt + c][32 * g + 8 * j]) = xa[mt][j];
+                *reinterpret_cast<uvec4 *>(&sm.xs[16 * mt + c][32 * j + 8 * g]) = xa[mt][j];
 
         // ---- row norms: row c of M tile mt, over the four lane groups
         float xnorm[4];
@@ -236,37 +271,55 @@ __global__ __launch_bounds__(kEThreads, 2) void k_encode_mfma(EncArgs a) {
             }
         __syncthreads();  // xs complete for the recomputations
 
-        // ---- bits: decided ones by ballot, the others recomputed
+        // ---- bits: the decided ones by ballot in one straight pass (lane L
+        // assembles the word of row L), then, only if some bit lies inside
+        // the band, a second pass recomputes those exactly.
+        float xnr[4][4];  // the norm of row 16 mt + 4 g + i
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xnr[mt][i] = __shfl(xnorm[mt], 4 * g + i, 64);
         uint32_t wordv = 0;
+        bool unsure = false;
+        const int gg = (lane >> 2) & 3;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int R = 16 * mt + 4 * g + i;
-                const float xn = __shfl(xnorm[mt], 4 * g + i, 64);
+                const bool valid = 16 * mt + 4 * g + i < nr;
                 uint64_t bits[2];
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     const float y = acc[mt][nt][i];
-                    const bool valid = R < nr;
-                    const bool sure = fabsf(y) > band(xn, wnorm[nt]);
-                    uint64_t bm = __ballot(valid && sure && y > 0.f);
-                    uint64_t um = __ballot(valid && !sure);
-                    while (um) {
-                        const int lb = __builtin_ctzll(um);
-                        um &= um - 1;
-                        const int Rf = 16 * mt + 4 * (lb >> 4) + i;
-                        const int col = 32 * wv + 16 * nt + (lb & 15);
-                        if (exact_bit(sm, Rf, col)) bm |= 1ull << lb;
-                    }
-                    bits[nt] = bm;
+                    const bool sure = fabsf(y) > band(xnr[mt][i], wnorm[nt]);
+                    unsure |= valid && !sure;
+                    bits[nt] = __ballot(valid && sure && y > 0.f);
                 }
                 // lane L holds the word of row L: L = 16 mt + 4 gg + i
-                const int gg = (lane >> 2) & 3;
                 const uint32_t wd = (uint32_t)((bits[0] >> (16 * gg)) & 0xFFFFu) |
                                     ((uint32_t)((bits[1] >> (16 * gg)) & 0xFFFFu) << 16);
                 if ((lane >> 4) == mt && (lane & 3) == i) wordv = wd;
             }
+        if (__ballot(unsure) != 0) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool valid = 16 * mt + 4 * g + i < nr;
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        const float y = acc[mt][nt][i];
+                        uint64_t um = __ballot(valid && !(fabsf(y) > band(xnr[mt][i], wnorm[nt])));
+                        while (um) {
+                            const int lb = __builtin_ctzll(um);
+                            um &= um - 1;
+                            const int Rf = 16 * mt + 4 * (lb >> 4) + i;
+                            const int cb = 16 * nt + (lb & 15);  // bit of the word
+                            if (exact_bit(sm, Rf, 32 * wv + cb) && lane == Rf) wordv |= 1u << cb;
+                        }
+                    }
+                }
+        }
         if (lane < nr) {
             const int64_t r = r0 + lane;
             uint32_t *dst = a.mode == 0 ? a.codes_out + (r * a.n_heads + h) * kWords
