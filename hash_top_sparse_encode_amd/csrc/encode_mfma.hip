@@ -153,8 +153,14 @@ struct ETile {
 __device__ __forceinline__ ETile tile_of(const EncArgs &a, const ESmem &sm, int64_t tile, int64_t n_tiles) {
     ETile e{0, 0, 0, 0};
     if (tile >= n_tiles) return e;
-    e.s = (int)(tile / a.tiles_per_seg);
-    e.r0 = (tile % a.tiles_per_seg) * kERows;
+    if (n_tiles <= 0x7FFFFFFF) {  // 32-bit division (the 64-bit one is a long routine)
+        const uint32_t t32 = (uint32_t)tile, tps = (uint32_t)a.tiles_per_seg;
+        e.s = (int)(t32 / tps);
+        e.r0 = (int64_t)(t32 - (uint32_t)e.s * tps) * kERows;
+    } else {
+        e.s = (int)(tile / a.tiles_per_seg);
+        e.r0 = (tile % a.tiles_per_seg) * kERows;
+    }
     int64_t rows;
     if (a.mode == 0) {
         rows = a.n_rows;
