@@ -170,10 +170,37 @@ def cpu_baseline(spec, reps):
             list(ex.map(decode, units))
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
+    # The same step on one core, and the oracle's key encoder on its own
+    # (one unit's prefilled rows, all threads): the encode is not part of a
+    # decode step, so it is reported beside it.
+    t0 = time.perf_counter()
+    for u in units:
+        decode(u)
+    t_one = time.perf_counter() - t0
+    K0 = ctx[units[0]][0]
+    t0 = time.perf_counter()
+    oracle.encode(K0, w[0], threads=cores)
+    t_enc = time.perf_counter() - t0
     return {"value": 1.0 / t, "unit": "steps/s", "cores": cores, "kind": "oracle",
             "sample": f"full decode step (all {len(units)} (batch, KV head) units, context "
                       f"{spec.lengths[0]}, top-k {spec.topk[0]}), median of {reps} runs; "
-                      f"{cores} threads over units"}
+                      f"{cores} threads over units",
+            "one_core_steps_per_s": 1.0 / t_one,
+            "encode_rows_per_s": K0.shape[0] / t_enc,
+            "encode_sample": f"oracle key encode of one unit's {K0.shape[0]} rows on "
+                             f"{cores} threads",
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -254,6 +281,34 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     steps_per_s = args.steps / wall
     dec_ms = ev0.elapsed_time(ev1) / args.steps
+    # Spread of single steps: one event pair per step over a second pass
+    # (the pairs add small gaps, so this pass is not the headline).
+    n_dist = min(args.steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_dist)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(args.warmup + args.steps + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+
+    def pct(p):
+        return step_us[min(len(step_us) - 1, int(p * len(step_us)))]
+
+    # Device-to-device copy bandwidth in the same run: the practical
+    # streaming rate the step's bytes can be set against.
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(3)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * src.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
     status = [ly.cache.status() for ly in layers]
     if any(status):
         print(f"[bench] device status flags set: {status}", file=sys.stderr)
@@ -326,7 +381,11 @@ def main():
             "traffic_bytes_per_launch": traffic_bytes,
             "alg_bytes_per_launch": step_bytes,
             "launch_us": dec_ms * 1e3,
+            "copy_GBps": copy_gbs,
+            "frac_of_copy": achieved / copy_gbs,
         },
+        "step_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9),
+                    "steps": n_dist, "how": "one HIP event pair per step, second pass"},
         "prefill_encode": prefill,
     }
     if args.copy_probe:

@@ -58,6 +58,8 @@ def lib():
         L.oracle_select.restype = i64
         L.oracle_attend.argtypes = [vp, ci, vp, vp, i64, ci, vp, i64, vp]
         L.oracle_attend.restype = ci
+        L.oracle_exact_topk.argtypes = [vp, vp, i64, ci, i64, i64, vp]
+        L.oracle_exact_topk.restype = i64
         _lib = L
     return _lib
 
@@ -174,3 +176,47 @@ def decode_unit(q_group: np.ndarray, w: np.ndarray, K: np.ndarray, V: np.ndarray
     idx = select(scores, k)
     out = attend(q_group, K, V, idx)
     return {"qcodes": qcodes, "kcodes": kcodes, "scores": scores, "idx": idx, "out": out}
+
+
+def exact_topk(q: np.ndarray, K: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k_eff = min(k, n) keys of K [n][d] (bf16) with the largest
+    exact logits q . k_i (q bf16 [d]; sequential double sum, lower index first
+    among equal logits), in ascending order."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    K = np.ascontiguousarray(K, dtype=np.uint16)
+    n, d = K.shape
+    assert q.shape == (d,)
+    idx = np.zeros(max(min(int(k), n), 0), dtype=np.int64)
+    m = lib().oracle_exact_topk(q.ctypes.data, K.ctypes.data, d, d, n, int(k), idx.ctypes.data)
+    if m < 0:
+        raise MemoryError("oracle_exact_topk")
+    return idx[:m]
+
+
+def overlap(sel: np.ndarray, exact: np.ndarray) -> int:
+    """|S intersect E|: how many of the Hamming-selected keys are in the exact top-k."""
+    return int(np.intersect1d(np.asarray(sel), np.asarray(exact)).size)
+
+
+def tie_bucket(scores: np.ndarray, k: int) -> tuple:
+    """The Hamming selection's cut, for the review's tie analysis (major
+    comment 1): with k_eff = min(k, n), T = the k_eff-th smallest score,
+    below = keys scoring under T, at = keys scoring exactly T (the bucket the
+    cut falls in; the selection takes k_eff - below of them).  Returns
+    (T, below, at, k_eff), or (-1, 0, 0, 0) when k_eff = 0."""
+    scores = np.asarray(scores)
+    k_eff = max(0, min(int(k), scores.size))
+    if k_eff == 0:
+        return (-1, 0, 0, 0)
+    T = int(np.sort(scores, kind="stable")[k_eff - 1])
+    return (T, int((scores < T).sum()), int((scores == T).sum()), k_eff)
+
+
+def recall_unit(q_group: np.ndarray, K: np.ndarray, k: int, sel: np.ndarray,
+                scores: np.ndarray) -> dict:
+    """The recall analysis of one (batch, KV head) unit: for every query head
+    of the group, its exact top-k set and the overlap with the group's
+    Hamming selection `sel`; and the tie bucket of the group's scores."""
+    exact = [exact_topk(q_group[h], K, k) for h in range(q_group.shape[0])]
+    return {"exact": exact, "overlap": [overlap(sel, e) for e in exact],
+            "tie": tie_bucket(scores, k)}

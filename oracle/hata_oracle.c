@@ -166,3 +166,49 @@ int oracle_attend(const uint16_t *q, int G, const uint16_t *K, const uint16_t *V
     free(z);
     return 0;
 }
+
+/*
+ * The exact top-k of one query head, the comparison set that the referee
+ * report of the HATA review asks for ("What would settle it": rank the keys
+ * by their exact q.k scores and compare that top-k set with the Hamming
+ * selection; major comment 1: exact top-k agreement).
+ * q: bf16 [d]; K: bf16 rows, row i at K + i * kv_stride, n rows.
+ *   z_i = sum_{t = 0..d-1} q[t] * K[i][t], a sequential double sum in
+ *         ascending t (every product of two bf16 values is exact in double);
+ *   the k_eff = min(k, n) keys of largest z_i are kept (k < 0 counts as 0),
+ *   equal z_i going to the lower index; their indices are written to
+ *   idx[0..k_eff) in ascending order.
+ * Returns k_eff, or -1 if memory runs out.  The scale 1/sqrt(d) of the
+ * logits does not change the order and is left out.
+ */
+typedef struct {
+    double z;
+    int64_t index;
+} logit_key;
+
+static int by_logit_desc_then_index(const void *a, const void *b) {
+    const logit_key *x = (const logit_key *)a, *y = (const logit_key *)b;
+    if (x->z != y->z) return x->z > y->z ? -1 : 1;
+    if (x->index != y->index) return x->index < y->index ? -1 : 1;
+    return 0;
+}
+
+int64_t oracle_exact_topk(const uint16_t *q, const uint16_t *K, int64_t kv_stride, int d,
+                          int64_t n, int64_t k, int64_t *idx) {
+    int64_t k_eff = k < n ? k : n;
+    if (k_eff <= 0) return 0;
+    logit_key *all = (logit_key *)malloc((size_t)n * sizeof *all);
+    if (!all) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        const uint16_t *krow = K + i * kv_stride;
+        double z = 0.0;
+        for (int t = 0; t < d; ++t) z = z + bf16_value(q[t]) * bf16_value(krow[t]);
+        all[i].z = z;
+        all[i].index = i;
+    }
+    qsort(all, (size_t)n, sizeof *all, by_logit_desc_then_index);
+    for (int64_t i = 0; i < k_eff; ++i) idx[i] = all[i].index;
+    free(all);
+    qsort(idx, (size_t)k_eff, sizeof *idx, by_index);
+    return k_eff;
+}
