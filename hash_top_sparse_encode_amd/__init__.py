@@ -9,7 +9,8 @@ there is no fallback of any kind.
 
 Names mirror the C ABI:
   hata_encode_keys, hata_append, hata_decode_workspace_bytes,
-  hata_decode_attn, hata_status_string
+  hata_decode_attn, hata_decode_step, hata_recall_workspace_bytes,
+  hata_exact_topk_recall, hata_status_string
 plus ``HataCache``, a holder of the caller-owned cache tensors.
 """
 from __future__ import annotations
@@ -45,7 +46,8 @@ HATA_DEV_BAD_NEW = 0x8
 HATA_DEV_STALL = 0x10
 
 EXPORTED_SYMBOLS = ("hata_encode_keys", "hata_append", "hata_decode_workspace_bytes",
-                    "hata_decode_attn", "hata_decode_step", "hata_status_string")
+                    "hata_decode_attn", "hata_decode_step", "hata_recall_workspace_bytes",
+                    "hata_exact_topk_recall", "hata_status_string")
 
 
 class _CCache(ctypes.Structure):
@@ -88,6 +90,11 @@ def lib() -> ctypes.CDLL:
         L.hata_decode_step.argtypes = [ctypes.POINTER(_CCache), vp, vp, vp, vp, vp, i32, vp, vp,
                                        sz, vp, vp, vp]
         L.hata_decode_step.restype = ctypes.c_int
+        L.hata_recall_workspace_bytes.argtypes = [ctypes.POINTER(_CCache)]
+        L.hata_recall_workspace_bytes.restype = sz
+        L.hata_exact_topk_recall.argtypes = [ctypes.POINTER(_CCache), vp, vp, i32, vp, vp, vp,
+                                             vp, vp, vp, sz, vp]
+        L.hata_exact_topk_recall.restype = ctypes.c_int
         L.hata_status_string.argtypes = [ctypes.c_int]
         L.hata_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -278,3 +285,50 @@ def hata_decode_step(cache: HataCache, k_new: torch.Tensor, v_new: torch.Tensor,
                                 _ptr(sel_idx_out), _ptr(scores_out), _stream(stream))
     _check("hata_decode_step", st)
     return out
+
+
+def hata_recall_workspace_bytes(cache: HataCache) -> int:
+    c = cache.c_struct()
+    return int(lib().hata_recall_workspace_bytes(ctypes.byref(c)))
+
+
+def alloc_recall_workspace(cache: HataCache) -> torch.Tensor:
+    """A device byte tensor for hata_exact_topk_recall (no initial contents needed)."""
+    n = hata_recall_workspace_bytes(cache)
+    if n == 0:
+        raise ValueError("unsupported cache shape")
+    return torch.empty(n, dtype=torch.uint8, device=cache.k.device)
+
+
+def hata_exact_topk_recall(cache: HataCache, q: torch.Tensor, topk: torch.Tensor, k_max: int,
+                           sel_idx: torch.Tensor, scores: torch.Tensor,
+                           workspace: torch.Tensor, overlap_out: torch.Tensor = None,
+                           tie_out: torch.Tensor = None, exact_idx_out: torch.Tensor = None,
+                           stream=None):
+    """Recall analysis of a decode call's selection (its sel_idx_out and
+    scores_out): returns (overlap int32 [batch][n_q_heads], tie int32
+    [batch][n_kv_heads][4] = (T, below, at, k_eff)); exact_idx_out (int32
+    [batch][n_q_heads][k_max]) receives each head's exact top-k if given."""
+    B, Hq, Hkv = cache.batch, cache.n_q_heads, cache.n_kv_heads
+    dev = cache.k.device
+    _need(q, "q", torch.bfloat16, B * Hq * HEAD_DIM)
+    _need(topk, "topk", torch.int32, B)
+    _need(sel_idx, "sel_idx", torch.int32, B * Hkv * int(k_max))
+    _need(scores, "scores", torch.int16, B * Hkv * cache.max_ctx)
+    _need(workspace, "workspace", torch.uint8)
+    if overlap_out is None:
+        overlap_out = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+    if tie_out is None:
+        tie_out = torch.empty((B, Hkv, 4), dtype=torch.int32, device=dev)
+    _need(overlap_out, "overlap_out", torch.int32, B * Hq)
+    _need(tie_out, "tie_out", torch.int32, B * Hkv * 4)
+    if exact_idx_out is not None:
+        _need(exact_idx_out, "exact_idx_out", torch.int32, B * Hq * int(k_max))
+    c = cache.c_struct()
+    st = lib().hata_exact_topk_recall(ctypes.byref(c), q.data_ptr(), topk.data_ptr(), int(k_max),
+                                      sel_idx.data_ptr(), scores.data_ptr(),
+                                      overlap_out.data_ptr(), tie_out.data_ptr(),
+                                      _ptr(exact_idx_out), workspace.data_ptr(),
+                                      workspace.numel(), _stream(stream))
+    _check("hata_exact_topk_recall", st)
+    return overlap_out, tie_out

@@ -6,6 +6,7 @@
 
 #include "../../include/hata.h"
 #include "hata_internal.h"
+#include "recall_plan.h"
 
 using namespace hata;
 
@@ -121,6 +122,35 @@ hata_status hata_decode_step(const hata_cache *c, const uint16_t *k_new, const u
     if (!k_new || !v_new) return HATA_ERR_INVALID_ARG;
     return decode_common(c, k_new, v_new, q, w_h, topk, k_max, out, workspace, ws_bytes,
                          sel_idx_out, scores_out, stream);
+}
+
+size_t hata_recall_workspace_bytes(const hata_cache *c) {
+    if (!c) return 0;
+    if (c->head_dim != kHeadDim || c->n_bits != kBits) return 0;
+    RecallPlan p;
+    if (!make_recall_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, &p)) return 0;
+    return p.total;
+}
+
+hata_status hata_exact_topk_recall(const hata_cache *c, const uint16_t *q, const int32_t *topk,
+                                   int32_t k_max, const int32_t *sel_idx,
+                                   const uint16_t *scores, int32_t *overlap_out,
+                                   int32_t *tie_out, int32_t *exact_idx_out, void *workspace,
+                                   size_t ws_bytes, void *stream) {
+    hata_status st = check_cache(c);
+    if (st != HATA_OK) return st;
+    if (!q || !topk || !sel_idx || !scores || !overlap_out || !tie_out || k_max < 0)
+        return HATA_ERR_INVALID_ARG;
+    if (!aligned16(q)) return HATA_ERR_INVALID_ARG;
+    RecallPlan p;
+    if (!make_recall_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, &p))
+        return HATA_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return HATA_ERR_WORKSPACE;
+    hipError_t e = launch_recall(p, c->k, c->seq_len, q, topk, k_max, sel_idx, scores,
+                                 overlap_out, tie_out, exact_idx_out, workspace,
+                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
 }
 
 }  // extern "C"

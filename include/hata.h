@@ -207,6 +207,51 @@ hata_status hata_decode_step(const hata_cache *c, const uint16_t *k_new, const u
                              int32_t k_max, uint16_t *out, void *workspace, size_t ws_bytes,
                              int32_t *sel_idx_out, uint16_t *scores_out, void *stream);
 
+/* Bytes of device workspace hata_exact_topk_recall needs for this cache
+ * (depends on batch, heads and max_ctx only; about 17 bytes per position and
+ * query head).  Returns 0 for an unsupported or invalid cache. */
+size_t hata_recall_workspace_bytes(const hata_cache *c);
+
+/*
+ * Recall analysis of a Hamming selection -- the test the referee report of
+ * the HATA review proposes ("What would settle it": compare the exact top-k
+ * key set by q.k with the Hamming-selected one) and the tie analysis of its
+ * major comment 1 (how many keys share the score at the cut).  Not part of
+ * the decode step; call it after hata_decode_attn or hata_decode_step with
+ * their debug outputs, on the same cache state and query.
+ *   q          device bf16 [batch][n_q_heads][128], the step's query.
+ *   topk, k_max as given to the decode call (k_eff = min(topk[b], k_max,
+ *              seq_len[b]), topk < 0 counting as 0).
+ *   sel_idx    device int32 [batch][n_kv_heads][k_max], the decode call's
+ *              sel_idx_out.
+ *   scores     device u16 [batch][n_kv_heads][max_ctx], its scores_out.
+ *   overlap_out device int32 [batch][n_q_heads]: for query head h, the
+ *              number of selected keys of its group that are in the exact
+ *              top-k_eff of h.  The exact top-k ranks the keys i < seq_len[b]
+ *              by z_i = sum_d q_d k_{i,d}, a sequential double sum over
+ *              d = 0..127 (bf16 products are exact in double), largest
+ *              first, the lower index first among equal z_i.
+ *   tie_out    device int32 [batch][n_kv_heads][4]: (T, below, at, k_eff)
+ *              with T the k_eff-th smallest Hamming score of the group,
+ *              `below` the keys scoring under T and `at` the keys scoring T;
+ *              (-1, 0, 0, 0) when k_eff = 0.
+ *   exact_idx_out optional device int32 [batch][n_q_heads][k_max]: each
+ *              query head's exact top-k indices in ascending order, -1 after
+ *              k_eff.
+ *   workspace  device, >= hata_recall_workspace_bytes(c) bytes, 256-byte
+ *              aligned; no initial contents needed (scratch of this call).
+ * The sets are identical to the definition above for finite inputs: fp32
+ * estimates decide every key whose margin to the cut exceeds their proven
+ * error bound, and the others are ranked on the exact double sums.
+ * Errors: HATA_ERR_INVALID_ARG (null pointers, unaligned q, k_max < 0),
+ * HATA_ERR_UNSUPPORTED, HATA_ERR_WORKSPACE, HATA_ERR_HIP.
+ */
+hata_status hata_exact_topk_recall(const hata_cache *c, const uint16_t *q, const int32_t *topk,
+                                   int32_t k_max, const int32_t *sel_idx,
+                                   const uint16_t *scores, int32_t *overlap_out,
+                                   int32_t *tie_out, int32_t *exact_idx_out, void *workspace,
+                                   size_t ws_bytes, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *hata_status_string(hata_status s);
 

@@ -127,3 +127,40 @@ def test_workspace_plan(B, Hq, Hkv, N):
     assert n % 256 == 0
     assert hata.lib().hata_decode_workspace_bytes(ctypes.byref(cache(head_dim=64)), 1) == 0
     assert hata.lib().hata_decode_workspace_bytes(None, 1) == 0
+
+
+def recall(c, q=FAKE, topk=FAKE, k_max=16, sel=FAKE, sc=FAKE, ov=FAKE, tie=FAKE, ex=None,
+           ws=FAKE, ws_bytes=1 << 40):
+    return hata.lib().hata_exact_topk_recall(ctypes.byref(c), q, topk, k_max, sel, sc, ov, tie,
+                                             ex, ws, ws_bytes, None)
+
+
+def test_recall_validation():
+    E = hata
+    assert recall(cache(head_dim=64)) == E.HATA_ERR_UNSUPPORTED
+    assert recall(cache(n_q_heads=32)) == E.HATA_ERR_UNSUPPORTED
+    assert recall(cache(k=0)) == E.HATA_ERR_INVALID_ARG
+    assert recall(cache(), q=0) == E.HATA_ERR_INVALID_ARG
+    assert recall(cache(), q=FAKE + 2) == E.HATA_ERR_INVALID_ARG
+    assert recall(cache(), topk=0) == E.HATA_ERR_INVALID_ARG
+    assert recall(cache(), sel=0) == E.HATA_ERR_INVALID_ARG
+    assert recall(cache(), sc=0) == E.HATA_ERR_INVALID_ARG
+    assert recall(cache(), ov=0) == E.HATA_ERR_INVALID_ARG
+    assert recall(cache(), tie=0) == E.HATA_ERR_INVALID_ARG
+    assert recall(cache(), k_max=-1) == E.HATA_ERR_INVALID_ARG
+    assert recall(cache(), ws=0) == E.HATA_ERR_WORKSPACE
+    assert recall(cache(), ws=FAKE + 64) == E.HATA_ERR_WORKSPACE
+    assert recall(cache(), ws_bytes=1000) == E.HATA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 8, 8, 4096), (4, 32, 8, 131072), (3, 6, 3, 1000)])
+def test_recall_workspace_plan(B, Hq, Hkv, N):
+    c = cache(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, max_ctx=N)
+    n = hata.lib().hata_recall_workspace_bytes(ctypes.byref(c))
+    # fp32 estimates (row stride rounded up to 64), band indices, exact
+    # logits and flags per query head and position, per-block key norms
+    lo = B * Hq * N * (4 + 4 + 8 + 1)
+    assert lo <= n <= lo + B * Hq * 64 * 4 + B * Hkv * (N // 1024 + 1) * 8 + 5 * 256
+    assert n % 256 == 0
+    assert hata.lib().hata_recall_workspace_bytes(ctypes.byref(cache(head_dim=64))) == 0
+    assert hata.lib().hata_recall_workspace_bytes(None) == 0
