@@ -90,7 +90,9 @@ def _pmc_per_dispatch(path):
 
 def pmc_summary(fetch_csv, write_csv):
     """Key: value lines for the traffic profile.  The decode kernel's
-    counters are averaged over its dispatches; the calibration copy is the
+    counters are the median over its dispatches (the run also makes one
+    decode call with the debug outputs, which writes the scores); the
+    calibration copy is the
     last 4 __amd_rocclr_copyBuffer dispatches (bench.py --copy-probe ends
     with 4 copies of COPY_PROBE_BYTES)."""
     vals = {}
@@ -100,7 +102,7 @@ def pmc_summary(fetch_csv, write_csv):
         cp = [v for k, v in per.items() if "copyBuffer" in k]
         if len(dec) != 1 or len(cp) != 1 or len(cp[0]) < 4:
             raise SystemExit(f"{path}: expected one decode kernel and >= 4 copies")
-        vals[f"decode_{counter}_kib_per_dispatch"] = statistics.mean(dec[0])
+        vals[f"decode_{counter}_kib_per_dispatch"] = statistics.median(dec[0])
         vals[f"decode_{counter}_dispatches"] = len(dec[0])
         vals[f"copy_{counter}_kib"] = statistics.mean(cp[0][-4:])
     lines = [f"decode_sources_sha256: {decode_sources_digest()}",
@@ -212,6 +214,7 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path "
               "has no multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
+    import numpy as np
     import torch
     import hash_top_sparse_encode_amd as hata
     import synth
@@ -340,6 +343,48 @@ def main():
         "mfma_peak_TFLOPs": 2500.0,
     }
 
+    # The recall analysis of one decode call (layer 0, step query 0, no
+    # append): each query head's exact top-k against its group's Hamming
+    # selection, and the tie bucket at the cut.
+    ly = layers[0]
+    sel = torch.empty((B, Hkv, base.k_max), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, Hkv, base.max_ctx), dtype=torch.int16, device=dev)
+    hata.hata_decode_attn(ly.cache, queries[0], base.w, base.topk, base.k_max, ly.out, ly.ws,
+                          sel_idx_out=sel, scores_out=sc)
+    rws = hata.alloc_recall_workspace(ly.cache)
+    ov = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+    tie = torch.empty((B, Hkv, 4), dtype=torch.int32, device=dev)
+    rec_ms = []
+    for r in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        hata.hata_exact_topk_recall(ly.cache, queries[0], base.topk, base.k_max, sel, sc, rws,
+                                    overlap_out=ov, tie_out=tie)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if r > 0:
+            rec_ms.append(e0.elapsed_time(e1))
+    rec_ctx = int(ly.cache.seq_len[0].item())
+    tie_h = tie.cpu().numpy().astype(float)
+    ov_h = ov.cpu().numpy().astype(float)
+    k_eff = tie_h[..., 3]
+    rec_s = statistics.mean(rec_ms) * 1e-3
+    recall = {
+        "what": "hata_exact_topk_recall after one decode call on the same cache: each query "
+                "head's exact top-k by q.k against its group's Hamming selection, and the "
+                "tie bucket at the selection's cut",
+        "context": rec_ctx,
+        "ms": rec_s * 1e3,
+        "key_rows_GBps": B * Hkv * rec_ctx * 256 / rec_s / 1e9,
+        "overlap_frac": float(ov_h.sum() / (k_eff.sum() * (Hq // Hkv))),
+        "overlap_frac_min_head": float((ov_h / np.repeat(k_eff, Hq // Hkv, axis=1)).min()),
+        "cut_T_mean": float(tie_h[..., 0].mean()),
+        "below_cut_mean": float(tie_h[..., 1].mean()),
+        "tied_at_cut_mean": float(tie_h[..., 2].mean()),
+        "taken_from_tie_mean": float((k_eff - tie_h[..., 1]).mean()),
+    }
+    del rws
+
     n_ctx = ctx0 + (args.steps // L) / 2.0  # mean context over the timed steps
     step_bytes = algorithmic_bytes(B, Hq, Hkv, n_ctx, K)
     achieved = step_bytes / (dec_ms * 1e-3) / 1e9
@@ -387,6 +432,7 @@ def main():
         "step_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9),
                     "steps": n_dist, "how": "one HIP event pair per step, second pass"},
         "prefill_encode": prefill,
+        "recall": recall,
     }
     if args.copy_probe:
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(7)
