@@ -385,6 +385,42 @@ def main():
     }
     del rws
 
+    # The offloaded layout: the same workload with the K/V rows in pinned host
+    # memory (codes, workspace and queries stay in device memory); each step
+    # reads its selected rows, and writes its appended ones, over the host link.
+    off = hata.HataCache(B, Hq, Hkv, base.max_ctx, device=dev, offload=True,
+                         codes=base.cache.codes.clone(), seq_len=base.n_pre.clone())
+    off.k.copy_(base.cache.k)
+    off.v.copy_(base.cache.v)
+    off_ws = hata.alloc_workspace(off, base.k_max)
+    off_out = torch.empty_like(base.out)
+
+    def off_step(s):
+        hata.hata_decode_step(off, k_new, v_new, queries[s % QUERIES], base.w, base.topk,
+                              base.k_max, off_out, off_ws)
+
+    n_off = max(1, min(args.steps, 50))
+    for s in range(8):
+        off_step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(n_off):
+        off_step(8 + s)
+    torch.cuda.synchronize()
+    off_s = (time.perf_counter() - t0) / n_off
+    if off.status():
+        print(f"[bench] offload status flags set: {off.status()}", file=sys.stderr)
+        sys.exit(1)
+    offload = {
+        "what": "hata_decode_step with the K/V cache in pinned host memory (codes in HBM)",
+        "steps": n_off,
+        "steps_per_s": 1.0 / off_s,
+        "us_per_step": off_s * 1e6,
+        "selected_rows_GBps": B * Hkv * K * 512 / off_s / 1e9,
+        "vs_device_resident": (1.0 / off_s) / steps_per_s,
+    }
+    del off, off_ws
+
     n_ctx = ctx0 + (args.steps // L) / 2.0  # mean context over the timed steps
     step_bytes = algorithmic_bytes(B, Hq, Hkv, n_ctx, K)
     achieved = step_bytes / (dec_ms * 1e-3) / 1e9
@@ -433,6 +469,7 @@ def main():
                     "steps": n_dist, "how": "one HIP event pair per step, second pass"},
         "prefill_encode": prefill,
         "recall": recall,
+        "offload": offload,
     }
     if args.copy_probe:
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(7)

@@ -95,6 +95,11 @@ def lib() -> ctypes.CDLL:
         L.hata_exact_topk_recall.argtypes = [ctypes.POINTER(_CCache), vp, vp, i32, vp, vp, vp,
                                              vp, vp, vp, sz, vp]
         L.hata_exact_topk_recall.restype = ctypes.c_int
+        # The HIP runtime the library is linked against (dlsym on the
+        # library's handle also searches its dependencies): device addresses
+        # of pinned host tensors that hold an offloaded K/V cache.
+        L.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(vp), vp, ctypes.c_uint]
+        L.hipHostGetDevicePointer.restype = ctypes.c_int
         L.hata_status_string.argtypes = [ctypes.c_int]
         L.hata_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -139,36 +144,68 @@ def _need(t: torch.Tensor, name: str, dtype, numel: int | None = None):
         raise ValueError(f"{name} must hold {numel} elements, has {t.numel()}")
 
 
+def _need_kv(t: torch.Tensor, name: str, numel: int):
+    """K/V cache tensors live in device memory, or in pinned host memory (the
+    offloaded layout: the kernels read the selected rows over the host link)."""
+    if isinstance(t, torch.Tensor) and not t.is_cuda:
+        if not t.is_pinned():
+            raise ValueError(f"{name} on the host must be pinned (pin_memory=True)")
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.numel() != numel:
+            raise ValueError(f"{name} must be a contiguous bf16 tensor of {numel} elements")
+        return
+    _need(t, name, torch.bfloat16, numel)
+
+
+def _device_address(t: torch.Tensor) -> int:
+    """The address kernels use for t: its own for device memory, the mapped
+    device address for pinned host memory."""
+    if t.is_cuda:
+        return t.data_ptr()
+    dev = ctypes.c_void_p()
+    err = lib().hipHostGetDevicePointer(ctypes.byref(dev), ctypes.c_void_p(t.data_ptr()), 0)
+    if err != 0 or not dev.value:
+        raise ValueError(f"host tensor at {t.data_ptr():#x} is not mapped into the device's "
+                         f"address space (hipHostGetDevicePointer error {err})")
+    return dev.value
+
+
 class HataCache:
     """Caller-owned cache tensors of include/hata.h's hata_cache.
 
-    k, v   : bf16 [batch][n_kv_heads][max_ctx][128]
+    k, v   : bf16 [batch][n_kv_heads][max_ctx][128], on the device or, for the
+             offloaded layout, pinned host tensors (``offload=True`` allocates
+             them so)
     codes  : int32 (u32 bit patterns) [batch][n_kv_heads][max_ctx][4]
     seq_len: int32 [batch]
     ctrl   : int32 [ctrl_words(batch, n_kv_heads)], zero at creation
     """
 
     def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, max_ctx: int,
-                 device="cuda", k=None, v=None, codes=None, seq_len=None, ctrl=None):
+                 device="cuda", k=None, v=None, codes=None, seq_len=None, ctrl=None,
+                 offload: bool = False):
         self.batch, self.n_q_heads, self.n_kv_heads, self.max_ctx = (
             int(batch), int(n_q_heads), int(n_kv_heads), int(max_ctx))
         shape = (self.batch, self.n_kv_heads, self.max_ctx, HEAD_DIM)
-        self.k = k if k is not None else torch.empty(shape, dtype=torch.bfloat16, device=device)
-        self.v = v if v is not None else torch.empty(shape, dtype=torch.bfloat16, device=device)
+        kv_dev = dict(device="cpu", pin_memory=True) if offload else dict(device=device)
+        self.k = k if k is not None else torch.empty(shape, dtype=torch.bfloat16, **kv_dev)
+        self.v = v if v is not None else torch.empty(shape, dtype=torch.bfloat16, **kv_dev)
         self.codes = codes if codes is not None else torch.zeros(
             shape[:3] + (CODE_WORDS,), dtype=torch.int32, device=device)
         self.seq_len = seq_len if seq_len is not None else torch.zeros(
             self.batch, dtype=torch.int32, device=device)
         self.ctrl = ctrl if ctrl is not None else torch.zeros(
             ctrl_words(self.batch, self.n_kv_heads), dtype=torch.int32, device=device)
-        _need(self.k, "k", torch.bfloat16, self.batch * self.n_kv_heads * self.max_ctx * HEAD_DIM)
-        _need(self.v, "v", torch.bfloat16, self.k.numel())
+        _need_kv(self.k, "k", self.batch * self.n_kv_heads * self.max_ctx * HEAD_DIM)
+        _need_kv(self.v, "v", self.k.numel())
+        self._kv_addr = None
         _need(self.codes, "codes", torch.int32, self.batch * self.n_kv_heads * self.max_ctx * 4)
         _need(self.seq_len, "seq_len", torch.int32, self.batch)
         _need(self.ctrl, "ctrl", torch.int32, ctrl_words(self.batch, self.n_kv_heads))
 
     def c_struct(self, head_dim: int = HEAD_DIM, n_bits: int = N_BITS) -> _CCache:
-        return _CCache(self.k.data_ptr(), self.v.data_ptr(), self.codes.data_ptr(),
+        if self._kv_addr is None:
+            self._kv_addr = (_device_address(self.k), _device_address(self.v))
+        return _CCache(self._kv_addr[0], self._kv_addr[1], self.codes.data_ptr(),
                        self.seq_len.data_ptr(), self.ctrl.data_ptr(), self.batch,
                        self.n_q_heads, self.n_kv_heads, head_dim, n_bits, self.max_ctx)
 

@@ -79,7 +79,13 @@ typedef enum {
  * A key/value cache with its key-code cache, all device memory owned by the
  * caller.  Sequence b, KV head g, position p:
  *   k, v  : bf16  [batch][n_kv_heads][max_ctx][128], row (b, g, p) at
- *           ((b * n_kv_heads + g) * max_ctx + p) * 128
+ *           ((b * n_kv_heads + g) * max_ctx + p) * 128.  Device memory, or
+ *           pinned host memory mapped into the device's address space
+ *           (hipHostMalloc; pass its device address from
+ *           hipHostGetDevicePointer): the offloaded layout of the HATA
+ *           review ("offloaded" speed-ups in "Core claim"), where the codes,
+ *           the scan and the selection stay in device memory and only the
+ *           selected rows (and the appended ones) cross the host link.
  *   codes : u32   [batch][n_kv_heads][max_ctx][4]
  *   seq_len: int32 [batch], the number of valid positions of each sequence;
  *           positions [0, seq_len[b]) hold keys, values and codes.

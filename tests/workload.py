@@ -29,7 +29,7 @@ class GpuWorkload:
     """Device state of one synthetic decode workload."""
 
     def __init__(self, spec: synth.Spec, device, extra_ctx: int = 0, units=None,
-                 encode_prefill: bool = True):
+                 encode_prefill: bool = True, offload: bool = False):
         self.spec = spec
         self.device = device
         B, Hq, Hkv = spec.B, spec.Hq, spec.Hkv
@@ -37,7 +37,7 @@ class GpuWorkload:
         self.q_host = synth.gen_q(spec)
         self.w_host = synth.gen_w(spec)
         self.new_host = synth.gen_new_token(spec)
-        self.cache = hata.HataCache(B, Hq, Hkv, self.max_ctx, device=device)
+        self.cache = hata.HataCache(B, Hq, Hkv, self.max_ctx, device=device, offload=offload)
         self.cache.k.zero_()
         self.cache.v.zero_()
         for b in range(B):
