@@ -267,7 +267,7 @@ def alloc_workspace(cache: HataCache, k_max: int) -> torch.Tensor:
     n = hata_decode_workspace_bytes(cache, k_max)
     if n == 0:
         raise ValueError("unsupported cache shape")
-    return torch.zeros(n, dtype=torch.uint8, device=cache.k.device)
+    return torch.zeros(n, dtype=torch.uint8, device=cache.codes.device)
 
 
 def hata_decode_attn(cache: HataCache, q: torch.Tensor, w_h: torch.Tensor, topk: torch.Tensor,
@@ -334,7 +334,7 @@ def alloc_recall_workspace(cache: HataCache) -> torch.Tensor:
     n = hata_recall_workspace_bytes(cache)
     if n == 0:
         raise ValueError("unsupported cache shape")
-    return torch.empty(n, dtype=torch.uint8, device=cache.k.device)
+    return torch.empty(n, dtype=torch.uint8, device=cache.codes.device)
 
 
 def hata_exact_topk_recall(cache: HataCache, q: torch.Tensor, topk: torch.Tensor, k_max: int,
@@ -347,7 +347,7 @@ def hata_exact_topk_recall(cache: HataCache, q: torch.Tensor, topk: torch.Tensor
     [batch][n_kv_heads][4] = (T, below, at, k_eff)); exact_idx_out (int32
     [batch][n_q_heads][k_max]) receives each head's exact top-k if given."""
     B, Hq, Hkv = cache.batch, cache.n_q_heads, cache.n_kv_heads
-    dev = cache.k.device
+    dev = cache.codes.device
     _need(q, "q", torch.bfloat16, B * Hq * HEAD_DIM)
     _need(topk, "topk", torch.int32, B)
     _need(sel_idx, "sel_idx", torch.int32, B * Hkv * int(k_max))

@@ -35,7 +35,7 @@ def _say(msg):
 def run_recall(cache, q, topk, k_max, sel, sc):
     ws = hata.alloc_recall_workspace(cache)
     B, Hq = cache.batch, cache.n_q_heads
-    ex = torch.full((B, Hq, max(k_max, 1)), -7, dtype=torch.int32, device=cache.k.device)
+    ex = torch.full((B, Hq, max(k_max, 1)), -7, dtype=torch.int32, device=cache.codes.device)
     ex = ex[:, :, :k_max].contiguous()
     ov, tie = hata.hata_exact_topk_recall(cache, q, topk, k_max, sel, sc, ws, exact_idx_out=ex)
     torch.cuda.synchronize()
