@@ -45,7 +45,7 @@ HATA_DEV_TOPK_CLAMPED = 0x4
 HATA_DEV_BAD_NEW = 0x8
 HATA_DEV_STALL = 0x10
 
-EXPORTED_SYMBOLS = ("hata_encode_keys", "hata_append", "hata_decode_workspace_bytes",
+EXPORTED_SYMBOLS = ("hata_encode_keys", "hata_encode_keys_nbits", "hata_append", "hata_decode_workspace_bytes",
                     "hata_decode_attn", "hata_decode_step", "hata_recall_workspace_bytes",
                     "hata_exact_topk_recall", "hata_status_string")
 
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
         L.hata_encode_keys.argtypes = [vp, i64, i32, i64, i64, vp, vp, vp]
         L.hata_encode_keys.restype = ctypes.c_int
+        L.hata_encode_keys_nbits.argtypes = [vp, i64, i32, i64, i64, vp, i32, vp, vp]
+        L.hata_encode_keys_nbits.restype = ctypes.c_int
         L.hata_append.argtypes = [ctypes.POINTER(_CCache), vp, vp, vp, i32, vp, vp]
         L.hata_append.restype = ctypes.c_int
         L.hata_decode_workspace_bytes.argtypes = [ctypes.POINTER(_CCache), i32]
@@ -182,15 +184,17 @@ class HataCache:
 
     def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, max_ctx: int,
                  device="cuda", k=None, v=None, codes=None, seq_len=None, ctrl=None,
-                 offload: bool = False):
+                 offload: bool = False, n_bits: int = N_BITS):
         self.batch, self.n_q_heads, self.n_kv_heads, self.max_ctx = (
             int(batch), int(n_q_heads), int(n_kv_heads), int(max_ctx))
+        self.n_bits = int(n_bits)
+        words = self.n_bits // 32
         shape = (self.batch, self.n_kv_heads, self.max_ctx, HEAD_DIM)
         kv_dev = dict(device="cpu", pin_memory=True) if offload else dict(device=device)
         self.k = k if k is not None else torch.empty(shape, dtype=torch.bfloat16, **kv_dev)
         self.v = v if v is not None else torch.empty(shape, dtype=torch.bfloat16, **kv_dev)
         self.codes = codes if codes is not None else torch.zeros(
-            shape[:3] + (CODE_WORDS,), dtype=torch.int32, device=device)
+            shape[:3] + (words,), dtype=torch.int32, device=device)
         self.seq_len = seq_len if seq_len is not None else torch.zeros(
             self.batch, dtype=torch.int32, device=device)
         self.ctrl = ctrl if ctrl is not None else torch.zeros(
@@ -198,11 +202,13 @@ class HataCache:
         _need_kv(self.k, "k", self.batch * self.n_kv_heads * self.max_ctx * HEAD_DIM)
         _need_kv(self.v, "v", self.k.numel())
         self._kv_addr = None
-        _need(self.codes, "codes", torch.int32, self.batch * self.n_kv_heads * self.max_ctx * 4)
+        _need(self.codes, "codes", torch.int32,
+              self.batch * self.n_kv_heads * self.max_ctx * words)
         _need(self.seq_len, "seq_len", torch.int32, self.batch)
         _need(self.ctrl, "ctrl", torch.int32, ctrl_words(self.batch, self.n_kv_heads))
 
-    def c_struct(self, head_dim: int = HEAD_DIM, n_bits: int = N_BITS) -> _CCache:
+    def c_struct(self, head_dim: int = HEAD_DIM, n_bits: int = None) -> _CCache:
+        n_bits = self.n_bits if n_bits is None else n_bits
         if self._kv_addr is None:
             self._kv_addr = (_device_address(self.k), _device_address(self.v))
         return _CCache(self._kv_addr[0], self._kv_addr[1], self.codes.data_ptr(),
@@ -217,22 +223,31 @@ class HataCache:
 def hata_encode_keys(keys: torch.Tensor, w_h: torch.Tensor, codes_out: torch.Tensor = None,
                      stream=None) -> torch.Tensor:
     """Codes of keys [n_rows][n_heads][128] (bf16; the last dim contiguous, the
-    others with any stride) under w_h [n_heads][128][128] (fp32):
-    int32 [n_rows][n_heads][4]."""
+    others with any stride) under w_h [n_heads][128][r] (fp32, r = 32, 64,
+    128 or 256): int32 [n_rows][n_heads][r / 32]."""
     if keys.dtype != torch.bfloat16 or keys.dim() != 3 or keys.shape[2] != HEAD_DIM:
         raise ValueError("keys must be bf16 [n_rows][n_heads][128]")
     if keys.stride(2) != 1:
         raise ValueError("keys' last dimension must be contiguous")
     n_rows, n_heads = keys.shape[0], keys.shape[1]
-    _need(w_h, "w_h", torch.float32, n_heads * HEAD_DIM * N_BITS)
+    if w_h.dim() != 3 or w_h.shape[0] != n_heads or w_h.shape[1] != HEAD_DIM:
+        raise ValueError("w_h must be fp32 [n_heads][128][n_bits]")
+    n_bits = int(w_h.shape[2])
+    words = max(n_bits // 32, 1)
+    _need(w_h, "w_h", torch.float32, n_heads * HEAD_DIM * n_bits)
     if codes_out is None:
-        codes_out = torch.empty((n_rows, n_heads, CODE_WORDS), dtype=torch.int32,
-                                device=keys.device)
-    _need(codes_out, "codes_out", torch.int32, n_rows * n_heads * CODE_WORDS)
-    st = lib().hata_encode_keys(keys.data_ptr(), n_rows, n_heads, keys.stride(0),
-                                keys.stride(1), w_h.data_ptr(), codes_out.data_ptr(),
-                                _stream(stream))
-    _check("hata_encode_keys", st)
+        codes_out = torch.empty((n_rows, n_heads, words), dtype=torch.int32, device=keys.device)
+    _need(codes_out, "codes_out", torch.int32, n_rows * n_heads * words)
+    if n_bits == N_BITS:
+        st = lib().hata_encode_keys(keys.data_ptr(), n_rows, n_heads, keys.stride(0),
+                                    keys.stride(1), w_h.data_ptr(), codes_out.data_ptr(),
+                                    _stream(stream))
+        _check("hata_encode_keys", st)
+    else:
+        st = lib().hata_encode_keys_nbits(keys.data_ptr(), n_rows, n_heads, keys.stride(0),
+                                          keys.stride(1), w_h.data_ptr(), n_bits,
+                                          codes_out.data_ptr(), _stream(stream))
+        _check("hata_encode_keys_nbits", st)
     return codes_out
 
 
@@ -248,7 +263,7 @@ def hata_append(cache: HataCache, k_new, v_new, n_new: torch.Tensor, t_max: int,
         _need(k_new, "k_new", torch.bfloat16, B * int(t_max) * Hkv * HEAD_DIM)
         _need(v_new, "v_new", torch.bfloat16, B * int(t_max) * Hkv * HEAD_DIM)
     _need(n_new, "n_new", torch.int32, B)
-    _need(w_h, "w_h", torch.float32, Hkv * HEAD_DIM * N_BITS)
+    _need(w_h, "w_h", torch.float32, Hkv * HEAD_DIM * cache.n_bits)
     c = cache.c_struct()
     st = lib().hata_append(ctypes.byref(c), _ptr(k_new), _ptr(v_new), n_new.data_ptr(),
                            int(t_max), w_h.data_ptr(), _stream(stream))
@@ -281,7 +296,7 @@ def hata_decode_attn(cache: HataCache, q: torch.Tensor, w_h: torch.Tensor, topk:
     B, Hq, Hkv = cache.batch, cache.n_q_heads, cache.n_kv_heads
     _need(q, "q", torch.bfloat16, B * Hq * HEAD_DIM)
     _need(out, "out", torch.bfloat16, B * Hq * HEAD_DIM)
-    _need(w_h, "w_h", torch.float32, Hkv * HEAD_DIM * N_BITS)
+    _need(w_h, "w_h", torch.float32, Hkv * HEAD_DIM * cache.n_bits)
     _need(topk, "topk", torch.int32, B)
     _need(workspace, "workspace", torch.uint8)
     if sel_idx_out is not None:
@@ -308,7 +323,7 @@ def hata_decode_step(cache: HataCache, k_new: torch.Tensor, v_new: torch.Tensor,
     _need(v_new, "v_new", torch.bfloat16, B * Hkv * HEAD_DIM)
     _need(q, "q", torch.bfloat16, B * Hq * HEAD_DIM)
     _need(out, "out", torch.bfloat16, B * Hq * HEAD_DIM)
-    _need(w_h, "w_h", torch.float32, Hkv * HEAD_DIM * N_BITS)
+    _need(w_h, "w_h", torch.float32, Hkv * HEAD_DIM * cache.n_bits)
     _need(topk, "topk", torch.int32, B)
     _need(workspace, "workspace", torch.uint8)
     if sel_idx_out is not None:

@@ -7,6 +7,7 @@
 #include "../../include/hata.h"
 #include "hata_internal.h"
 #include "recall_plan.h"
+#include "bits_plan.h"
 
 using namespace hata;
 
@@ -14,9 +15,13 @@ namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool supported_bits(int n_bits) {
+    return n_bits == 32 || n_bits == 64 || n_bits == 128 || n_bits == 256;
+}
+
 hata_status check_cache(const hata_cache *c) {
     if (!c) return HATA_ERR_INVALID_ARG;
-    if (c->head_dim != kHeadDim || c->n_bits != kBits) return HATA_ERR_UNSUPPORTED;
+    if (c->head_dim != kHeadDim || !supported_bits(c->n_bits)) return HATA_ERR_UNSUPPORTED;
     if (c->batch <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0) return HATA_ERR_INVALID_ARG;
     if (c->n_q_heads % c->n_kv_heads) return HATA_ERR_UNSUPPORTED;
     const int G = c->n_q_heads / c->n_kv_heads;
@@ -62,6 +67,24 @@ hata_status hata_encode_keys(const uint16_t *keys, int64_t n_rows, int32_t n_hea
     return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
 }
 
+hata_status hata_encode_keys_nbits(const uint16_t *keys, int64_t n_rows, int32_t n_heads,
+                                   int64_t row_stride, int64_t head_stride, const float *w_h,
+                                   int32_t n_bits, uint32_t *codes_out, void *stream) {
+    if (!supported_bits(n_bits)) return HATA_ERR_UNSUPPORTED;
+    if (n_bits == kBits)
+        return hata_encode_keys(keys, n_rows, n_heads, row_stride, head_stride, w_h, codes_out,
+                                stream);
+    if (n_rows < 0 || n_heads <= 0 || n_heads > 65535) return HATA_ERR_INVALID_ARG;
+    if (n_rows == 0) return HATA_OK;
+    if (!keys || !w_h || !codes_out) return HATA_ERR_INVALID_ARG;
+    if (row_stride < 0 || head_stride < 0) return HATA_ERR_INVALID_ARG;
+    if (n_heads > 1 && head_stride < kHeadDim && row_stride < kHeadDim) return HATA_ERR_INVALID_ARG;
+    if (!aligned16(keys) || row_stride % 8 || head_stride % 8) return HATA_ERR_INVALID_ARG;
+    hipError_t e = launch_encode_bits(keys, n_rows, n_heads, row_stride, head_stride, w_h, n_bits,
+                                      codes_out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
+}
+
 hata_status hata_append(const hata_cache *c, const uint16_t *k_new, const uint16_t *v_new,
                         const int32_t *n_new, int32_t t_max, const float *w_h, void *stream) {
     hata_status st = check_cache(c);
@@ -69,6 +92,13 @@ hata_status hata_append(const hata_cache *c, const uint16_t *k_new, const uint16
     if (t_max < 0 || !n_new || !w_h) return HATA_ERR_INVALID_ARG;
     if ((k_new == nullptr) != (v_new == nullptr)) return HATA_ERR_INVALID_ARG;
     if (t_max == 0) return HATA_OK;
+    if (c->n_bits != kBits) {
+        if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return HATA_ERR_INVALID_ARG;
+        hipError_t e = launch_append_bits(c->k, c->v, c->codes, c->seq_len, c->ctrl, c->batch,
+                                          c->n_kv_heads, c->max_ctx, k_new, v_new, n_new, t_max,
+                                          w_h, c->n_bits, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
+    }
     const bool mfma = t_max >= kMfmaMinRows && (k_new == nullptr || (aligned16(k_new) && aligned16(v_new)));
     hipError_t e = mfma ? launch_append_mfma(c->k, c->v, c->codes, c->seq_len, c->ctrl, c->batch,
                                              c->n_kv_heads, c->max_ctx, k_new, v_new, n_new, t_max,
@@ -81,7 +111,14 @@ hata_status hata_append(const hata_cache *c, const uint16_t *k_new, const uint16
 
 size_t hata_decode_workspace_bytes(const hata_cache *c, int32_t k_max) {
     if (!c || k_max < 0) return 0;
-    if (c->head_dim != kHeadDim || c->n_bits != kBits) return 0;
+    if (c->head_dim != kHeadDim || !supported_bits(c->n_bits)) return 0;
+    if (c->n_bits != kBits) {
+        BitsPlan bp;
+        if (!make_bits_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, c->n_bits, k_max,
+                            &bp))
+            return 0;
+        return bp.total;
+    }
     DecodePlan p;
     if (!make_decode_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, &p)) return 0;
     return p.total;
@@ -96,6 +133,19 @@ static hata_status decode_common(const hata_cache *c, const uint16_t *k_new,
     if (st != HATA_OK) return st;
     if (!q || !w_h || !topk || !out || k_max < 0) return HATA_ERR_INVALID_ARG;
     if (!aligned16(q)) return HATA_ERR_INVALID_ARG;
+    if (c->n_bits != kBits) {
+        if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return HATA_ERR_INVALID_ARG;
+        BitsPlan bp;
+        if (!make_bits_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, c->n_bits, k_max,
+                            &bp))
+            return HATA_ERR_UNSUPPORTED;
+        if (!workspace || ws_bytes < bp.total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+            return HATA_ERR_WORKSPACE;
+        hipError_t e = launch_decode_bits(bp, c->k, c->v, c->codes, c->seq_len, c->ctrl, k_new,
+                                          v_new, q, w_h, topk, out, workspace, sel_idx_out,
+                                          scores_out, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
+    }
     DecodePlan p;
     if (!make_decode_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, &p))
         return HATA_ERR_UNSUPPORTED;
@@ -126,7 +176,7 @@ hata_status hata_decode_step(const hata_cache *c, const uint16_t *k_new, const u
 
 size_t hata_recall_workspace_bytes(const hata_cache *c) {
     if (!c) return 0;
-    if (c->head_dim != kHeadDim || c->n_bits != kBits) return 0;
+    if (c->head_dim != kHeadDim || !supported_bits(c->n_bits)) return 0;
     RecallPlan p;
     if (!make_recall_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, &p)) return 0;
     return p.total;
@@ -147,7 +197,7 @@ hata_status hata_exact_topk_recall(const hata_cache *c, const uint16_t *q, const
         return HATA_ERR_UNSUPPORTED;
     if (!workspace || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return HATA_ERR_WORKSPACE;
-    hipError_t e = launch_recall(p, c->k, c->seq_len, q, topk, k_max, sel_idx, scores,
+    hipError_t e = launch_recall(p, c->n_bits, c->k, c->seq_len, q, topk, k_max, sel_idx, scores,
                                  overlap_out, tie_out, exact_idx_out, workspace,
                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;

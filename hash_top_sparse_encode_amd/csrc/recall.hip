@@ -58,7 +58,7 @@ struct RecallArgs {
     int32_t *band_idx; // [B][Hq][max_ctx] keys ranked exactly
     double *band_z;    // [B][Hq][max_ctx] their exact logits
     uint8_t *member;   // [B][Hq][max_ctx] exact top-k flag of those keys
-    int B, Hq, Hkv, G, k_max, n_kblk;
+    int B, Hq, Hkv, G, k_max, n_kblk, nbits;
     int64_t max_ctx, zstride;
 };
 
@@ -215,7 +215,7 @@ __device__ __forceinline__ float from_okey(uint32_t k) {
 }
 
 struct RecSmem {
-    uint32_t hist[2048];
+    uint32_t hist[4096];  // radix passes use 2048 bins, the score histogram up to 8 * 256 + 1
     float qs[kHeadDim];
     int wt[16];
     double wd[16];
@@ -226,8 +226,8 @@ struct RecSmem {
 // score, keys below T, keys at T.
 __device__ void tie_bucket(const RecallArgs &a, RecSmem &sm, int unit, int64_t len, int ke) {
     const int t = threadIdx.x;
-    const int nbins = kBits * a.G + 1;
-    for (int j = t; j < 2048; j += kRecThreads) sm.hist[j] = 0;
+    const int nbins = a.nbits * a.G + 1;
+    for (int j = t; j < 4096; j += kRecThreads) sm.hist[j] = 0;
     __syncthreads();
     const uint16_t *sc = a.scores + (int64_t)unit * a.max_ctx;
     for (int64_t i = t; i < len; i += kRecThreads) {
@@ -235,7 +235,8 @@ __device__ void tie_bucket(const RecallArgs &a, RecSmem &sm, int unit, int64_t l
         atomicAdd(&sm.hist[v < nbins ? v : nbins - 1], 1u);
     }
     __syncthreads();
-    const int c = (int)(sm.hist[2 * t] + sm.hist[2 * t + 1]);
+    const int c = (int)(sm.hist[4 * t] + sm.hist[4 * t + 1] + sm.hist[4 * t + 2] +
+                        sm.hist[4 * t + 3]);
     int tot;
     const int incl = scan_incl_1024(c, sm.wt, &tot);
     const int excl = incl - c;
@@ -247,8 +248,8 @@ __device__ void tie_bucket(const RecallArgs &a, RecSmem &sm, int unit, int64_t l
         }
     } else if (excl < ke && ke <= incl) {
         int cum = excl;
-        for (int j = 0; j < 2; ++j) {
-            const int bin = 2 * t + j, hv = (int)sm.hist[bin];
+        for (int j = 0; j < 4; ++j) {
+            const int bin = 4 * t + j, hv = (int)sm.hist[bin];
             if (cum + hv >= ke) {
                 out[0] = bin;
                 out[1] = cum;
@@ -459,7 +460,7 @@ bool make_recall_plan(int B, int Hq, int Hkv, int64_t max_ctx, RecallPlan *p) {
     return true;
 }
 
-hipError_t launch_recall(const RecallPlan &p, const uint16_t *k_cache, const int32_t *seq_len,
+hipError_t launch_recall(const RecallPlan &p, int n_bits, const uint16_t *k_cache, const int32_t *seq_len,
                          const uint16_t *q, const int32_t *topk, int k_max,
                          const int32_t *sel_idx, const uint16_t *scores, int32_t *overlap,
                          int32_t *tie, int32_t *exact_idx, void *ws, hipStream_t s) {
@@ -484,6 +485,7 @@ hipError_t launch_recall(const RecallPlan &p, const uint16_t *k_cache, const int
     a.Hkv = p.Hkv;
     a.G = p.G;
     a.k_max = k_max;
+    a.nbits = n_bits;
     a.n_kblk = p.n_kblk;
     a.max_ctx = p.max_ctx;
     a.zstride = p.zstride;

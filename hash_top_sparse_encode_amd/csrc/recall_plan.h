@@ -19,7 +19,7 @@ struct RecallPlan {
 
 bool make_recall_plan(int B, int Hq, int Hkv, int64_t max_ctx, RecallPlan *p);
 
-hipError_t launch_recall(const RecallPlan &p, const uint16_t *k_cache, const int32_t *seq_len,
+hipError_t launch_recall(const RecallPlan &p, int n_bits, const uint16_t *k_cache, const int32_t *seq_len,
                          const uint16_t *q, const int32_t *topk, int k_max,
                          const int32_t *sel_idx, const uint16_t *scores, int32_t *overlap,
                          int32_t *tie, int32_t *exact_idx, void *ws, hipStream_t s);

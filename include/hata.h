@@ -25,9 +25,12 @@
  *     can see (a cache overflow, an out-of-range length) set bits in the
  *     cache's status word (HATA_DEV_*) and the affected batch entry is left
  *     unchanged or clamped as documented below.
- *   - Supported shapes: head_dim = 128, n_bits = 128, query heads a
- *     multiple G of KV heads with G in {1, 2, 4, 8}.  Other shapes return
- *     HATA_ERR_UNSUPPORTED.
+ *   - Supported shapes: head_dim = 128, n_bits in {32, 64, 128, 256}, query
+ *     heads a multiple G of KV heads with G in {1, 2, 4, 8}.  Other shapes
+ *     return HATA_ERR_UNSUPPORTED.  n_bits = 128 (the pages' choice) runs
+ *     the fused single-launch decode; the other code lengths (the pages'
+ *     hash-length ablation, "Free parameters") run a multi-launch path with
+ *     the same results by definition.
  *   - bf16 values are passed as their 16-bit patterns (uint16_t).
  *   - Reentrant: the library keeps no mutable global state.  Calls that use
  *     the same cache or workspace must be ordered by the caller (same
@@ -86,7 +89,7 @@ typedef enum {
  *           review ("offloaded" speed-ups in "Core claim"), where the codes,
  *           the scan and the selection stay in device memory and only the
  *           selected rows (and the appended ones) cross the host link.
- *   codes : u32   [batch][n_kv_heads][max_ctx][4]
+ *   codes : u32   [batch][n_kv_heads][max_ctx][n_bits / 32]
  *   seq_len: int32 [batch], the number of valid positions of each sequence;
  *           positions [0, seq_len[b]) hold keys, values and codes.
  *   ctrl  : int32 [HATA_CTRL_WORDS(batch, n_kv_heads)], zero-filled by the
@@ -106,7 +109,7 @@ typedef struct {
     int32_t n_q_heads;
     int32_t n_kv_heads;
     int32_t head_dim; /* must be 128 */
-    int32_t n_bits;   /* must be 128 */
+    int32_t n_bits;   /* 32, 64, 128 or 256 */
     int64_t max_ctx;
 } hata_cache;
 
@@ -133,6 +136,20 @@ hata_status hata_encode_keys(const uint16_t *keys, int64_t n_rows, int32_t n_hea
                              uint32_t *codes_out, void *stream);
 
 /*
+ * hata_encode_keys for any supported code length r = n_bits (32, 64, 128 or
+ * 256; the hash-length ablation of the review's "Free parameters"):
+ *   w_h       device fp32 [n_heads][128 (d)][r (bit)].
+ *   codes_out device u32 [n_rows][n_heads][r / 32].
+ * Same bit convention and exactness.  For r != 128, keys must be 16-byte
+ * aligned and both strides multiples of 8 elements (else
+ * HATA_ERR_INVALID_ARG); r = 128 is hata_encode_keys itself.
+ * Errors as hata_encode_keys, plus HATA_ERR_UNSUPPORTED for other n_bits.
+ */
+hata_status hata_encode_keys_nbits(const uint16_t *keys, int64_t n_rows, int32_t n_heads,
+                                   int64_t row_stride, int64_t head_stride, const float *w_h,
+                                   int32_t n_bits, uint32_t *codes_out, void *stream);
+
+/*
  * Append new tokens to the cache (Algorithm 1's cache fill at prefill; one
  * token per sequence at decode): for each sequence b and t < n_new[b], key
  * row t of b goes to position seq_len[b] + t, its code is computed with the
@@ -143,7 +160,7 @@ hata_status hata_encode_keys(const uint16_t *keys, int64_t n_rows, int32_t n_hea
  *             computed (encode in place).
  *   n_new     device int32 [batch], each in [0, t_max].
  *   t_max     host bound on n_new (sizes the launch); t_max = 0 is a no-op.
- *   w_h       device fp32 [n_kv_heads][128][128].
+ *   w_h       device fp32 [n_kv_heads][128][n_bits].
  * Device-detected errors: an entry with seq_len[b] + n_new[b] > max_ctx is
  * not appended and sets HATA_DEV_APPEND_OVERFLOW; n_new[b] outside
  * [0, t_max] sets HATA_DEV_BAD_NEW and the entry is skipped.
@@ -168,13 +185,13 @@ size_t hata_decode_workspace_bytes(const hata_cache *c, int32_t k_max);
  *      (KV head of query head h = h / G);
  *   2. score every cached key i < seq_len[b] of KV head g by the sum over
  *      the group's G query heads of popcount(q_code XOR k_code[i])
- *      (range 0 .. 128 G);
+ *      (range 0 .. n_bits G);
  *   3. select S = the k_eff = min(topk[b], k_max, seq_len[b]) keys of lowest
  *      (score, index) -- ties at the cut go to the lowest indices;
  *   4. for each query head: softmax over i in S of (q . k_i) / sqrt(128),
  *      output sum_i p_i v_i (fp32 accumulation), stored as bf16.
  *   q          device bf16 [batch][n_q_heads][128].
- *   w_h        device fp32 [n_kv_heads][128][128].
+ *   w_h        device fp32 [n_kv_heads][128][n_bits].
  *   topk       device int32 [batch]; values < 0 count as 0, values above
  *              k_max are clamped (HATA_DEV_TOPK_CLAMPED).
  *   k_max      host upper bound of the budget, >= 0.

@@ -252,6 +252,14 @@ def gen_w(spec: Spec) -> np.ndarray:
         spec.Hkv, HEAD_DIM, N_BITS)
 
 
+def gen_w_bits(spec: Spec, n_bits: int) -> np.ndarray:
+    """Hash projections for a code length of n_bits, fp32 [Hkv][128 (d)][n_bits],
+    N(0, 1/128), from the same stream as gen_w (identical at 128 bits)."""
+    n = spec.Hkv * HEAD_DIM * n_bits
+    return normal_f32(spec.seed, T_W, 0, n, 1.0 / math.sqrt(128.0)).reshape(
+        spec.Hkv, HEAD_DIM, n_bits)
+
+
 def planted_positions(spec: Spec, b: int, kv: int) -> np.ndarray:
     """Sorted planted positions of unit (b, kv): the `planted[b]` positions in
     [0, N_b - 1) with the smallest (random u64, position) pairs."""

@@ -60,7 +60,8 @@ def decode(c, q=FAKE, w=FAKE, topk=FAKE, k_max=16, out=FAKE, ws=FAKE, ws_bytes=1
 def test_decode_validation():
     E = hata
     assert decode(cache(head_dim=64)) == E.HATA_ERR_UNSUPPORTED
-    assert decode(cache(n_bits=64)) == E.HATA_ERR_UNSUPPORTED
+    assert decode(cache(n_bits=96)) == E.HATA_ERR_UNSUPPORTED
+    assert decode(cache(n_bits=512)) == E.HATA_ERR_UNSUPPORTED
     assert decode(cache(n_q_heads=6)) == E.HATA_ERR_UNSUPPORTED        # 6 % 4? G = 3
     assert decode(cache(n_q_heads=32)) == E.HATA_ERR_UNSUPPORTED       # G = 16
     assert decode(cache(n_q_heads=7)) == E.HATA_ERR_UNSUPPORTED        # not a multiple
@@ -103,6 +104,12 @@ def test_append_validation():
 
 def test_encode_keys_validation():
     L = hata.lib()
+    enc = L.hata_encode_keys_nbits
+    assert enc(FAKE, 5, 1, 128, 128, FAKE, 96, FAKE, None) == hata.HATA_ERR_UNSUPPORTED
+    assert enc(FAKE + 2, 5, 1, 128, 128, FAKE, 64, FAKE, None) == hata.HATA_ERR_INVALID_ARG
+    assert enc(FAKE, 5, 1, 132, 128, FAKE, 64, FAKE, None) == hata.HATA_ERR_INVALID_ARG
+    assert enc(FAKE, 5, 1, 128, 128, None, 256, FAKE, None) == hata.HATA_ERR_INVALID_ARG
+    assert enc(None, 0, 1, 128, 128, None, 32, None, None) == hata.HATA_OK
     assert L.hata_encode_keys(FAKE, -1, 1, 128, 128, FAKE, FAKE, None) == hata.HATA_ERR_INVALID_ARG
     assert L.hata_encode_keys(FAKE, 5, 0, 128, 128, FAKE, FAKE, None) == hata.HATA_ERR_INVALID_ARG
     assert L.hata_encode_keys(None, 5, 1, 128, 128, FAKE, FAKE, None) == hata.HATA_ERR_INVALID_ARG
@@ -126,7 +133,22 @@ def test_workspace_plan(B, Hq, Hkv, N):
     assert n < units * (N + 8) * (2 + 4 * (128 * G + 1) / 2048 + 0.4) + (1 << 22)
     assert n % 256 == 0
     assert hata.lib().hata_decode_workspace_bytes(ctypes.byref(cache(head_dim=64)), 1) == 0
+    assert hata.lib().hata_decode_workspace_bytes(ctypes.byref(cache(n_bits=48)), 1) == 0
     assert hata.lib().hata_decode_workspace_bytes(None, 1) == 0
+
+
+@pytest.mark.parametrize("n_bits", [32, 64, 256])
+def test_workspace_plan_other_code_lengths(n_bits):
+    B, Hq, Hkv, N, k_max = 4, 32, 8, 131072, 2048
+    c = cache(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, max_ctx=N, n_bits=n_bits)
+    n = hata.lib().hata_decode_workspace_bytes(ctypes.byref(c), k_max)
+    units, G = B * Hkv, Hq // Hkv
+    # u16 scores, per-span histograms (8192-key spans, G r + 1 bins), the
+    # selection, per-chunk softmax states (256 keys, G heads x 130 floats)
+    span_hist = units * (N // 8192) * ((G * n_bits + 1 + 63) // 64 * 64) * 4
+    lo = units * N * 2 + span_hist + units * k_max * 4 + units * (k_max // 256) * G * 130 * 4
+    assert lo <= n <= lo + (1 << 20)
+    assert n % 256 == 0
 
 
 def recall(c, q=FAKE, topk=FAKE, k_max=16, sel=FAKE, sc=FAKE, ov=FAKE, tie=FAKE, ex=None,

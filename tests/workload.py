@@ -29,15 +29,17 @@ class GpuWorkload:
     """Device state of one synthetic decode workload."""
 
     def __init__(self, spec: synth.Spec, device, extra_ctx: int = 0, units=None,
-                 encode_prefill: bool = True, offload: bool = False):
+                 encode_prefill: bool = True, offload: bool = False, n_bits: int = 128):
         self.spec = spec
         self.device = device
         B, Hq, Hkv = spec.B, spec.Hq, spec.Hkv
         self.max_ctx = max(spec.max_len + extra_ctx, 1)
         self.q_host = synth.gen_q(spec)
-        self.w_host = synth.gen_w(spec)
+        self.n_bits = n_bits
+        self.w_host = synth.gen_w(spec) if n_bits == 128 else synth.gen_w_bits(spec, n_bits)
         self.new_host = synth.gen_new_token(spec)
-        self.cache = hata.HataCache(B, Hq, Hkv, self.max_ctx, device=device, offload=offload)
+        self.cache = hata.HataCache(B, Hq, Hkv, self.max_ctx, device=device, offload=offload,
+                                    n_bits=n_bits)
         self.cache.k.zero_()
         self.cache.v.zero_()
         for b in range(B):
