@@ -383,6 +383,11 @@ __global__ void __launch_bounds__(kBThreads) k_select_bits(BitsDecArgs a) {
     const int t = threadIdx.x;
     const int64_t len = bits_len(a, b);
     const int ke = bits_keff(a, b, len);
+    if (t == 0) {
+        const int64_t raw = a.seq_len[b];
+        if (raw < 0 || raw > a.max_ctx) atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_BAD_LENGTH);
+        if (a.topk[b] > a.k_max) atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_TOPK_CLAMPED);
+    }
     int32_t *sel = a.sel + (int64_t)unit * a.k_max;
     for (int i = ke + t; i < a.k_max; i += kBThreads) sel[i] = -1;
     if (ke == 0) {
@@ -523,6 +528,7 @@ __global__ void __launch_bounds__(kBThreads) k_attend_bits(BitsDecArgs a) {
     const int ke = a.info[unit * 4 + 1];
     const int c0 = chunk * kBChunk;
     if (c0 >= ke) return;
+    const int64_t len = bits_len(a, b);
     const float qscale = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
     float qf[G][8];
 #pragma unroll
@@ -546,10 +552,10 @@ __global__ void __launch_bounds__(kBThreads) k_attend_bits(BitsDecArgs a) {
     const uint16_t *vb = a.v + (int64_t)unit * a.max_ctx * kHeadDim + 8 * sub;
     for (int it = 0; it < 16; ++it) {
         const int p = c0 + wv * 64 + it * 4 + kk;
-        const bool valid = p < ke;  // uniform within the row
+        const int64_t key = p < ke ? sel[p] : -1;
+        const bool valid = key >= 0 && key < len;  // uniform within the row
         uvec4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
         if (valid) {
-            const int64_t key = sel[p];
             kr = *reinterpret_cast<const uvec4 *>(kb + key * kHeadDim);
             vr = *reinterpret_cast<const uvec4 *>(vb + key * kHeadDim);
         }
