@@ -421,6 +421,54 @@ def main():
     }
     del off, off_ws
 
+    # Other code lengths (the hash-length ablation): the same workload with
+    # r-bit codes over the same K/V rows, one cache (the codes of r = 32 and
+    # 64 bits, 17 and 34 MB, fit in the last-level cache, so they are
+    # flattered), prefill encode in place, then decode steps on the
+    # multi-launch path.
+    code_lengths = []
+    for r in (32, 64, 256):
+        w_r = torch.from_numpy(synth.gen_w_bits(spec, r)).to(dev)
+        c_r = hata.HataCache(B, Hq, Hkv, base.max_ctx, device=dev, k=base.cache.k,
+                             v=base.cache.v, n_bits=r)
+        enc_t = []
+        for rep_i in range(2):
+            c_r.seq_len.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            hata.hata_append(c_r, None, None, base.n_pre, N - 1, w_r)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            enc_t.append(e0.elapsed_time(e1))
+        ws_r = hata.alloc_workspace(c_r, base.k_max)
+        out_r = torch.empty_like(base.out)
+
+        def step_r(s):
+            hata.hata_decode_step(c_r, k_new, v_new, queries[s % QUERIES], w_r, base.topk,
+                                  base.k_max, out_r, ws_r)
+
+        for s in range(5):
+            step_r(s)
+        n_r = max(1, min(args.steps, 30))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(n_r):
+            step_r(5 + s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if c_r.status():
+            print(f"[bench] r={r}: device status flags set: {c_r.status()}", file=sys.stderr)
+            sys.exit(1)
+        us = e0.elapsed_time(e1) * 1e3 / n_r
+        ctx_r = N + 5 + (n_r - 1) / 2.0  # mean context of the timed steps
+        alg_r = (r // 8) * B * Hkv * ctx_r + 512 * B * Hkv * K + 4 * Hkv * 128 * r + \
+            4 * B * Hq * 128 + B * Hkv * (512 + r // 8)
+        code_lengths.append({"n_bits": r, "us_per_step": us, "steps_per_s": 1e6 / us,
+                             "alg_bytes": alg_r, "alg_GBps": alg_r / us / 1e3,
+                             "prefill_encode_ms": enc_t[-1]})
+        del c_r, ws_r
+    base.cache.seq_len.copy_(base.n_pre)
+
     n_ctx = ctx0 + (args.steps // L) / 2.0  # mean context over the timed steps
     step_bytes = algorithmic_bytes(B, Hq, Hkv, n_ctx, K)
     achieved = step_bytes / (dec_ms * 1e-3) / 1e9
@@ -470,6 +518,7 @@ def main():
         "prefill_encode": prefill,
         "recall": recall,
         "offload": offload,
+        "code_lengths": code_lengths,
     }
     if args.copy_probe:
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(7)
