@@ -224,7 +224,9 @@ def main():
     spec = synth.config(3)
     B, Hq, Hkv, N, K = spec.B, spec.Hq, spec.Hkv, spec.lengths[0], spec.topk[0]
     L = max(1, args.layers)
-    per_layer = math.ceil((args.warmup + 2 * args.steps) / L) + 2
+    # room for every append: the layer steps, and up to 58 steps each on the
+    # offloaded and other-code-length caches (which start from the prefill)
+    per_layer = max(math.ceil((args.warmup + 2 * args.steps) / L) + 2, 64)
     print(f"[bench] generating {spec.name}", file=sys.stderr, flush=True)
     base = GpuWorkload(spec, dev, extra_ctx=per_layer)
     torch.cuda.synchronize()
