@@ -165,13 +165,15 @@ __global__ void __launch_bounds__(kBThreads) k_encode_bits(BitsEncArgs a) {
             if (q4 == 0) xn[rr] = sqrt(s);
         }
         __syncthreads();
+        const int rows_here = (int)(n_rows - r0 < kBTile ? n_rows - r0 : kBTile);
         for (int rr = slot; rr < kBTile; rr += P) {
             const int64_t row = r0 + rr;
+            bool bit = false;
+            if (rr < rows_here) {
             float y = 0.f;
 #pragma unroll
             for (int d = 0; d < kHeadDim; ++d) y = fmaf(xs[rr][d], wv_[d], y);
             const double nn = xn[rr] * nw;
-            bool bit;
             if (nn < 0x1p120 && fabs((double)y) > 0x1p-16 * nn + 0x1p-100) {
                 bit = y > 0.f;
             } else {
@@ -182,6 +184,7 @@ __global__ void __launch_bounds__(kBThreads) k_encode_bits(BitsEncArgs a) {
                 for (int d = 0; d < kHeadDim; ++d)
                     e = fma((double)xs[rr][d], (double)wc[(int64_t)d * R], e);
                 bit = e > 0.0;
+            }
             }
             const uint64_t m = __ballot(bit);
             if (row < n_rows) {
@@ -371,8 +374,20 @@ __global__ void __launch_bounds__(kBThreads) k_scan_bits(BitsDecArgs a) {
         }
     }
     __syncthreads();
+    // The span's cumulative histogram (keys scoring <= bin): each thread
+    // sums a run of consecutive bins, one block scan places the runs.
+    __shared__ int tmp[4];
+    const int per = (a.NB + kBThreads - 1) / kBThreads;
+    const int lo = t * per, hi = lo + per < a.NB ? lo + per : a.NB;
+    int c = 0;
+    for (int bin = lo; bin < hi; ++bin) c += hist[bin];
+    int tot;
+    int cum = block_excl_scan_256(c, tmp, &tot);
     int32_t *hrow = a.span_hist + ((int64_t)unit * a.n_span + span) * a.NBpad;
-    for (int i = t; i < a.NB; i += kBThreads) hrow[i] = hist[i];
+    for (int bin = lo; bin < hi; ++bin) {
+        cum += hist[bin];
+        hrow[bin] = cum;
+    }
 }
 
 __global__ void __launch_bounds__(kBThreads) k_select_bits(BitsDecArgs a) {
@@ -399,29 +414,18 @@ __global__ void __launch_bounds__(kBThreads) k_select_bits(BitsDecArgs a) {
     }
     const int n_used = (int)((len + kBSpan - 1) / kBSpan);
     const int32_t *hb = a.span_hist + (int64_t)unit * a.n_span * a.NBpad;
+    // The unit's cumulative histogram is the sum of its spans' ones; T is
+    // the first bin where it reaches k_eff (it is non-decreasing).
     for (int bin = t; bin < a.NB; bin += kBThreads) {
         int s = 0;
         for (int sp = 0; sp < n_used; ++sp) s += hb[(int64_t)sp * a.NBpad + bin];
         uh[bin] = s;
     }
     __syncthreads();
-    // T: the first bin whose cumulative count reaches k_eff.  Each thread
-    // sums a run of consecutive bins.
-    const int per = (a.NB + kBThreads - 1) / kBThreads;
-    const int lo = t * per, hi = lo + per < a.NB ? lo + per : a.NB;
-    int c = 0;
-    for (int bin = lo; bin < hi; ++bin) c += uh[bin];
-    int tot;
-    const int excl = block_excl_scan_256(c, tmp, &tot);
-    if (excl < ke && ke <= excl + c) {
-        int cum = excl;
-        for (int bin = lo; bin < hi; ++bin) {
-            if (cum + uh[bin] >= ke) {
-                s_T = bin;
-                s_below = cum;
-                break;
-            }
-            cum += uh[bin];
+    for (int bin = t; bin < a.NB; bin += kBThreads) {
+        if (uh[bin] >= ke && (bin == 0 || uh[bin - 1] < ke)) {
+            s_T = bin;
+            s_below = bin == 0 ? 0 : uh[bin - 1];
         }
     }
     __syncthreads();
@@ -433,8 +437,8 @@ __global__ void __launch_bounds__(kBThreads) k_select_bits(BitsDecArgs a) {
         int below = 0, ties = 0;
         if (sp < n_used) {
             const int32_t *hr = hb + (int64_t)sp * a.NBpad;
-            for (int bin = 0; bin < T; ++bin) below += hr[bin];
-            ties = hr[T];
+            below = T > 0 ? hr[T - 1] : 0;
+            ties = hr[T] - below;
         }
         int tt;
         const int ties_before = carry_ties + block_excl_scan_256(ties, tmp, &tt);
@@ -550,14 +554,35 @@ __global__ void __launch_bounds__(kBThreads) k_attend_bits(BitsDecArgs a) {
     const int32_t *sel = a.sel + (int64_t)unit * a.k_max;
     const uint16_t *kb = a.k + (int64_t)unit * a.max_ctx * kHeadDim + 8 * sub;
     const uint16_t *vb = a.v + (int64_t)unit * a.max_ctx * kHeadDim + 8 * sub;
+    // This lane's 16 keys first (one round trip), then the K/V pieces four
+    // iterations ahead of their use.
+    int64_t keyv[16];
+#pragma unroll
     for (int it = 0; it < 16; ++it) {
         const int p = c0 + wv * 64 + it * 4 + kk;
         const int64_t key = p < ke ? sel[p] : -1;
-        const bool valid = key >= 0 && key < len;  // uniform within the row
-        uvec4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
-        if (valid) {
-            kr = *reinterpret_cast<const uvec4 *>(kb + key * kHeadDim);
-            vr = *reinterpret_cast<const uvec4 *>(vb + key * kHeadDim);
+        keyv[it] = (key >= 0 && key < len) ? key : -1;  // uniform within the row
+    }
+    uvec4 kq[4], vq[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        kq[it] = vq[it] = uvec4{0u, 0u, 0u, 0u};
+        if (keyv[it] >= 0) {
+            kq[it] = *reinterpret_cast<const uvec4 *>(kb + keyv[it] * kHeadDim);
+            vq[it] = *reinterpret_cast<const uvec4 *>(vb + keyv[it] * kHeadDim);
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int sl = it & 3;
+        const bool valid = keyv[it] >= 0;
+        const uvec4 kr = kq[sl], vr = vq[sl];
+        if (it + 4 < 16) {
+            kq[sl] = vq[sl] = uvec4{0u, 0u, 0u, 0u};
+            if (keyv[it + 4] >= 0) {
+                kq[sl] = *reinterpret_cast<const uvec4 *>(kb + keyv[it + 4] * kHeadDim);
+                vq[sl] = *reinterpret_cast<const uvec4 *>(vb + keyv[it + 4] * kHeadDim);
+            }
         }
         float kf[8], vf[8];
         unpack8b(kr, kf);
