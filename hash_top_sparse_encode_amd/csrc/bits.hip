@@ -51,10 +51,11 @@ __device__ __forceinline__ void unpack8b(const uvec4 &r, float (&f)[8]) {
 // ---------------------------------------------------------------- encoder
 
 struct BitsEncArgs {
-    int mode;  // 0: flat rows, 1: cache append, 2: query heads
+    int mode;  // 0: flat rows, 1: cache append, 2: query heads, 3: 1 and 2 in one launch
     const uint16_t *x;
     int64_t row_stride, head_stride, n_rows;
     uint32_t *codes;
+    uint32_t *qcodes;  // mode 3: where the query codes go
     int n_heads;
     const float *w;
     uint16_t *k_cache, *v_cache;
@@ -78,7 +79,10 @@ __global__ void __launch_bounds__(kBThreads) k_encode_bits(BitsEncArgs a) {
     __shared__ int s_last;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int j = t % R, slot = t / R;
-    const int hy = blockIdx.y;
+    // mode 3: grid rows [0, B Hkv) append, the next Hkv rows encode the queries
+    const int role = a.mode != 3 ? a.mode : ((int)blockIdx.y < a.B * a.Hkv ? 1 : 2);
+    const int hy = (a.mode == 3 && role == 2) ? (int)blockIdx.y - a.B * a.Hkv : (int)blockIdx.y;
+    uint32_t *const codes_out = (a.mode == 3 && role == 2) ? a.qcodes : a.codes;
 
     // The rows this workgroup's grid column encodes, and their head.
     int head;
@@ -87,10 +91,10 @@ __global__ void __launch_bounds__(kBThreads) k_encode_bits(BitsEncArgs a) {
     int n_app = 0;
     bool entry_ok = true;
     int b_entry = 0;
-    if (a.mode == 0) {
+    if (role == 0) {
         head = hy;
         n_rows = a.n_rows;
-    } else if (a.mode == 1) {
+    } else if (role == 1) {
         b_entry = hy / a.Hkv;
         head = hy - b_entry * a.Hkv;
         len = a.seq_len[b_entry];
@@ -124,9 +128,9 @@ __global__ void __launch_bounds__(kBThreads) k_encode_bits(BitsEncArgs a) {
             uvec4 raw = {0u, 0u, 0u, 0u};
             if (row < n_rows) {
                 const uint16_t *src;
-                if (a.mode == 0) {
+                if (role == 0) {
                     src = a.x + row * a.row_stride + (int64_t)head * a.head_stride;
-                } else if (a.mode == 1) {
+                } else if (role == 1) {
                     const int64_t crow =
                         ((int64_t)hy * a.max_ctx + len + row) * kHeadDim;
                     if (a.k_new) {
@@ -189,13 +193,13 @@ __global__ void __launch_bounds__(kBThreads) k_encode_bits(BitsEncArgs a) {
             const uint64_t m = __ballot(bit);
             if (row < n_rows) {
                 uint32_t *out;
-                if (a.mode == 0) {
-                    out = a.codes + (row * a.n_heads + head) * W;
-                } else if (a.mode == 1) {
-                    out = a.codes + ((int64_t)hy * a.max_ctx + len + row) * W;
+                if (role == 0) {
+                    out = codes_out + (row * a.n_heads + head) * W;
+                } else if (role == 1) {
+                    out = codes_out + ((int64_t)hy * a.max_ctx + len + row) * W;
                 } else {
                     const int bb = (int)(row / a.G), g = (int)(row - (int64_t)bb * a.G);
-                    out = a.codes + ((int64_t)bb * a.Hkv * a.G + (int64_t)head * a.G + g) * W;
+                    out = codes_out + ((int64_t)bb * a.Hkv * a.G + (int64_t)head * a.G + g) * W;
                 }
                 if (R >= 64) {
                     // wave = 64 consecutive bits of one row
@@ -212,7 +216,7 @@ __global__ void __launch_bounds__(kBThreads) k_encode_bits(BitsEncArgs a) {
         }
     }
     (void)wv;
-    if (a.mode != 1) return;
+    if (a.mode != 1 && a.mode != 3) return;
     // The last workgroup publishes the new lengths (every workgroup has read
     // seq_len by then).
     __syncthreads();
@@ -418,6 +422,7 @@ __global__ void __launch_bounds__(kBThreads) k_select_bits(BitsDecArgs a) {
     // the first bin where it reaches k_eff (it is non-decreasing).
     for (int bin = t; bin < a.NB; bin += kBThreads) {
         int s = 0;
+#pragma unroll 8
         for (int sp = 0; sp < n_used; ++sp) s += hb[(int64_t)sp * a.NBpad + bin];
         uh[bin] = s;
     }
@@ -663,11 +668,13 @@ __global__ void __launch_bounds__(kBThreads) k_merge_bits(BitsDecArgs a) {
         float r = 0.f;
         if (nc > 0) {
             float M = -INFINITY;
+#pragma unroll 8
             for (int c = 0; c < nc; ++c) {
                 const float *ph = a.part + (((int64_t)unit * a.n_chunk + c) * a.G + h) * (2 + kHeadDim);
                 M = fmaxf(M, ph[0]);
             }
             float L = 0.f, O = 0.f;
+#pragma unroll 8
             for (int c = 0; c < nc; ++c) {
                 const float *ph = a.part + (((int64_t)unit * a.n_chunk + c) * a.G + h) * (2 + kHeadDim);
                 const float sc = exp2f(ph[0] - M);
@@ -740,22 +747,29 @@ hipError_t launch_decode_bits(const BitsPlan &p, uint16_t *k_cache, uint16_t *v_
     char *wsb = static_cast<char *>(ws);
     hipError_t e;
     const int units = p.B * p.Hkv;
-    if (k_new) {
-        e = launch_append_bits(k_cache, v_cache, codes, seq_len, ctrl, p.B, p.Hkv, p.max_ctx,
-                               k_new, v_new, nullptr, 1, w, p.R, s);
-        if (e != hipSuccess) return e;
-    }
     uint32_t *qcodes = reinterpret_cast<uint32_t *>(wsb + p.off_qcodes);
     {
+        // the step's append (one row per sequence) and the query codes
         BitsEncArgs ea = {};
-        ea.mode = 2;
+        ea.mode = k_new ? 3 : 2;
         ea.x = q;
-        ea.codes = qcodes;
+        ea.codes = k_new ? codes : qcodes;
+        ea.qcodes = qcodes;
         ea.w = w;
+        ea.k_cache = k_cache;
+        ea.v_cache = v_cache;
+        ea.seq_len = seq_len;
+        ea.ctrl = ctrl;
+        ea.n_new = nullptr;
+        ea.k_new = k_new;
+        ea.v_new = v_new;
         ea.B = p.B;
         ea.Hkv = p.Hkv;
         ea.G = p.G;
-        e = dispatch_enc_bits(ea, p.R, dim3(enc_grid_x((int64_t)p.B * p.G, p.Hkv), p.Hkv), s);
+        ea.t_max = 1;
+        ea.max_ctx = p.max_ctx;
+        const int rows_y = k_new ? p.B * p.Hkv + p.Hkv : p.Hkv;
+        e = dispatch_enc_bits(ea, p.R, dim3(enc_grid_x((int64_t)p.B * p.G, rows_y), rows_y), s);
         if (e != hipSuccess) return e;
     }
     BitsDecArgs a;
