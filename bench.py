@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=2)
+    ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with 4 plain 256 MiB device-to-device copies (the "
                          "calibration kernel for HBM byte counters)")

@@ -9,8 +9,10 @@
 //   k_encode_bits<R>   codes of flat rows, of appended cache rows, or of the
 //                      query heads.  Thread (row slot s, bit j) keeps column
 //                      j of W_H in registers; rows are staged 64 at a time in
-//                      LDS.  An fp32 fused multiply-add chain over d gives y'
-//                      with |y' - y| <= gamma_128 sum_d |x_d w_dj| + 2^-119
+//                      LDS.  Four interleaved fp32 fused multiply-add chains
+//                      over d, then their sum, give y' (at most 34 roundings
+//                      on any path) with
+//                      |y' - y| <= gamma_128 sum_d |x_d w_dj| + 2^-119
 //                      against the sequential double sum y, so the sign of
 //                      y' is taken when |y'| > 2^-16 ||x|| ||w_j|| + 2^-100
 //                      (and ||x|| ||w_j|| < 2^120, so no partial sum
@@ -174,9 +176,17 @@ __global__ void __launch_bounds__(kBThreads) k_encode_bits(BitsEncArgs a) {
             const int64_t row = r0 + rr;
             bool bit = false;
             if (rr < rows_here) {
-            float y = 0.f;
+            // four interleaved chains (34 roundings deep at most, inside the
+            // gamma_128 bound) so that the FMA latency overlaps
+            float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
 #pragma unroll
-            for (int d = 0; d < kHeadDim; ++d) y = fmaf(xs[rr][d], wv_[d], y);
+            for (int d = 0; d < kHeadDim; d += 4) {
+                y0 = fmaf(xs[rr][d], wv_[d], y0);
+                y1 = fmaf(xs[rr][d + 1], wv_[d + 1], y1);
+                y2 = fmaf(xs[rr][d + 2], wv_[d + 2], y2);
+                y3 = fmaf(xs[rr][d + 3], wv_[d + 3], y3);
+            }
+            const float y = (y0 + y1) + (y2 + y3);
             const double nn = xn[rr] * nw;
             if (nn < 0x1p120 && fabs((double)y) > 0x1p-16 * nn + 0x1p-100) {
                 bit = y > 0.f;
