@@ -9,10 +9,8 @@
 //   k_encode_bits<R>   codes of flat rows, of appended cache rows, or of the
 //                      query heads.  Thread (row slot s, bit j) keeps column
 //                      j of W_H in registers; rows are staged 64 at a time in
-//                      LDS.  Four interleaved fp32 fused multiply-add chains
-//                      over d, then their sum, give y' (at most 34 roundings
-//                      on any path) with
-//                      |y' - y| <= gamma_128 sum_d |x_d w_dj| + 2^-119
+//                      LDS.  An fp32 fused multiply-add chain over d gives y'
+//                      with |y' - y| <= gamma_128 sum_d |x_d w_dj| + 2^-119
 //                      against the sequential double sum y, so the sign of
 //                      y' is taken when |y'| > 2^-16 ||x|| ||w_j|| + 2^-100
 //                      (and ||x|| ||w_j|| < 2^120, so no partial sum
@@ -51,6 +49,54 @@ __device__ __forceinline__ void unpack8b(const uvec4 &r, float (&f)[8]) {
 }
 
 // ---------------------------------------------------------------- encoder
+
+// A double sum over the 64 lanes of a wave, in every lane: within each row of
+// 16 lanes by DPP (xor 1, xor 2, half-row mirror, row mirror), then the four
+// row sums added in order: with the caller's pair sum, eight rounding levels.
+template <int CTRL>
+__device__ __forceinline__ double bdpp_f64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ double blane_f64(double v, int l) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double bsum64(double v) {
+    v += bdpp_f64<0xB1>(v);
+    v += bdpp_f64<0x4E>(v);
+    v += bdpp_f64<0x141>(v);
+    v += bdpp_f64<0x140>(v);
+    return ((blane_f64(v, 0) + blane_f64(v, 16)) + blane_f64(v, 32)) + blane_f64(v, 48);
+}
+
+// The exact bit of one (row, column), by the whole wave: lane l forms the
+// exact double products of dims 2 l and 2 l + 1; their sum s is within
+// gamma_8 sum|p| of the real sum, the sequential double sum that defines the
+// bit within gamma_127 sum|p|, so the sign of s is the bit when
+// |s| > 2^-44 sum|p|; otherwise lane 0 runs the sequential loop itself.
+__device__ __attribute__((noinline)) bool wave_exact_bit(const float *xrow, const float *wcol, int R) {
+    const int lane = threadIdx.x & 63;
+    const double p0 = (double)xrow[2 * lane] * (double)wcol[(int64_t)(2 * lane) * R];
+    const double p1 = (double)xrow[2 * lane + 1] * (double)wcol[(int64_t)(2 * lane + 1) * R];
+    const double sv = bsum64(p0 + p1);
+    const double A = bsum64(fabs(p0) + fabs(p1));
+    bool bit = sv > 0.0;
+    if (!(fabs(sv) > 0x1p-44 * A)) {
+        int b = 0;
+        if (lane == 0) {
+            double y = 0.0;
+            for (int d = 0; d < kHeadDim; ++d) y = fma((double)xrow[d], (double)wcol[(int64_t)d * R], y);
+            b = y > 0.0;
+        }
+        bit = __builtin_amdgcn_readfirstlane(b) != 0;
+    }
+    return bit;
+}
 
 struct BitsEncArgs {
     int mode;  // 0: flat rows, 1: cache append, 2: query heads, 3: 1 and 2 in one launch
@@ -174,31 +220,28 @@ __global__ void __launch_bounds__(kBThreads) k_encode_bits(BitsEncArgs a) {
         const int rows_here = (int)(n_rows - r0 < kBTile ? n_rows - r0 : kBTile);
         for (int rr = slot; rr < kBTile; rr += P) {
             const int64_t row = r0 + rr;
-            bool bit = false;
+            bool bit = false, unsure = false;
             if (rr < rows_here) {
-            // four interleaved chains (34 roundings deep at most, inside the
-            // gamma_128 bound) so that the FMA latency overlaps
-            float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
+            float y = 0.f;
 #pragma unroll
-            for (int d = 0; d < kHeadDim; d += 4) {
-                y0 = fmaf(xs[rr][d], wv_[d], y0);
-                y1 = fmaf(xs[rr][d + 1], wv_[d + 1], y1);
-                y2 = fmaf(xs[rr][d + 2], wv_[d + 2], y2);
-                y3 = fmaf(xs[rr][d + 3], wv_[d + 3], y3);
-            }
-            const float y = (y0 + y1) + (y2 + y3);
+            for (int d = 0; d < kHeadDim; ++d) y = fmaf(xs[rr][d], wv_[d], y);
             const double nn = xn[rr] * nw;
             if (nn < 0x1p120 && fabs((double)y) > 0x1p-16 * nn + 0x1p-100) {
                 bit = y > 0.f;
             } else {
-                // rare: W_H's column is read again from memory, so the
-                // register copy stays fully unrolled
-                double e = 0.0;
-#pragma unroll 8
-                for (int d = 0; d < kHeadDim; ++d)
-                    e = fma((double)xs[rr][d], (double)wc[(int64_t)d * R], e);
-                bit = e > 0.0;
+                unsure = true;
             }
+            }
+            // the rare bits inside the band, one at a time by the whole wave
+            uint64_t um = __ballot(unsure);
+            while (um) {
+                const int lb = __builtin_ctzll(um);
+                um &= um - 1;
+                const int rr_l = __builtin_amdgcn_readlane(rr, lb);
+                const int j_l = __builtin_amdgcn_readlane(j, lb);
+                const bool eb = wave_exact_bit(&xs[rr_l][0],
+                                               a.w + (int64_t)head * kHeadDim * R + j_l, R);
+                if (lane == lb) bit = eb;
             }
             const uint64_t m = __ballot(bit);
             if (row < n_rows) {
