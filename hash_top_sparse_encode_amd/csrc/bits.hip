@@ -218,13 +218,26 @@ __global__ void __launch_bounds__(kBThreads) k_encode_bits(BitsEncArgs a) {
         }
         __syncthreads();
         const int rows_here = (int)(n_rows - r0 < kBTile ? n_rows - r0 : kBTile);
-        for (int rr = slot; rr < kBTile; rr += P) {
+        // Four rows per thread at a time (rows rb, rb + P, rb + 2P, rb + 3P):
+        // four independent FMA chains share the W_H registers, so the
+        // chains' latency overlaps.
+        for (int rb = slot; rb < kBTile; rb += 4 * P) {
+            float y4[4] = {0.f, 0.f, 0.f, 0.f};
+            if (rb < rows_here) {
+#pragma unroll
+                for (int d = 0; d < kHeadDim; ++d) {
+                    const float wd = wv_[d];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) y4[q] = fmaf(xs[rb + q * P][d], wd, y4[q]);
+                }
+            }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int rr = rb + q * P;
             const int64_t row = r0 + rr;
             bool bit = false, unsure = false;
             if (rr < rows_here) {
-            float y = 0.f;
-#pragma unroll
-            for (int d = 0; d < kHeadDim; ++d) y = fmaf(xs[rr][d], wv_[d], y);
+            const float y = y4[q];
             const double nn = xn[rr] * nw;
             if (nn < 0x1p120 && fabs((double)y) > 0x1p-16 * nn + 0x1p-100) {
                 bit = y > 0.f;
@@ -266,6 +279,7 @@ __global__ void __launch_bounds__(kBThreads) k_encode_bits(BitsEncArgs a) {
                     if (lane == 0 || lane == 32) out[0] = (uint32_t)(m >> lane);
                 }
             }
+        }
         }
     }
     (void)wv;
