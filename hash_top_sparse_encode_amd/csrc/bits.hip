@@ -25,9 +25,8 @@
 //                      earlier spans first).
 //   k_compact_bits     per (unit, span): the selected indices in index order.
 //   k_attend_bits      per (unit, chunk of 256 selected keys): softmax state
-//                      (m, l, o) of each query head of the group; the last
-//                      chunk of a unit to finish (a per-unit counter) merges
-//                      the chunks in chunk order into the bf16 output.
+//                      (m, l, o) of each query head of the group.
+//   k_merge_bits       per unit: the chunks merged in order, bf16 output.
 #include "device_util.h"
 #include "hata_internal.h"
 #include "bits_plan.h"
@@ -392,7 +391,6 @@ struct BitsDecArgs {
     int32_t *info;      // [unit][4]: T, k_eff
     int32_t *sel;       // [unit][k_max]
     float *part;        // [unit][n_chunk][G][2 + 128]
-    int32_t *cnt;       // [unit]: chunks finished (zero between calls)
     int B, Hq, Hkv, G, NB, NBpad, n_span, n_chunk, k_max;
     int64_t max_ctx;
 };
@@ -605,13 +603,7 @@ __global__ void __launch_bounds__(kBThreads) k_attend_bits(BitsDecArgs a) {
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6, sub = lane & 15, kk = lane >> 4;
     const int ke = a.info[unit * 4 + 1];
     const int c0 = chunk * kBChunk;
-    if (c0 >= ke) {
-        if (ke == 0 && chunk == 0) {
-            for (int idx = t; idx < G * kHeadDim; idx += kBThreads)
-                a.out[((int64_t)b * a.Hq + (int64_t)kv * G) * kHeadDim + idx] = 0;
-        }
-        return;
-    }
+    if (c0 >= ke) return;
     const int64_t len = bits_len(a, b);
     const float qscale = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
     float qf[G][8];
@@ -731,33 +723,35 @@ __global__ void __launch_bounds__(kBThreads) k_attend_bits(BitsDecArgs a) {
         }
         ph[2 + d] = O;
     }
-    // The last chunk of the unit merges: partials written and made visible
-    // device-wide before the count, read after it.
-    __shared__ int s_last;
+}
+
+__global__ void __launch_bounds__(kBThreads) k_merge_bits(BitsDecArgs a) {
+    const int unit = blockIdx.x, b = unit / a.Hkv, kv = unit - b * a.Hkv;
+    const int t = threadIdx.x;
+    const int ke = a.info[unit * 4 + 1];
     const int nc = (ke + kBChunk - 1) / kBChunk;
-    __threadfence();
-    __syncthreads();
-    if (t == 0) s_last = atomicAdd(&a.cnt[unit], 1) == nc - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int idx = t; idx < G * kHeadDim; idx += kBThreads) {
+    for (int idx = t; idx < a.G * kHeadDim; idx += kBThreads) {
         const int h = idx / kHeadDim, d = idx - h * kHeadDim;
-        const float *pu = a.part + (int64_t)unit * a.n_chunk * G * (2 + kHeadDim) + h * (2 + kHeadDim);
-        float M = -INFINITY;
+        float r = 0.f;
+        if (nc > 0) {
+            float M = -INFINITY;
 #pragma unroll 8
-        for (int c = 0; c < nc; ++c) M = fmaxf(M, pu[(int64_t)c * G * (2 + kHeadDim)]);
-        float L = 0.f, O = 0.f;
+            for (int c = 0; c < nc; ++c) {
+                const float *ph = a.part + (((int64_t)unit * a.n_chunk + c) * a.G + h) * (2 + kHeadDim);
+                M = fmaxf(M, ph[0]);
+            }
+            float L = 0.f, O = 0.f;
 #pragma unroll 8
-        for (int c = 0; c < nc; ++c) {
-            const float *ph = pu + (int64_t)c * G * (2 + kHeadDim);
-            const float sc = exp2f(ph[0] - M);
-            L = fmaf(ph[1], sc, L);
-            O = fmaf(ph[2 + d], sc, O);
+            for (int c = 0; c < nc; ++c) {
+                const float *ph = a.part + (((int64_t)unit * a.n_chunk + c) * a.G + h) * (2 + kHeadDim);
+                const float sc = exp2f(ph[0] - M);
+                L = fmaf(ph[1], sc, L);
+                O = fmaf(ph[2 + d], sc, O);
+            }
+            r = O / L;
         }
-        a.out[((int64_t)b * a.Hq + (int64_t)kv * G + h) * kHeadDim + d] = f32_to_bf16(O / L);
+        a.out[((int64_t)b * a.Hq + (int64_t)kv * a.G + h) * kHeadDim + d] = f32_to_bf16(r);
     }
-    if (t == 0) a.cnt[unit] = 0;
 }
 
 bool make_bits_plan(int B, int Hq, int Hkv, int64_t max_ctx, int n_bits, int k_max,
@@ -796,8 +790,6 @@ bool make_bits_plan(int B, int Hq, int Hkv, int64_t max_ctx, int n_bits, int k_m
     off = up(off + units * (size_t)k_max * 4);
     p->off_part = off;
     off = up(off + units * p->n_chunk * (size_t)G * (2 + kHeadDim) * 4);
-    p->off_cnt = off;
-    off = up(off + units * 4);
     p->total = off;
     return true;
 }
@@ -863,7 +855,6 @@ hipError_t launch_decode_bits(const BitsPlan &p, uint16_t *k_cache, uint16_t *v_
     a.info = reinterpret_cast<int32_t *>(wsb + p.off_info);
     a.sel = sel_idx_out ? sel_idx_out : reinterpret_cast<int32_t *>(wsb + p.off_sel);
     a.part = reinterpret_cast<float *>(wsb + p.off_part);
-    a.cnt = reinterpret_cast<int32_t *>(wsb + p.off_cnt);
     a.B = p.B;
     a.Hq = p.Hq;
     a.Hkv = p.Hkv;
@@ -893,7 +884,9 @@ hipError_t launch_decode_bits(const BitsPlan &p, uint16_t *k_cache, uint16_t *v_
         case 4: e = launch_attend_g<4>(a, ag, s); break;
         default: e = launch_attend_g<8>(a, ag, s); break;
     }
-    return e;
+    if (e != hipSuccess) return e;
+    k_merge_bits<<<units, kBThreads, 0, s>>>(a);
+    return hipGetLastError();
 }
 
 }  // namespace hata

@@ -19,7 +19,7 @@ struct BitsPlan {
     int k_max = 0;
     int64_t max_ctx = 0;
     size_t off_qcodes = 0, off_scores = 0, off_span_hist = 0, off_span_info = 0, off_info = 0,
-           off_sel = 0, off_part = 0, off_cnt = 0, total = 0;
+           off_sel = 0, off_part = 0, total = 0;
 };
 
 bool make_bits_plan(int B, int Hq, int Hkv, int64_t max_ctx, int n_bits, int k_max,
