@@ -307,9 +307,17 @@ __global__ void __launch_bounds__(kRecThreads) k_recall_select(RecallArgs a) {
             const int nb = pass == 2 ? 1024 : 2048;
             for (int j = t; j < 2048; j += kRecThreads) sm.hist[j] = 0;
             __syncthreads();
-            for (int64_t i = t; i < len; i += kRecThreads) {
-                const uint32_t key = okey(zrow[i]);
-                if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & (nb - 1)], 1u);
+            // four estimates per load (rows are padded to 64 entries; the
+            // entries past len are not counted)
+            for (int64_t i4 = 4 * (int64_t)t; i4 < len; i4 += 4 * kRecThreads) {
+                const float4 v = *reinterpret_cast<const float4 *>(zrow + i4);
+                const float e4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t key = okey(e4[e]);
+                    if (i4 + e < len && (key & pmask) == prefix)
+                        atomicAdd(&sm.hist[(key >> shift) & (nb - 1)], 1u);
+                }
             }
             __syncthreads();
             const int per = nb / kRecThreads;  // bins per thread, from the top
@@ -345,13 +353,20 @@ __global__ void __launch_bounds__(kRecThreads) k_recall_select(RecallArgs a) {
     if (t == 0) sm.nband = 0;
     __syncthreads();
     int u = 0;
-    for (int64_t i = t; i < len; i += kRecThreads) {
-        const double z = zrow[i];
-        if (!all_exact && z > hi) {
-            ++u;
-        } else if (all_exact || z >= lo) {
-            const int p = atomicAdd(&sm.nband, 1);
-            a.band_idx[bbase + p] = (int)i;
+    for (int64_t i4 = 4 * (int64_t)t; i4 < len; i4 += 4 * kRecThreads) {
+        const float4 v = *reinterpret_cast<const float4 *>(zrow + i4);
+        const float e4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t i = i4 + e;
+            const double z = e4[e];
+            if (i >= len) {
+            } else if (!all_exact && z > hi) {
+                ++u;
+            } else if (all_exact || z >= lo) {
+                const int p = atomicAdd(&sm.nband, 1);
+                a.band_idx[bbase + p] = (int)i;
+            }
         }
     }
     int n_in;
