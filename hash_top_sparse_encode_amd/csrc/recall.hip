@@ -230,9 +230,17 @@ __device__ void tie_bucket(const RecallArgs &a, RecSmem &sm, int unit, int64_t l
     for (int j = t; j < 4096; j += kRecThreads) sm.hist[j] = 0;
     __syncthreads();
     const uint16_t *sc = a.scores + (int64_t)unit * a.max_ctx;
-    for (int64_t i = t; i < len; i += kRecThreads) {
-        const int v = sc[i];
-        atomicAdd(&sm.hist[v < nbins ? v : nbins - 1], 1u);
+    // four independent loads in flight per thread
+    for (int64_t i0 = t; i0 < len; i0 += 4 * kRecThreads) {
+        int v4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t i = i0 + (int64_t)e * kRecThreads;
+            v4[e] = i < len ? (int)sc[i] : -1;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (v4[e] >= 0) atomicAdd(&sm.hist[v4[e] < nbins ? v4[e] : nbins - 1], 1u);
     }
     __syncthreads();
     const int c = (int)(sm.hist[4 * t] + sm.hist[4 * t + 1] + sm.hist[4 * t + 2] +
