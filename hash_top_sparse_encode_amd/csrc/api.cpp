@@ -41,7 +41,8 @@ const char *hata_status_string(hata_status s) {
     switch (s) {
         case HATA_OK: return "ok";
         case HATA_ERR_INVALID_ARG: return "invalid argument";
-        case HATA_ERR_UNSUPPORTED: return "unsupported shape (head_dim and n_bits must be 128, G in {1,2,4,8})";
+        case HATA_ERR_UNSUPPORTED:
+            return "unsupported shape (head_dim 128, n_bits in {32, 64, 128, 256}, G in {1, 2, 4, 8})";
         case HATA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case HATA_ERR_HIP: return "HIP launch failed";
     }

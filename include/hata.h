@@ -65,7 +65,7 @@ extern "C" {
 typedef enum {
     HATA_OK = 0,
     HATA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad stride ... */
-    HATA_ERR_UNSUPPORTED = 2, /* head_dim / n_bits != 128, G not in {1,2,4,8} */
+    HATA_ERR_UNSUPPORTED = 2, /* head_dim != 128, n_bits not in {32,64,128,256}, G not in {1,2,4,8} */
     HATA_ERR_WORKSPACE = 3,   /* workspace null or smaller than required */
     HATA_ERR_HIP = 4          /* a HIP launch failed */
 } hata_status;
@@ -172,9 +172,10 @@ hata_status hata_encode_keys_nbits(const uint16_t *keys, int64_t n_rows, int32_t
 hata_status hata_append(const hata_cache *c, const uint16_t *k_new, const uint16_t *v_new,
                         const int32_t *n_new, int32_t t_max, const float *w_h, void *stream);
 
-/* Bytes of device workspace hata_decode_attn needs for this cache (depends
- * on batch, heads and max_ctx only).  Returns 0 for an unsupported or
- * invalid cache. */
+/* Bytes of device workspace hata_decode_attn / hata_decode_step need for
+ * this cache: at n_bits = 128 a function of batch, heads and max_ctx; for
+ * the other code lengths also of n_bits and k_max.  Returns 0 for an
+ * unsupported or invalid cache. */
 size_t hata_decode_workspace_bytes(const hata_cache *c, int32_t k_max);
 
 /*
