@@ -8,7 +8,8 @@ binding raises if the shared library is missing (build it with
 there is no fallback of any kind.
 
 Names mirror the C ABI:
-  hata_encode_keys, hata_append, hata_decode_workspace_bytes,
+  hata_encode_keys (also the other code lengths, through
+  hata_encode_keys_nbits), hata_append, hata_decode_workspace_bytes,
   hata_decode_attn, hata_decode_step, hata_recall_workspace_bytes,
   hata_exact_topk_recall, hata_status_string
 plus ``HataCache``, a holder of the caller-owned cache tensors.
@@ -45,8 +46,8 @@ HATA_DEV_TOPK_CLAMPED = 0x4
 HATA_DEV_BAD_NEW = 0x8
 HATA_DEV_STALL = 0x10
 
-EXPORTED_SYMBOLS = ("hata_encode_keys", "hata_encode_keys_nbits", "hata_append", "hata_decode_workspace_bytes",
-                    "hata_decode_attn", "hata_decode_step", "hata_recall_workspace_bytes",
+EXPORTED_SYMBOLS = ("hata_encode_keys", "hata_encode_keys_nbits", "hata_append",
+                    "hata_decode_workspace_bytes", "hata_decode_attn", "hata_decode_step", "hata_recall_workspace_bytes",
                     "hata_exact_topk_recall", "hata_status_string")
 
 
