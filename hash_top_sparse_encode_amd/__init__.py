@@ -47,8 +47,9 @@ HATA_DEV_BAD_NEW = 0x8
 HATA_DEV_STALL = 0x10
 
 EXPORTED_SYMBOLS = ("hata_encode_keys", "hata_encode_keys_nbits", "hata_append",
-                    "hata_decode_workspace_bytes", "hata_decode_attn", "hata_decode_step", "hata_recall_workspace_bytes",
-                    "hata_exact_topk_recall", "hata_status_string")
+                    "hata_decode_workspace_bytes", "hata_decode_attn", "hata_decode_step",
+                    "hata_recall_workspace_bytes", "hata_exact_topk_recall",
+                    "hata_status_string")
 
 
 class _CCache(ctypes.Structure):
