@@ -45,7 +45,6 @@ constexpr int kERows = 64;     // rows per tile
 constexpr int kEThreads = 512;
 constexpr int kEBuf = 4;       // tiles in LDS: one computed, three on their way
 constexpr int kESegLds = 1024; // batch entries whose lengths are kept in LDS
-constexpr int kEBandQ = 512;   // in-band bits of a tile shared out to all waves (more: own wave)
 
 struct EncArgs {
     int mode;  // 0: flat rows (hata_encode_keys), 1: cache append
@@ -72,8 +71,6 @@ struct ESmem {
     float wt[kBits][kHeadDim];             // W_H transposed: wt[j][t] = W[t][j]
     uint16_t xs[kEBuf][kERows][kHeadDim];  // tile rows (bf16), 16-byte chunks swizzled
     uint16_t half[kERows][2 * kWords];     // each wave's 16 code bits per row
-    uint32_t band_q[kEBandQ];              // in-band bits of the tile: row << 8 | column
-    int band_n;
     int64_t seg_l0[kESegLds];              // mode 1: each entry's length ...
     int32_t seg_rows[kESegLds];            // ... and rows to encode
     int last;
@@ -266,7 +263,6 @@ __global__ __launch_bounds__(kEThreads, 1) void k_encode_mfma(EncArgs a) {
         ss += __shfl_xor(ss, 32, 64);
         wnorm = sqrtf(ss) * (1.f + 0x1p-10f);
     }
-    if (t == 0) sm.band_n = 0;
     __syncthreads();  // W_H and the lengths in LDS
 
     const int64_t n_tiles = a.tiles_per_seg * a.n_seg;
@@ -344,51 +340,24 @@ __global__ __launch_bounds__(kEThreads, 1) void k_encode_mfma(EncArgs a) {
                     if ((lane >> 4) == mt && (lane & 3) == i) hv = (uint32_t)((bits >> (16 * gg)) & 0xFFFFu);
                 }
             if (__ballot(unsure) != 0) {
-                // in-band bits go to the tile's queue, which all eight waves
-                // share once every wave has its decided bits (the slowest
-                // wave no longer holds the others); past the queue's end a
-                // wave recomputes its own
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const bool valid = 16 * mt + 4 * g + i < e.nr;
                         uint64_t um = __ballot(valid && !(fabsf(acc[mt][i]) > band(xnr[mt][i], wnorm)));
-                        if (um == 0) continue;
-                        int slot = 0;
-                        if (lane == 0) slot = atomicAdd(&sm.band_n, __popcll(um));
-                        slot = __builtin_amdgcn_readfirstlane(slot);
                         while (um) {
                             const int lb = __builtin_ctzll(um);
                             um &= um - 1;
                             const int Rf = 16 * mt + 4 * (lb >> 4) + i;
                             const int cb = lb & 15;
-                            if (slot < kEBandQ) {
-                                if (lane == 0) sm.band_q[slot] = (uint32_t)(Rf << 8 | (16 * wv + cb));
-                            } else if (exact_bit(sm, xb, Rf, 16 * wv + cb) && lane == Rf) {
-                                hv |= 1u << cb;
-                            }
-                            ++slot;
+                            if (exact_bit(sm, xb, Rf, 16 * wv + cb) && lane == Rf) hv |= 1u << cb;
                         }
                     }
             }
             sm.half[lane][wv] = (uint16_t)hv;
         }
-        __syncthreads();  // every wave has its decided bits in LDS, the queue is complete
-        {
-            const int nq = sm.band_n < kEBandQ ? sm.band_n : kEBandQ;
-            if (nq > 0) {
-                for (int q = wv; q < nq; q += kEThreads / 64) {
-                    const uint32_t ent = sm.band_q[q];
-                    const int Rf = (int)(ent >> 8), col = (int)(ent & 0xFF);
-                    if (exact_bit(sm, xb, Rf, col) && lane == 0)
-                        atomicOr(reinterpret_cast<uint32_t *>(&sm.half[Rf][0]) + (col >> 5),
-                                 1u << (col & 31));
-                }
-                __syncthreads();  // every queued bit is in LDS
-            }
-        }
-        if (t == 0) sm.band_n = 0;  // the next tile's appends follow its first barrier
+        __syncthreads();  // every wave is done with xb and has its bits in LDS
         if (e.nr > 0 && wv == 4 && lane < e.nr) {
             // wave 4: whole code words of row lane (and, for appends of new
             // rows, the K / V rows into the cache)
