@@ -18,12 +18,13 @@
 //                      sum itself.  Bits are packed with wave ballots.
 //   k_scan_bits<R>     per (unit, span of 8192 keys): summed Hamming scores
 //                      (u16) and the span's score histogram.
-//   k_select_bits      per unit: the cut T (first score whose cumulative
-//                      count reaches k_eff), and per span the offset of its
-//                      selected keys and how many of its score-T keys it
-//                      takes (ties go to the lowest indices, i.e. to the
-//                      earlier spans first).
-//   k_compact_bits     per (unit, span): the selected indices in index order.
+//   k_compact_bits     per (unit, span): the cut T (first score whose
+//                      cumulative count over the unit reaches k_eff, found
+//                      from the spans' cumulative histograms), this span's
+//                      offset in the selection and how many of its score-T
+//                      keys it takes (ties go to the lowest indices, i.e. to
+//                      the earlier spans first), then its selected indices in
+//                      index order.
 //   k_attend_bits      per (unit, chunk of 256 selected keys): softmax state
 //                      (m, l, o) of each query head of the group.
 //   k_merge_bits       per unit: the chunks merged in order, bf16 output.
@@ -461,90 +462,94 @@ __global__ void __launch_bounds__(kBThreads) k_scan_bits(BitsDecArgs a) {
     }
 }
 
-__global__ void __launch_bounds__(kBThreads) k_select_bits(BitsDecArgs a) {
-    __shared__ int uh[8 * 256 + 1];
+__global__ void __launch_bounds__(kBThreads) k_compact_bits(BitsDecArgs a) {
     __shared__ int tmp[8];
-    __shared__ int s_T, s_below;
-    const int unit = blockIdx.x, b = unit / a.Hkv;
+    __shared__ int c1[2 * kBThreads + 8];  // cumulative count at the end of each group of 8 bins
+    __shared__ int c2[8];
+    __shared__ int s_g, s_T, s_below, s_off, s_take;
+    const int span = blockIdx.x, unit = blockIdx.y, b = unit / a.Hkv;
     const int t = threadIdx.x;
     const int64_t len = bits_len(a, b);
     const int ke = bits_keff(a, b, len);
-    if (t == 0) {
-        const int64_t raw = a.seq_len[b];
-        if (raw < 0 || raw > a.max_ctx) atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_BAD_LENGTH);
-        if (a.topk[b] > a.k_max) atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_TOPK_CLAMPED);
-    }
+    const int64_t i0 = (int64_t)span * kBSpan;
     int32_t *sel = a.sel + (int64_t)unit * a.k_max;
-    for (int i = ke + t; i < a.k_max; i += kBThreads) sel[i] = -1;
-    if (ke == 0) {
+    if (span == 0) {
         if (t == 0) {
-            a.info[unit * 4 + 0] = -1;
-            a.info[unit * 4 + 1] = 0;
+            const int64_t raw = a.seq_len[b];
+            if (raw < 0 || raw > a.max_ctx) atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_BAD_LENGTH);
+            if (a.topk[b] > a.k_max) atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_TOPK_CLAMPED);
+            a.info[unit * 4 + 1] = ke;
         }
-        return;
+        for (int i = ke + t; i < a.k_max; i += kBThreads) sel[i] = -1;
     }
+    if (ke == 0 || i0 >= len) return;
+    // The cut T: the first bin where the unit's cumulative count (the sum of
+    // its spans' cumulative histograms) reaches k_eff -- first among the ends
+    // of groups of 8 bins, then within the group found.
     const int n_used = (int)((len + kBSpan - 1) / kBSpan);
     const int32_t *hb = a.span_hist + (int64_t)unit * a.n_span * a.NBpad;
-    // The unit's cumulative histogram is the sum of its spans' ones; T is
-    // the first bin where it reaches k_eff (it is non-decreasing).
-    for (int bin = t; bin < a.NB; bin += kBThreads) {
-        int s = 0;
+    const int ngr = (a.NB + 7) / 8;
+    for (int gi = t; gi < ngr; gi += kBThreads) {
+        const int bin = 8 * gi + 7 < a.NB ? 8 * gi + 7 : a.NB - 1;
+        int sum = 0;
 #pragma unroll 8
-        for (int sp = 0; sp < n_used; ++sp) s += hb[(int64_t)sp * a.NBpad + bin];
-        uh[bin] = s;
+        for (int sp = 0; sp < n_used; ++sp) sum += hb[(int64_t)sp * a.NBpad + bin];
+        c1[gi] = sum;
     }
     __syncthreads();
-    for (int bin = t; bin < a.NB; bin += kBThreads) {
-        if (uh[bin] >= ke && (bin == 0 || uh[bin - 1] < ke)) {
+    for (int gi = t; gi < ngr; gi += kBThreads)
+        if (c1[gi] >= ke && (gi == 0 || c1[gi - 1] < ke)) s_g = gi;
+    __syncthreads();
+    const int g = s_g;
+    if (t < 8) {
+        const int bin = 8 * g + t;
+        int sum = (int)len;  // bins past the last: the total
+        if (bin < a.NB) {
+            sum = 0;
+#pragma unroll 8
+            for (int sp = 0; sp < n_used; ++sp) sum += hb[(int64_t)sp * a.NBpad + bin];
+        }
+        c2[t] = sum;
+    }
+    __syncthreads();
+    if (t < 8) {
+        const int bin = 8 * g + t;
+        const int prev = t == 0 ? (g == 0 ? 0 : c1[g - 1]) : c2[t - 1];
+        if (bin < a.NB && c2[t] >= ke && prev < ke) {
             s_T = bin;
-            s_below = bin == 0 ? 0 : uh[bin - 1];
+            s_below = prev;
         }
     }
     __syncthreads();
     const int T = s_T, need = ke - s_below;
-    // Per span: keys under T, keys at T taken (the earlier spans first).
+    // This span's offset in the selection and its share of the score-T keys
+    // (the earlier spans first).
     int carry_ties = 0, carry_off = 0;
-    for (int s0 = 0; s0 < n_used; s0 += kBThreads) {
+    for (int s0 = 0; s0 <= span; s0 += kBThreads) {
         const int sp = s0 + t;
         int below = 0, ties = 0;
-        if (sp < n_used) {
+        if (sp <= span) {
             const int32_t *hr = hb + (int64_t)sp * a.NBpad;
             below = T > 0 ? hr[T - 1] : 0;
             ties = hr[T] - below;
         }
         int tt;
         const int ties_before = carry_ties + block_excl_scan_256(ties, tmp, &tt);
-        int take = need - ties_before;
-        take = take < 0 ? 0 : (take > ties ? ties : take);
+        int take_sp = need - ties_before;
+        take_sp = take_sp < 0 ? 0 : (take_sp > ties ? ties : take_sp);
         int to;
-        const int off = carry_off + block_excl_scan_256(below + take, tmp, &to);
-        if (sp < n_used) {
-            int32_t *si = a.span_info + ((int64_t)unit * a.n_span + sp) * 2;
-            si[0] = off;
-            si[1] = take;
+        const int off_sp = carry_off + block_excl_scan_256(below + take_sp, tmp, &to);
+        if (sp == span) {
+            s_off = off_sp;
+            s_take = take_sp;
         }
         carry_ties += tt;
         carry_off += to;
     }
-    if (t == 0) {
-        a.info[unit * 4 + 0] = T;
-        a.info[unit * 4 + 1] = ke;
-    }
-}
-
-__global__ void __launch_bounds__(kBThreads) k_compact_bits(BitsDecArgs a) {
-    __shared__ int tmp[8];
-    const int span = blockIdx.x, unit = blockIdx.y, b = unit / a.Hkv;
-    const int t = threadIdx.x;
-    const int64_t len = bits_len(a, b);
-    const int ke = a.info[unit * 4 + 1];
-    const int64_t i0 = (int64_t)span * kBSpan;
-    if (ke == 0 || i0 >= len) return;
-    const int T = a.info[unit * 4 + 0];
-    const int32_t *si = a.span_info + ((int64_t)unit * a.n_span + span) * 2;
-    const int off = si[0], take = si[1];
+    __syncthreads();
+    const int off = s_off, take = s_take;
+    if (span == 0 && t == 0) a.info[unit * 4 + 0] = T;
     const uint16_t *sb = a.scores + (int64_t)unit * a.max_ctx;
-    int32_t *sel = a.sel + (int64_t)unit * a.k_max;
     int ties_seen = 0, written = 0;
     for (int c0 = 0; c0 < kBSpan; c0 += 8 * kBThreads) {
         int below_f = 0, tie_f = 0, nt = 0;
@@ -873,8 +878,6 @@ hipError_t launch_decode_bits(const BitsPlan &p, uint16_t *k_cache, uint16_t *v_
         default: e = launch_scan_r<256>(a, sg, s); break;
     }
     if (e != hipSuccess) return e;
-    k_select_bits<<<units, kBThreads, 0, s>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     k_compact_bits<<<sg, kBThreads, 0, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 ag(p.n_chunk, units);
