@@ -388,7 +388,6 @@ struct BitsDecArgs {
     const uint32_t *qcodes;
     uint16_t *scores;   // [unit][max_ctx]
     int32_t *span_hist; // [unit][n_span][NBpad]
-    int32_t *span_info; // [unit][n_span][2]: offset, score-T keys taken
     int32_t *info;      // [unit][4]: T, k_eff
     int32_t *sel;       // [unit][k_max]
     float *part;        // [unit][n_chunk][G][2 + 128]
@@ -787,8 +786,6 @@ bool make_bits_plan(int B, int Hq, int Hkv, int64_t max_ctx, int n_bits, int k_m
     off = up(off + units * (size_t)max_ctx * 2);
     p->off_span_hist = off;
     off = up(off + units * p->n_span * (size_t)p->NBpad * 4);
-    p->off_span_info = off;
-    off = up(off + units * p->n_span * 2 * 4);
     p->off_info = off;
     off = up(off + units * 4 * 4);
     p->off_sel = off;
@@ -856,7 +853,6 @@ hipError_t launch_decode_bits(const BitsPlan &p, uint16_t *k_cache, uint16_t *v_
     a.qcodes = qcodes;
     a.scores = scores_out ? scores_out : reinterpret_cast<uint16_t *>(wsb + p.off_scores);
     a.span_hist = reinterpret_cast<int32_t *>(wsb + p.off_span_hist);
-    a.span_info = reinterpret_cast<int32_t *>(wsb + p.off_span_info);
     a.info = reinterpret_cast<int32_t *>(wsb + p.off_info);
     a.sel = sel_idx_out ? sel_idx_out : reinterpret_cast<int32_t *>(wsb + p.off_sel);
     a.part = reinterpret_cast<float *>(wsb + p.off_part);

@@ -18,7 +18,7 @@ struct BitsPlan {
     int B = 0, Hq = 0, Hkv = 0, G = 0, R = 0, NB = 0, NBpad = 0, n_span = 0, n_chunk = 0;
     int k_max = 0;
     int64_t max_ctx = 0;
-    size_t off_qcodes = 0, off_scores = 0, off_span_hist = 0, off_span_info = 0, off_info = 0,
+    size_t off_qcodes = 0, off_scores = 0, off_span_hist = 0, off_info = 0,
            off_sel = 0, off_part = 0, total = 0;
 };
 
