@@ -487,7 +487,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 K/V/q/out, fp32 W_H and accumulation, u32 codes",
+        "dtype": "bf16",
+        "dtype_detail": "bf16 K/V/q/out, fp32 W_H and accumulation, u32 codes",
         "data": "synthetic (seeded SplitMix64/Box-Muller; N(0,1) K/V/q, N(0,1/128) W_H, "
                 "0.1% planted aligned keys)",
         "config": {
