@@ -22,7 +22,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhata.so")
+# HATA_LIB_PATH names another build of the same library (the sanitizer test
+# loads a host-side ASan/UBSan build this way).
+LIB_PATH = os.environ.get("HATA_LIB_PATH") or os.path.join(_PKG, "libhata.so")
 
 HEAD_DIM = 128
 N_BITS = 128

@@ -26,7 +26,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hata_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# HATA_ORACLE_LIB names another build of hata_oracle.c (the sanitizer test
+# loads an ASan/UBSan build this way).
+_LIB_PATH = os.environ.get("HATA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 D = 128
