@@ -13,7 +13,13 @@ codes between two visits of the same layer, and over QUERIES step queries
 (step 0's is the one the planted keys align with; the others are fresh
 draws), so the gathered rows change from visit to visit.
 
-Prints one JSON line.  value = decode steps per second on one GPU.
+Prints one JSON line.  value = decode steps per second on one GPU.  The
+line also carries every workload configuration (``configs``: 1 = 4K batch 1,
+2 = Llama-3.1-8B-shaped 32K batch 8, 3 = the headline, 4 = 1M batch 1,
+5 = 64 ragged sequences of 1K-64K with their prefill encode), each timed the
+same way with its own rotation of layer caches, and the oracle timed beside
+it on a bounded sample.  ``--config N`` makes configuration N the headline
+workload (default 3, the one the metric names).
 """
 from __future__ import annotations
 
@@ -48,6 +54,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5],
+                    help="the headline workload (3: 128K context, the metric's)")
+    ap.add_argument("--configs", default="1,2,3,4,5",
+                    help="configurations measured beside the headline ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--copy-probe", action="store_true",
@@ -194,6 +204,140 @@ def cpu_baseline(spec, reps):
             "cpu_model": _cpu_model()}
 
 
+LLC_BYTES = 256 << 20
+
+
+def rotation_layers(step_bytes, cap=16):
+    """Distinct layer caches for a timing loop: enough that the bytes the
+    other layers' steps move between two visits of one layer exceed 2.5 times
+    the 256 MB last-level cache, so a visit finds its codes in HBM."""
+    return int(min(cap, max(2, math.ceil(2.5 * LLC_BYTES / max(step_bytes, 1)) + 1)))
+
+
+def spec_alg_bytes(spec, appended, n_bits=128):
+    """algorithmic_bytes for any workload (ragged lengths included), with
+    `appended` tokens added to every context since the prefill."""
+    Hkv, Hq, words_b = spec.Hkv, spec.Hq, n_bits // 8
+    tot = 0.0
+    for b in range(spec.B):
+        n = spec.lengths[b] + appended
+        tot += words_b * Hkv * n + 512 * Hkv * min(spec.topk[b], n)
+    return tot + 4 * Hkv * 128 * n_bits + 4 * spec.B * Hq * 128 + spec.B * Hkv * (512 + words_b)
+
+
+def oracle_sample(spec, units, cores):
+    """The oracle's decode step (query codes, per-bit Hamming, sort, double
+    attention; key codes from an untimed oracle encode) on a few units, one
+    core each; projected to the whole step by key rows, spread over `cores`
+    threads (units are independent)."""
+    import oracle
+    import synth
+    q, w, new = synth.gen_q(spec), synth.gen_w(spec), synth.gen_new_token(spec)
+    G = spec.G
+    t_rows, rows = 0.0, 0
+    for (b, kv) in units:
+        K, V = synth.unit_context(spec, b, kv, q, new)
+        kc = oracle.encode(K, w[kv], threads=cores)
+        t0 = time.perf_counter()
+        oracle.decode_unit(q[b, kv * G:(kv + 1) * G], w[kv], K, V, spec.topk[b], kcodes=kc,
+                           threads=1)
+        t_rows += time.perf_counter() - t0
+        rows += K.shape[0]
+    all_rows = spec.Hkv * sum(spec.lengths)
+    n_units = spec.B * spec.Hkv
+    par = min(cores, n_units)
+    step_s = t_rows / rows * all_rows / par
+    return {"steps_per_s_est": 1.0 / step_s, "us_per_step_est": step_s * 1e6, "cores": par,
+            "kind": "oracle",
+            "sample": f"{len(units)} of {n_units} units timed on one core each "
+                      f"({rows} key rows), projected by key rows to the whole step on "
+                      f"{par} threads over units"}
+
+
+def measure_config(cfg, args, dev, cores):
+    """One configuration's decode step timed as the headline is (events and
+    wall clock around back-to-back hata_decode_step calls over a rotation of
+    layer caches and step queries), plus its prefill encode and the oracle
+    on a sample."""
+    import torch
+    import hash_top_sparse_encode_amd as hata
+    import synth
+    from workload import GpuWorkload, bf16_dev
+
+    spec = synth.config(cfg)
+    B, Hq, Hkv = spec.B, spec.Hq, spec.Hkv
+    L = rotation_layers(spec_alg_bytes(spec, 0))
+    per_layer = math.ceil((args.warmup + args.steps) / L) + 2
+    print(f"[bench] configuration {cfg}: {spec.name}, {L} layer caches", file=sys.stderr,
+          flush=True)
+    base = GpuWorkload(spec, dev, extra_ctx=per_layer)
+    stream = torch.cuda.current_stream()
+    enc = []
+    for _ in range(2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        base.encode_prefill()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        enc.append(e0.elapsed_time(e1))
+    enc_rows = Hkv * sum(n - 1 for n in spec.lengths)
+    enc_s = enc[-1] * 1e-3
+    caches = [(base.cache, base.ws)]
+    for i in range(1, L):
+        c = hata.HataCache(B, Hq, Hkv, base.max_ctx, device=dev, k=base.cache.k.clone(),
+                           v=base.cache.v.clone(), codes=base.cache.codes.clone(),
+                           seq_len=base.n_pre.clone())
+        caches.append((c, hata.alloc_workspace(c, base.k_max)))
+    base.cache.seq_len.copy_(base.n_pre)
+    k_new, v_new = base.k_new.view(B, Hkv, 128), base.v_new.view(B, Hkv, 128)
+    queries = [base.q] + [bf16_dev(synth.gen_q(spec, i), dev) for i in range(1, QUERIES)]
+    out = torch.empty_like(base.out)
+
+    def step(s):
+        c, ws = caches[s % L]
+        hata.hata_decode_step(c, k_new, v_new, queries[s % QUERIES], base.w, base.topk,
+                              base.k_max, out, ws)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for s in range(args.steps):
+        step(args.warmup + s)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    if any(c.status() for c, _ in caches):
+        print(f"[bench] configuration {cfg}: device status flags set", file=sys.stderr)
+        sys.exit(1)
+    appended = args.warmup / L + (args.steps / L) / 2.0  # mean over the timed steps
+    alg = spec_alg_bytes(spec, appended)
+    sps = args.steps / wall
+    res = {
+        "config": cfg,
+        "workload": spec.name,
+        "layer_caches": L,
+        "us_per_step": wall * 1e6 / args.steps,
+        "steps_per_s": sps,
+        "tokens_per_s": sps * B,
+        "launch_us": launch_us,
+        "alg_bytes": alg,
+        "hbm_frac": alg / (launch_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+        "prefill_encode": {"rows": enc_rows, "ms": enc_s * 1e3,
+                           "hbm_GBps": enc_rows * (256 + 16) / enc_s / 1e9,
+                           "alg_bytes": enc_rows * (256 + 16)},
+    }
+    del caches, base, queries, out
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        units = [(0, 0)] if spec.lengths[0] > 100000 else [(0, 0), (spec.B - 1, spec.Hkv - 1)]
+        res["oracle"] = oracle_sample(spec, units, cores)
+    return res
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -221,7 +365,7 @@ def main():
     from workload import GpuWorkload
 
     dev = torch.device("cuda:0")
-    spec = synth.config(3)
+    spec = synth.config(args.config)
     B, Hq, Hkv, N, K = spec.B, spec.Hq, spec.Hkv, spec.lengths[0], spec.topk[0]
     L = max(1, args.layers)
     # room for every append: the layer steps, and up to 58 steps each on the
@@ -331,7 +475,7 @@ def main():
         torch.cuda.synchronize()
         if r > 0:
             enc_ms.append(e0.elapsed_time(e1))
-    enc_rows = B * Hkv * (N - 1)
+    enc_rows = Hkv * sum(n - 1 for n in spec.lengths)
     enc_s = statistics.mean(enc_ms) * 1e-3
     prefill = {
         "what": "hata_append encoding the N - 1 prefilled rows of every (sequence, KV head) "
@@ -418,7 +562,8 @@ def main():
         "steps": n_off,
         "steps_per_s": 1.0 / off_s,
         "us_per_step": off_s * 1e6,
-        "selected_rows_GBps": B * Hkv * K * 512 / off_s / 1e9,
+        "selected_rows_GBps": Hkv * sum(min(k, n) for k, n in zip(spec.topk, spec.lengths)) * 512
+                              / off_s / 1e9,
         "vs_device_resident": (1.0 / off_s) / steps_per_s,
     }
     del off, off_ws
@@ -428,51 +573,62 @@ def main():
     # 64 bits, 17 and 34 MB, fit in the last-level cache, so they are
     # flattered), prefill encode in place, then decode steps on the
     # multi-launch path.
+    # Each code length gets its own rotation of layer caches (K/V copies and
+    # r-bit codes) sized as for the configurations, so that its codes are
+    # read from HBM and not the last-level cache.
     code_lengths = []
     for r in (32, 64, 256):
         w_r = torch.from_numpy(synth.gen_w_bits(spec, r)).to(dev)
-        c_r = hata.HataCache(B, Hq, Hkv, base.max_ctx, device=dev, k=base.cache.k,
-                             v=base.cache.v, n_bits=r)
+        L_r = rotation_layers(spec_alg_bytes(spec, 0, r))
+        c_r = hata.HataCache(B, Hq, Hkv, base.max_ctx, device=dev, k=base.cache.k.clone(),
+                             v=base.cache.v.clone(), n_bits=r)
         enc_t = []
         for rep_i in range(2):
             c_r.seq_len.zero_()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            hata.hata_append(c_r, None, None, base.n_pre, N - 1, w_r)
+            hata.hata_append(c_r, None, None, base.n_pre, spec.max_len - 1, w_r)
             e1.record(stream)
             torch.cuda.synchronize()
             enc_t.append(e0.elapsed_time(e1))
-        ws_r = hata.alloc_workspace(c_r, base.k_max)
+        rot = [(c_r, hata.alloc_workspace(c_r, base.k_max))]
+        for i in range(1, L_r):
+            c = hata.HataCache(B, Hq, Hkv, base.max_ctx, device=dev, k=base.cache.k.clone(),
+                               v=base.cache.v.clone(), codes=c_r.codes.clone(),
+                               seq_len=c_r.seq_len.clone(), n_bits=r)
+            rot.append((c, hata.alloc_workspace(c, base.k_max)))
         out_r = torch.empty_like(base.out)
 
         def step_r(s):
-            hata.hata_decode_step(c_r, k_new, v_new, queries[s % QUERIES], w_r, base.topk,
-                                  base.k_max, out_r, ws_r)
+            c, ws = rot[s % L_r]
+            hata.hata_decode_step(c, k_new, v_new, queries[s % QUERIES], w_r, base.topk,
+                                  base.k_max, out_r, ws)
 
-        for s in range(5):
+        warm_r = 2 * L_r
+        for s in range(warm_r):
             step_r(s)
-        n_r = max(1, min(args.steps, 30))
+        n_r = max(1, min(args.steps, 8 * L_r))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for s in range(n_r):
-            step_r(5 + s)
+            step_r(warm_r + s)
         e1.record(stream)
         torch.cuda.synchronize()
-        if c_r.status():
-            print(f"[bench] r={r}: device status flags set: {c_r.status()}", file=sys.stderr)
+        if any(c.status() for c, _ in rot):
+            print(f"[bench] r={r}: device status flags set", file=sys.stderr)
             sys.exit(1)
         us = e0.elapsed_time(e1) * 1e3 / n_r
-        ctx_r = N + 5 + (n_r - 1) / 2.0  # mean context of the timed steps
-        alg_r = (r // 8) * B * Hkv * ctx_r + 512 * B * Hkv * K + 4 * Hkv * 128 * r + \
-            4 * B * Hq * 128 + B * Hkv * (512 + r // 8)
+        alg_r = spec_alg_bytes(spec, warm_r / L_r + (n_r / L_r) / 2.0, r)
         code_lengths.append({"n_bits": r, "us_per_step": us, "steps_per_s": 1e6 / us,
                              "alg_bytes": alg_r, "alg_GBps": alg_r / us / 1e3,
-                             "prefill_encode_ms": enc_t[-1]})
-        del c_r, ws_r
+                             "hbm_frac": alg_r / us / 1e3 / HBM_PEAK_GBS,
+                             "layer_caches": L_r, "prefill_encode_ms": enc_t[-1]})
+        del rot, c_r
+        torch.cuda.empty_cache()
     base.cache.seq_len.copy_(base.n_pre)
 
     n_ctx = ctx0 + (args.steps // L) / 2.0  # mean context over the timed steps
-    step_bytes = algorithmic_bytes(B, Hq, Hkv, n_ctx, K)
+    step_bytes = spec_alg_bytes(spec, n_ctx - spec.lengths[0])
     achieved = step_bytes / (dec_ms * 1e-3) / 1e9
     traffic_bytes = measured_traffic_bytes()
 
@@ -492,8 +648,8 @@ def main():
         "data": "synthetic (seeded SplitMix64/Box-Muller; N(0,1) K/V/q, N(0,1/128) W_H, "
                 "0.1% planted aligned keys)",
         "config": {
-            "workload": "hashed top-k decode step: B=4, Hq=32, Hkv=8, d=128, r=128, "
-                        f"context {N} (+{args.steps // L} appended), top-k {K}, "
+            "workload": f"hashed top-k decode step, {spec.name}: B={B}, Hq={Hq}, Hkv={Hkv}, "
+                        f"d=128, r=128, context {N} (+{args.steps // L} appended), top-k {K}, "
                         f"{L} layer caches visited in turn, {QUERIES} step queries",
             "tokens_per_s": steps_per_s * B,
             "us_per_step": ms_per_step * 1e3,
@@ -533,6 +689,33 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(spec, args.cpu_reps)
+
+    # Every configuration, each with its own layer rotation; the headline's
+    # own entry reuses the numbers above.
+    wanted = [] if args.configs == "none" else [int(c) for c in args.configs.split(",")]
+    if wanted:
+        del layers, base, queries, ly
+        torch.cuda.empty_cache()
+        cores = max(1, min(16, os.cpu_count() or 1))
+        per_cfg = []
+        for c in wanted:
+            if c == args.config:
+                e = {"config": c, "workload": spec.name, "layer_caches": L,
+                     "us_per_step": ms_per_step * 1e3, "steps_per_s": steps_per_s,
+                     "tokens_per_s": steps_per_s * B, "launch_us": dec_ms * 1e3,
+                     "alg_bytes": step_bytes, "hbm_frac": achieved / HBM_PEAK_GBS,
+                     "prefill_encode": {"rows": prefill["rows"], "ms": prefill["ms"],
+                                        "hbm_GBps": prefill["hbm_GBps"],
+                                        "alg_bytes": prefill["rows"] * (256 + 16)}}
+                if "cpu_baseline" in result:
+                    cb = result["cpu_baseline"]
+                    e["oracle"] = {"steps_per_s": cb["value"], "us_per_step": 1e6 / cb["value"],
+                                   "cores": cb["cores"], "kind": "oracle",
+                                   "sample": "the whole step (cpu_baseline)"}
+                per_cfg.append(e)
+            else:
+                per_cfg.append(measure_config(c, args, dev, cores))
+        result["configs"] = per_cfg
     print(json.dumps(result), flush=True)
 
 

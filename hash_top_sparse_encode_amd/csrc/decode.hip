@@ -63,6 +63,8 @@
 // Only the split partials are published behind a counter (stores drained,
 // then one atomic add), for the merge.  An agent-scope fence would write
 // back / invalidate whole L2s instead, which costs more than the step.
+#include <stdlib.h>
+
 #include "device_util.h"
 #include "hata_internal.h"
 #include "../../include/hata.h"
@@ -125,6 +127,8 @@ struct FusedArgs {
     int n_chunks;            // work items per unit
     int tails_last;          // every unit's last work item after all the others (see item_of)
     int n_items;
+    int spin_limit;          // bound of the query-code wait (re-reads by one wave)
+    int poll_limit;          // bound of the histogram waits (block-wide re-reads)
 };
 
 // ---------------------------------------------------------------- coherent access
@@ -572,7 +576,7 @@ __device__ __forceinline__ void slot_fetch_qcodes(const FusedArgs &a, const Slot
     const uint32_t tag = ld_dev(a.gen + s.u) + 1u;
     uint64_t v = lane < NW ? ld_dev(src + lane) : (uint64_t)tag << 32;
     for (int spins = 0; __ballot((uint32_t)(v >> 32) != tag) != 0; ++spins) {
-        if (spins > kSpinLimit) {
+        if (spins > a.spin_limit) {
             if (lane == 0) atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_STALL);
             break;
         }
@@ -1262,7 +1266,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
             }
             break;
         }
-        if (spins > kPollLimit) {
+        if (spins > a.poll_limit) {
             if (t == 0) atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_STALL);
             break;
         }
@@ -1305,7 +1309,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
                 lo += (uint32_t)l;
             }
             if (!__syncthreads_or(bad)) break;
-            if (spins > kPollLimit) {
+            if (spins > a.poll_limit) {
                 if (t == 0) atomicOr(&a.ctrl[kCtrlStatus], HATA_DEV_STALL);
                 break;
             }
@@ -1649,7 +1653,10 @@ bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, DecodePlan *p) {
 
 // The last-items-last order gives up the unit-by-unit order that lets a grid
 // larger than the chip make progress, so it is only used when every
-// workgroup of the launch can be resident at once.
+// workgroup of the launch can be resident at once, with kTailHeadroom slots
+// to spare for workgroups of other kernels that may still hold CUs.
+constexpr int kTailHeadroom = 64;
+
 template <int G>
 static hipError_t launch_g(const DecodePlan &p, FusedArgs &a, hipStream_t s) {
     (void)p;
@@ -1658,7 +1665,7 @@ static hipError_t launch_g(const DecodePlan &p, FusedArgs &a, hipStream_t s) {
     if (a.n_chunks > 1 && hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_fused<G>, kThreads, 0) == hipSuccess)
-        a.tails_last = (int64_t)a.n_items <= (int64_t)per_cu * n_cu;
+        a.tails_last = (int64_t)a.n_items + kTailHeadroom <= (int64_t)per_cu * n_cu;
     hipLaunchKernelGGL(k_decode_fused<G>, dim3(a.n_items), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
@@ -1698,6 +1705,14 @@ hipError_t launch_decode(const DecodePlan &p, uint16_t *k_cache, uint16_t *v_cac
     a.span = p.span;
     a.n_chunks = p.n_chunks;
     a.n_items = p.n_items;
+    // Bounds of the waits; HATA_DECODE_WAIT_LIMIT (a test control) lowers
+    // both so that the waits give up and the stall path can be exercised.
+    a.spin_limit = kSpinLimit;
+    a.poll_limit = kPollLimit;
+    if (const char *e = getenv("HATA_DECODE_WAIT_LIMIT")) {
+        const long v = strtol(e, nullptr, 10);
+        if (v >= 0 && v < a.poll_limit) a.spin_limit = a.poll_limit = (int)v;
+    }
     switch (p.G) {
         case 1: return launch_g<1>(p, a, s);
         case 2: return launch_g<2>(p, a, s);

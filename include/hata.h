@@ -79,6 +79,29 @@ typedef enum {
 #define HATA_DEV_STALL 0x10          /* a decode wait timed out: outputs of that call invalid */
 
 /*
+ * Scheduling assumption of the 128-bit decode (hata_decode_attn and
+ * hata_decode_step at n_bits = 128).  The step is one kernel launch whose
+ * workgroups hand results to each other: a work item waits for the query
+ * codes of its (sequence, KV head) unit and, before it selects, for the
+ * histogram counts of every other work item of that unit.  This needs those
+ * other items to be running: workgroups start in block order and a unit's
+ * items (at most 68) fit on the GPU together.  When the whole launch fits on
+ * the GPU with 64 workgroup slots to spare, the items are also reordered for
+ * balance, which needs every workgroup of the launch resident at once.  Both
+ * hold on a GPU that no other kernel occupies while the step runs; kernels
+ * running concurrently (other streams, other processes) that hold many CUs
+ * can break them.  Every wait is bounded, so the launch always ends; if a
+ * wait gave up, HATA_DEV_STALL is set in ctrl[0] and that call's outputs
+ * (out, sel_idx_out, scores_out) are invalid.  The cache itself stays valid
+ * (an appended row, its code and the new length are written as usual).
+ * Recovery: zero-fill the workspace again, clear the status bit, and call
+ * hata_decode_attn (no append) for the outputs.
+ * Test control: the environment variable HATA_DECODE_WAIT_LIMIT, when set
+ * to a number n below the built-in bounds, makes every such wait give up
+ * after n re-reads, so that this path can be exercised.
+ */
+
+/*
  * A key/value cache with its key-code cache, all device memory owned by the
  * caller.  Sequence b, KV head g, position p:
  *   k, v  : bf16  [batch][n_kv_heads][max_ctx][128], row (b, g, p) at

@@ -4,9 +4,8 @@ Bars (per unit (batch, KV head) checked):
   - key codes, query-group Hamming scores and selected indices: bit-exact;
   - attention outputs: max |gpu - oracle| <= 2e-2 (bf16 output, fp32
     accumulation; the oracle is exact double precision).
-Small workloads are checked unit by unit in full; the full-size
-configurations are checked on sampled units, with structural properties
-(selection size, ordering, the -1 tail) on every unit.
+Small and fuzzed workloads are checked unit by unit in full here; the
+full-size configurations, every unit of them, in test_gpu_fullsize.py.
 """
 from __future__ import annotations
 
@@ -173,22 +172,6 @@ def test_step_without_debug_outputs_matches(gpu, spec):
     assert a.cache.status() == 0 and b.cache.status() == 0
 
 
-def test_config3_step_without_debug_outputs(gpu):
-    # The benchmarked call (no debug outputs) at full size, outputs against
-    # the oracle on sampled units.
-    spec = synth.config(3)
-    wl = GpuWorkload(spec, gpu, extra_ctx=2)
-    out, _, _ = wl.step(debug=False)
-    torch.cuda.synchronize()
-    assert wl.cache.status() == 0
-    G = spec.G
-    for (b, kv) in [(0, 0), (1, 6), (3, 3)]:
-        _say(f"[parity] cfg3 no-debug: oracle unit {(b, kv)}")
-        ref = oracle_unit(spec, wl, b, kv)
-        o = out[b, kv * G:(kv + 1) * G].float().cpu().numpy().astype(np.float64)
-        assert np.abs(o - ref["out"]).max() <= OUT_TOL
-
-
 def test_many_units_dense_and_sparse(gpu):
     # 512 units, so each unit has a single split of up to 3000 keys; half the
     # sequences select everything (dense), which overflows the LDS index
@@ -218,23 +201,3 @@ def test_determinism(gpu):
 
 def bf16_bits_t(t):
     return t.view(torch.int16)
-
-
-@pytest.mark.parametrize("cfg,units", [
-    (2, [(0, 0), (7, 7), (3, 4)]),
-    (3, [(0, 0), (3, 7), (2, 5)]),
-])
-def test_full_config_sampled(gpu, cfg, units):
-    run_spec(synth.config(cfg), gpu, units=units)
-
-
-def test_config4_sampled(gpu):
-    run_spec(synth.config(4), gpu, units=[(0, 0), (0, 5)])
-
-
-def test_config5_sampled(gpu):
-    spec = synth.config(5)
-    lens = spec.lengths
-    bmax = int(np.argmax(lens))
-    bmin = int(np.argmin(lens))
-    run_spec(spec, gpu, units=[(bmax, 0), (bmin, 7), (17, 3)])

@@ -29,7 +29,11 @@ class GpuWorkload:
     """Device state of one synthetic decode workload."""
 
     def __init__(self, spec: synth.Spec, device, extra_ctx: int = 0, units=None,
-                 encode_prefill: bool = True, offload: bool = False, n_bits: int = 128):
+                 encode_prefill: bool = True, offload: bool = False, n_bits: int = 128,
+                 unit_hook=None):
+        """unit_hook(b, kv, k, v), if given, sees each unit's prefilled rows
+        (host bf16 bits) as they are generated, so a caller can run the oracle
+        on the very bytes uploaded without generating them twice."""
         self.spec = spec
         self.device = device
         B, Hq, Hkv = spec.B, spec.Hq, spec.Hkv
@@ -50,6 +54,11 @@ class GpuWorkload:
                     v = synth.gen_unit_v(spec, b, kv)
                     self.cache.k[b, kv, :n_pre] = bf16_dev(k, device)
                     self.cache.v[b, kv, :n_pre] = bf16_dev(v, device)
+                    if unit_hook is not None:
+                        unit_hook(b, kv, k, v)
+                elif unit_hook is not None:
+                    empty = np.zeros((0, 128), dtype=np.uint16)
+                    unit_hook(b, kv, empty, empty)
         self.w = torch.from_numpy(self.w_host).to(device)
         self.q = bf16_dev(self.q_host, device)
         self.k_new = bf16_dev(self.new_host[0], device)
