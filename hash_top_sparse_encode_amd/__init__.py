@@ -10,7 +10,8 @@ there is no fallback of any kind.
 Names mirror the C ABI:
   hata_encode_keys (also the other code lengths, through
   hata_encode_keys_nbits), hata_append, hata_decode_workspace_bytes,
-  hata_decode_attn, hata_decode_step, hata_recall_workspace_bytes,
+  hata_decode_attn, hata_decode_step, hata_decode_step_static (no workspace),
+  hata_recall_workspace_bytes,
   hata_exact_topk_recall, hata_status_string
 plus ``HataCache``, a holder of the caller-owned cache tensors.
 """
@@ -41,6 +42,8 @@ HATA_ERR_INVALID_ARG = 1
 HATA_ERR_UNSUPPORTED = 2
 HATA_ERR_WORKSPACE = 3
 HATA_ERR_HIP = 4
+HATA_ERR_SCRATCH_LIMIT = 5
+STATIC_SCRATCH_BYTES = 32 << 20
 
 HATA_DEV_APPEND_OVERFLOW = 0x1
 HATA_DEV_BAD_LENGTH = 0x2
@@ -51,7 +54,7 @@ HATA_DEV_STALL = 0x10
 EXPORTED_SYMBOLS = ("hata_encode_keys", "hata_encode_keys_nbits", "hata_append",
                     "hata_decode_workspace_bytes", "hata_decode_attn", "hata_decode_step",
                     "hata_recall_workspace_bytes", "hata_exact_topk_recall",
-                    "hata_status_string")
+                    "hata_status_string", "hata_decode_step_static")
 
 
 class _CCache(ctypes.Structure):
@@ -96,6 +99,9 @@ def lib() -> ctypes.CDLL:
         L.hata_decode_step.argtypes = [ctypes.POINTER(_CCache), vp, vp, vp, vp, vp, i32, vp, vp,
                                        sz, vp, vp, vp]
         L.hata_decode_step.restype = ctypes.c_int
+        L.hata_decode_step_static.argtypes = [ctypes.POINTER(_CCache), vp, vp, vp, vp, vp, i32,
+                                              vp, vp, vp, vp]
+        L.hata_decode_step_static.restype = ctypes.c_int
         L.hata_recall_workspace_bytes.argtypes = [ctypes.POINTER(_CCache)]
         L.hata_recall_workspace_bytes.restype = sz
         L.hata_exact_topk_recall.argtypes = [ctypes.POINTER(_CCache), vp, vp, i32, vp, vp, vp,
@@ -340,6 +346,32 @@ def hata_decode_step(cache: HataCache, k_new: torch.Tensor, v_new: torch.Tensor,
                                 out.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                 _ptr(sel_idx_out), _ptr(scores_out), _stream(stream))
     _check("hata_decode_step", st)
+    return out
+
+
+def hata_decode_step_static(cache: HataCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                            q: torch.Tensor, w_h: torch.Tensor, topk: torch.Tensor, k_max: int,
+                            out: torch.Tensor, sel_idx_out: torch.Tensor = None,
+                            scores_out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """hata_decode_step on the library's static scratch (no workspace, no
+    allocation; n_bits = 128; calls on one GPU must not overlap)."""
+    B, Hq, Hkv = cache.batch, cache.n_q_heads, cache.n_kv_heads
+    _need(k_new, "k_new", torch.bfloat16, B * Hkv * HEAD_DIM)
+    _need(v_new, "v_new", torch.bfloat16, B * Hkv * HEAD_DIM)
+    _need(q, "q", torch.bfloat16, B * Hq * HEAD_DIM)
+    _need(out, "out", torch.bfloat16, B * Hq * HEAD_DIM)
+    _need(w_h, "w_h", torch.float32, Hkv * HEAD_DIM * cache.n_bits)
+    _need(topk, "topk", torch.int32, B)
+    if sel_idx_out is not None:
+        _need(sel_idx_out, "sel_idx_out", torch.int32, B * Hkv * int(k_max))
+    if scores_out is not None:
+        _need(scores_out, "scores_out", torch.int16, B * Hkv * cache.max_ctx)
+    c = cache.c_struct()
+    st = lib().hata_decode_step_static(ctypes.byref(c), k_new.data_ptr(), v_new.data_ptr(),
+                                       q.data_ptr(), w_h.data_ptr(), topk.data_ptr(), int(k_max),
+                                       out.data_ptr(), _ptr(sel_idx_out), _ptr(scores_out),
+                                       _stream(stream))
+    _check("hata_decode_step_static", st)
     return out
 
 

@@ -45,6 +45,8 @@ const char *hata_status_string(hata_status s) {
             return "unsupported shape (head_dim 128, n_bits in {32, 64, 128, 256}, G in {1, 2, 4, 8})";
         case HATA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case HATA_ERR_HIP: return "HIP launch failed";
+        case HATA_ERR_SCRATCH_LIMIT:
+            return "the cache needs more decode scratch than the allocation-free entry point holds";
     }
     return "unknown status";
 }
@@ -173,6 +175,25 @@ hata_status hata_decode_step(const hata_cache *c, const uint16_t *k_new, const u
     if (!k_new || !v_new) return HATA_ERR_INVALID_ARG;
     return decode_common(c, k_new, v_new, q, w_h, topk, k_max, out, workspace, ws_bytes,
                          sel_idx_out, scores_out, stream);
+}
+
+hata_status hata_decode_step_static(const hata_cache *c, const uint16_t *k_new,
+                                    const uint16_t *v_new, const uint16_t *q, const float *w_h,
+                                    const int32_t *topk, int32_t k_max, uint16_t *out,
+                                    int32_t *sel_idx_out, uint16_t *scores_out, void *stream) {
+    hata_status st = check_cache(c);
+    if (st != HATA_OK) return st;
+    if (c->n_bits != kBits) return HATA_ERR_UNSUPPORTED;
+    if (!k_new || !v_new || !q || !w_h || !topk || !out || k_max < 0) return HATA_ERR_INVALID_ARG;
+    if (!aligned16(q)) return HATA_ERR_INVALID_ARG;
+    DecodePlan p;
+    if (!make_decode_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, &p))
+        return HATA_ERR_UNSUPPORTED;
+    if (p.used > kStaticScratchBytes) return HATA_ERR_SCRATCH_LIMIT;
+    hipError_t e = launch_decode_static(p, c->k, c->v, c->codes, c->seq_len, c->ctrl, k_new, v_new,
+                                        q, w_h, topk, k_max, out, sel_idx_out, scores_out,
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
 }
 
 size_t hata_recall_workspace_bytes(const hata_cache *c) {

@@ -65,6 +65,8 @@
 // back / invalidate whole L2s instead, which costs more than the step.
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "device_util.h"
 #include "hata_internal.h"
 #include "../../include/hata.h"
@@ -1645,6 +1647,7 @@ bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, DecodePlan *p) {
     d.off_part_o = off;
     off = align256(off + (size_t)units * d.n_chunks * G * kHeadDim * 4);
     d.off_scores = off;
+    d.used = d.span <= kSpanUnit ? off : align256(off + (size_t)units * d.sstride * 2);
     off = align256(off + (size_t)units * d.sstride * 2);
     d.total = off;
     *p = d;
@@ -1720,6 +1723,71 @@ hipError_t launch_decode(const DecodePlan &p, uint16_t *k_cache, uint16_t *v_cac
         case 8: return launch_g<8>(p, a, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+}  // namespace hata
+
+// ---------------------------------------------------------------- allocation-free form
+
+namespace hata {
+
+// The scratch of hata_decode_step_static.  In host code `scratch` only names
+// the symbol; its device address (one per GPU) comes from
+// hipGetSymbolAddress and is the only form passed to kernels or copies.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_addr[kMaxDevices];  // set once per device, never changed
+
+hipError_t scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_addr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev] = ptr;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
+}
+
+// Zero n 16-byte words at p (a fill kernel rather than hipMemsetAsync, so a
+// captured graph replays it correctly).
+__global__ __launch_bounds__(256) void k_zero16(uint4 *p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+}  // namespace
+
+hipError_t launch_decode_static(const DecodePlan &p, uint16_t *k_cache, uint16_t *v_cache,
+                                uint32_t *codes, int32_t *seq_len, int32_t *ctrl,
+                                const uint16_t *k_new, const uint16_t *v_new, const uint16_t *q,
+                                const float *w, const int32_t *topk, int k_max, uint16_t *out,
+                                int32_t *sel_idx_out, uint16_t *scores_out, hipStream_t s) {
+    if (p.used > kStaticScratchBytes) return hipErrorInvalidValue;
+    void *ws = nullptr;
+    hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+    // The launch generations, tagged code words, unit histograms and
+    // cumulative span histograms must start at zero (they lie in front of
+    // the split partials); the array keeps whatever the previous call on this
+    // GPU left, possibly under another cache's layout.
+    const int64_t n16 = (int64_t)(p.off_part_ml / 16);
+    const int64_t blocks = n16 / 256 + 1 < 1024 ? n16 / 256 + 1 : 1024;
+    hipLaunchKernelGGL(k_zero16, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint4 *>(ws), n16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_decode(p, k_cache, v_cache, codes, seq_len, ctrl, k_new, v_new, q, w, topk, k_max,
+                         out, ws, sel_idx_out, scores_out, s);
 }
 
 }  // namespace hata

@@ -32,6 +32,9 @@ struct DecodePlan {
     int64_t sstride = 0; // score row stride (elements) in the workspace
     size_t off_gen = 0, off_qtag = 0, off_unit_hist = 0, off_chunk_hist = 0, off_part_ml = 0,
            off_part_o = 0, off_scores = 0, total = 0;
+    // Bytes actually touched: the score rows are used only when a span is
+    // longer than the 8192 keys an item keeps in LDS.
+    size_t used = 0;
 };
 
 bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, DecodePlan *p);
@@ -68,5 +71,19 @@ hipError_t launch_decode(const DecodePlan &p, uint16_t *k_cache, uint16_t *v_cac
                          const uint16_t *k_new, const uint16_t *v_new, const uint16_t *q,
                          const float *w, const int32_t *topk, int k_max, uint16_t *out, void *ws,
                          int32_t *sel_idx_out, uint16_t *scores_out, hipStream_t s);
+
+// The allocation-free decode step's scratch: a static device array of
+// kStaticScratchBytes per GPU inside the library.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+
+// hata_decode_step on that scratch: looks its address up once per device,
+// clears the sections that must start at zero, then launches as
+// launch_decode.  hipErrorInvalidValue if the plan needs more than the
+// scratch holds.
+hipError_t launch_decode_static(const DecodePlan &p, uint16_t *k_cache, uint16_t *v_cache,
+                                uint32_t *codes, int32_t *seq_len, int32_t *ctrl,
+                                const uint16_t *k_new, const uint16_t *v_new, const uint16_t *q,
+                                const float *w, const int32_t *topk, int k_max, uint16_t *out,
+                                int32_t *sel_idx_out, uint16_t *scores_out, hipStream_t s);
 
 }  // namespace hata

@@ -67,7 +67,8 @@ typedef enum {
     HATA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad stride ... */
     HATA_ERR_UNSUPPORTED = 2, /* head_dim != 128, n_bits not in {32,64,128,256}, G not in {1,2,4,8} */
     HATA_ERR_WORKSPACE = 3,   /* workspace null or smaller than required */
-    HATA_ERR_HIP = 4          /* a HIP launch failed */
+    HATA_ERR_HIP = 4,         /* a HIP launch failed */
+    HATA_ERR_SCRATCH_LIMIT = 5 /* hata_decode_step_static: the cache needs more than its scratch */
 } hata_status;
 
 /* Device status bits, OR-ed into ctrl[0] by kernels (sticky until the
@@ -253,6 +254,30 @@ hata_status hata_decode_step(const hata_cache *c, const uint16_t *k_new, const u
                              const uint16_t *q, const float *w_h, const int32_t *topk,
                              int32_t k_max, uint16_t *out, void *workspace, size_t ws_bytes,
                              int32_t *sel_idx_out, uint16_t *scores_out, void *stream);
+
+/*
+ * hata_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory or hand one in: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The call allocates
+ * nothing; the decode's scratch is a static device array of
+ * HATA_STATIC_SCRATCH_BYTES inside the library (one per GPU, held until the
+ * process ends; its address is looked up once per device on the first call
+ * there).  Each call first clears the parts of that array that must start at
+ * zero (a small fill kernel on `stream`), so calls may alternate between
+ * caches of any shape; calls that overlap in time on one GPU (other streams,
+ * other threads) share the array and race -- order them.
+ * n_bits must be 128.  The array holds the decode workspace minus the score
+ * rows of items longer than 8192 keys; caches whose layout needs more (for
+ * example 64 sequences x 8 KV heads beyond 64K context) return
+ * HATA_ERR_SCRATCH_LIMIT before anything is enqueued.  Arguments, results
+ * and the other errors as hata_decode_step; the stall recovery (see the
+ * scheduling note above) needs no workspace fill: the next call clears it.
+ */
+#define HATA_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+hata_status hata_decode_step_static(const hata_cache *c, const uint16_t *k_new,
+                                    const uint16_t *v_new, const uint16_t *q, const float *w_h,
+                                    const int32_t *topk, int32_t k_max, uint16_t *out,
+                                    int32_t *sel_idx_out, uint16_t *scores_out, void *stream);
 
 /* Bytes of device workspace hata_exact_topk_recall needs for this cache
  * (depends on batch, heads and max_ctx only; about 17 bytes per position and

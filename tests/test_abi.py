@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert hata.hata_status_string(s)
     assert "unknown" in hata.hata_status_string(99)
 
@@ -186,3 +186,26 @@ def test_recall_workspace_plan(B, Hq, Hkv, N):
     assert n % 256 == 0
     assert hata.lib().hata_recall_workspace_bytes(ctypes.byref(cache(head_dim=64))) == 0
     assert hata.lib().hata_recall_workspace_bytes(None) == 0
+
+
+def static_step(c, k_new=FAKE, v_new=FAKE, q=FAKE, w=FAKE, topk=FAKE, k_max=16, out=FAKE):
+    return hata.lib().hata_decode_step_static(ctypes.byref(c), k_new, v_new, q, w, topk, k_max,
+                                              out, None, None, None)
+
+
+def test_static_step_validation():
+    # Every failure below is decided on the host before anything is enqueued
+    # (and before the scratch's address is looked up).
+    E = hata
+    assert static_step(cache(n_bits=64)) == E.HATA_ERR_UNSUPPORTED
+    assert static_step(cache(head_dim=64)) == E.HATA_ERR_UNSUPPORTED
+    assert static_step(cache(k=0)) == E.HATA_ERR_INVALID_ARG
+    assert static_step(cache(), k_new=0) == E.HATA_ERR_INVALID_ARG
+    assert static_step(cache(), v_new=0) == E.HATA_ERR_INVALID_ARG
+    assert static_step(cache(), q=FAKE + 8) == E.HATA_ERR_INVALID_ARG
+    assert static_step(cache(), k_max=-1) == E.HATA_ERR_INVALID_ARG
+    # 64 sequences x 8 KV heads at 200K context: the span histograms alone
+    # take 512 units x 25 items x 513 bins x 8 B = 52 MB > the 32 MiB scratch
+    big = cache(batch=64, n_q_heads=32, n_kv_heads=8, max_ctx=200000)
+    assert static_step(big) == E.HATA_ERR_SCRATCH_LIMIT
+    assert "scratch" in hata.hata_status_string(E.HATA_ERR_SCRATCH_LIMIT)
