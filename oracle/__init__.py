@@ -26,6 +26,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hata_oracle.c")
+_SRC_TRAIN = os.path.join(_HERE, "hash_train_oracle.c")
 # HATA_ORACLE_LIB names another build of hata_oracle.c (the sanitizer test
 # loads an ASan/UBSan build this way).
 _LIB_PATH = os.environ.get("HATA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
@@ -40,7 +41,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
-                               "-fno-fast-math", _SRC, "-o", tmp, "-lm"])
+                               "-fno-fast-math", _SRC, _SRC_TRAIN, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -62,6 +63,14 @@ def lib():
         L.oracle_attend.restype = ci
         L.oracle_exact_topk.argtypes = [vp, vp, i64, ci, i64, i64, vp]
         L.oracle_exact_topk.restype = i64
+        dbl = ctypes.c_double
+        L.oracle_hash_labels.argtypes = [vp, ci, vp, ci, ci, vp]
+        L.oracle_hash_labels.restype = ci
+        L.oracle_hash_loss_grad.argtypes = [vp, ci, vp, ci, ci, vp, ci, vp, dbl, dbl, dbl, dbl,
+                                            vp, vp]
+        L.oracle_hash_loss_grad.restype = ci
+        L.oracle_adam.argtypes = [vp, vp, vp, vp, i64, ci, dbl, dbl, dbl, dbl]
+        L.oracle_adam.restype = None
         _lib = L
     return _lib
 
@@ -222,3 +231,62 @@ def recall_unit(q_group: np.ndarray, K: np.ndarray, k: int, sel: np.ndarray,
     exact = [exact_topk(q_group[h], K, k) for h in range(q_group.shape[0])]
     return {"exact": exact, "overlap": [overlap(sel, e) for e in exact],
             "tie": tie_bucket(scores, k)}
+
+
+# ------------------------------------------------------------ hash training
+# The learning-to-hash objective that produces W_H (hash_train_oracle.c):
+# relaxed codes 2 Sigmoid(sigma x W_H) - 1, labels from exact qk scores, a
+# similarity-weighted Hamming loss plus bit-balance and uncorrelation
+# penalties, Adam updates.
+
+SIGMA, EPSILON, ETA, LAMBDA = 0.1, 0.01, 2.0, 1.0
+
+
+def hash_labels(q: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """Training labels [n_q][n_k] (float32) of queries q [n_q][d] and keys
+    k [n_k][d] (bf16): per query, the top ceil(n_k / 10) keys by exact q.k
+    (lower index first among equal scores) get 20 - 19 t / (m - 1) by rank t,
+    the rest -1."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    nq, d = q.shape
+    nk = k.shape[0]
+    assert k.shape[1] == d
+    out = np.zeros((nq, nk), dtype=np.float32)
+    if lib().oracle_hash_labels(q.ctypes.data, nq, k.ctypes.data, nk, d, out.ctypes.data) != 0:
+        raise MemoryError("oracle_hash_labels")
+    return out
+
+
+def hash_loss_grad(q: np.ndarray, k: np.ndarray, w: np.ndarray, labels: np.ndarray,
+                   sigma=SIGMA, epsilon=EPSILON, eta=ETA, lam=LAMBDA):
+    """(loss[4] = (L, L_sim, L_bal, L_unc), dL/dW [d][r]) in double, at W
+    (fp32 [d][r]) for the batch (q [n_q][d], k [n_k][d] bf16; labels
+    [n_q][n_k] fp32)."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    labels = np.ascontiguousarray(labels, dtype=np.float32)
+    nq, d = q.shape
+    nk = k.shape[0]
+    r = w.shape[1]
+    assert w.shape[0] == d and labels.shape == (nq, nk)
+    loss = np.zeros(4, dtype=np.float64)
+    grad = np.zeros((d, r), dtype=np.float64)
+    rc = lib().oracle_hash_loss_grad(q.ctypes.data, nq, k.ctypes.data, nk, d, w.ctypes.data, r,
+                                     labels.ctypes.data, float(sigma), float(epsilon), float(eta),
+                                     float(lam), loss.ctypes.data, grad.ctypes.data)
+    if rc != 0:
+        raise MemoryError("oracle_hash_loss_grad")
+    return loss, grad
+
+
+def adam(w, m, v, g, step: int, lr: float, b1=0.9, b2=0.999, e=1e-8):
+    """One Adam step in double; returns the new (w, m, v)."""
+    w = np.array(w, dtype=np.float64)
+    m = np.array(m, dtype=np.float64)
+    v = np.array(v, dtype=np.float64)
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    lib().oracle_adam(w.ctypes.data, m.ctypes.data, v.ctypes.data, g.ctypes.data, w.size,
+                      int(step), float(lr), float(b1), float(b2), float(e))
+    return w, m, v
