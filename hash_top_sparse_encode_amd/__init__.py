@@ -54,7 +54,9 @@ HATA_DEV_STALL = 0x10
 EXPORTED_SYMBOLS = ("hata_encode_keys", "hata_encode_keys_nbits", "hata_append",
                     "hata_decode_workspace_bytes", "hata_decode_attn", "hata_decode_step",
                     "hata_recall_workspace_bytes", "hata_exact_topk_recall",
-                    "hata_status_string", "hata_decode_step_static")
+                    "hata_status_string", "hata_decode_step_static",
+                    "hata_hash_train_workspace_bytes", "hata_hash_labels",
+                    "hata_hash_train_step")
 
 
 class _CCache(ctypes.Structure):
@@ -71,6 +73,18 @@ class _CCache(ctypes.Structure):
         ("n_bits", ctypes.c_int32),
         ("max_ctx", ctypes.c_int64),
     ]
+
+
+class TrainParams(ctypes.Structure):
+    """hata_train_params: the objective's constants (the pages' values by
+    default) and Adam's."""
+    _fields_ = [("sigma", ctypes.c_float), ("epsilon", ctypes.c_float), ("eta", ctypes.c_float),
+                ("lambda_", ctypes.c_float), ("lr", ctypes.c_float), ("beta1", ctypes.c_float),
+                ("beta2", ctypes.c_float), ("adam_eps", ctypes.c_float)]
+
+    def __init__(self, sigma=0.1, epsilon=0.01, eta=2.0, lambda_=1.0, lr=0.01, beta1=0.9,
+                 beta2=0.999, adam_eps=1e-8):
+        super().__init__(sigma, epsilon, eta, lambda_, lr, beta1, beta2, adam_eps)
 
 
 _lib = None
@@ -102,6 +116,13 @@ def lib() -> ctypes.CDLL:
         L.hata_decode_step_static.argtypes = [ctypes.POINTER(_CCache), vp, vp, vp, vp, vp, i32,
                                               vp, vp, vp, vp]
         L.hata_decode_step_static.restype = ctypes.c_int
+        L.hata_hash_train_workspace_bytes.argtypes = [i32, i32, i32]
+        L.hata_hash_train_workspace_bytes.restype = sz
+        L.hata_hash_labels.argtypes = [vp, i32, vp, i32, vp, vp]
+        L.hata_hash_labels.restype = ctypes.c_int
+        L.hata_hash_train_step.argtypes = [vp, i32, vp, i32, vp, i32, vp, vp, vp, i32,
+                                           ctypes.POINTER(TrainParams), vp, vp, vp, sz, vp]
+        L.hata_hash_train_step.restype = ctypes.c_int
         L.hata_recall_workspace_bytes.argtypes = [ctypes.POINTER(_CCache)]
         L.hata_recall_workspace_bytes.restype = sz
         L.hata_exact_topk_recall.argtypes = [ctypes.POINTER(_CCache), vp, vp, i32, vp, vp, vp,
@@ -420,3 +441,68 @@ def hata_exact_topk_recall(cache: HataCache, q: torch.Tensor, topk: torch.Tensor
                                       workspace.numel(), _stream(stream))
     _check("hata_exact_topk_recall", st)
     return overlap_out, tie_out
+
+
+# ------------------------------------------------------------ hash training
+
+
+def hata_hash_train_workspace_bytes(n_q: int, n_k: int, n_bits: int) -> int:
+    return int(lib().hata_hash_train_workspace_bytes(int(n_q), int(n_k), int(n_bits)))
+
+
+def hata_hash_labels(q: torch.Tensor, k: torch.Tensor, labels: torch.Tensor = None,
+                     stream=None) -> torch.Tensor:
+    """Training labels [n_q][n_k] (fp32) of queries q [n_q][128] and keys
+    k [n_k][128] (bf16): top ceil(n_k / 10) keys by exact q.k per query,
+    linearly decayed over [20, 1]; the rest -1."""
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16)
+    n_q, n_k = q.numel() // HEAD_DIM, k.numel() // HEAD_DIM
+    if labels is None:
+        labels = torch.empty((n_q, n_k), dtype=torch.float32, device=q.device)
+    _need(labels, "labels", torch.float32, n_q * n_k)
+    st = lib().hata_hash_labels(q.data_ptr(), n_q, k.data_ptr(), n_k, labels.data_ptr(),
+                                _stream(stream))
+    _check("hata_hash_labels", st)
+    return labels
+
+
+class HashTrainer:
+    """Device state of W_H training: the weights [128][n_bits], Adam's moments,
+    a workspace for batches of n_q queries and n_k keys, the step count."""
+
+    def __init__(self, w_init: torch.Tensor, n_q: int, n_k: int, params: TrainParams = None):
+        _need(w_init, "w_init", torch.float32)
+        self.n_bits = w_init.numel() // HEAD_DIM
+        self.w = w_init.clone().reshape(HEAD_DIM, self.n_bits)
+        self.m = torch.zeros_like(self.w)
+        self.v = torch.zeros_like(self.w)
+        self.n_q, self.n_k = int(n_q), int(n_k)
+        n = hata_hash_train_workspace_bytes(self.n_q, self.n_k, self.n_bits)
+        if n == 0:
+            raise ValueError("unsupported training batch shape")
+        self.ws = torch.empty(n, dtype=torch.uint8, device=w_init.device)
+        self.loss = torch.zeros(4, dtype=torch.float32, device=w_init.device)
+        self.params = params if params is not None else TrainParams()
+        self.steps = 0
+
+    def step(self, q: torch.Tensor, k: torch.Tensor, labels: torch.Tensor, update: bool = True,
+             grad_out: torch.Tensor = None, stream=None) -> torch.Tensor:
+        """One training step (hata_hash_train_step); returns the loss tensor
+        (L, L_sim, L_bal, L_unc) at the weights before the update."""
+        _need(q, "q", torch.bfloat16, self.n_q * HEAD_DIM)
+        _need(k, "k", torch.bfloat16, self.n_k * HEAD_DIM)
+        _need(labels, "labels", torch.float32, self.n_q * self.n_k)
+        if grad_out is not None:
+            _need(grad_out, "grad_out", torch.float32, HEAD_DIM * self.n_bits)
+        step = self.steps + 1 if update else 0
+        st = lib().hata_hash_train_step(q.data_ptr(), self.n_q, k.data_ptr(), self.n_k,
+                                        labels.data_ptr(), self.n_bits, self.w.data_ptr(),
+                                        self.m.data_ptr(), self.v.data_ptr(), step,
+                                        ctypes.byref(self.params), self.loss.data_ptr(),
+                                        _ptr(grad_out), self.ws.data_ptr(), self.ws.numel(),
+                                        _stream(stream))
+        _check("hata_hash_train_step", st)
+        if update:
+            self.steps += 1
+        return self.loss

@@ -10,7 +10,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libhata.so")
 
-SOURCES = ["api.cpp", "encode_exact.hip", "encode_mfma.hip", "decode.hip", "recall.hip", "bits.hip"]
+SOURCES = ["api.cpp", "encode_exact.hip", "encode_mfma.hip", "decode.hip", "recall.hip", "bits.hip",
+           "train.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -35,7 +36,7 @@ def _compile(src: str) -> str:
 def build() -> str:
     """Compile every HIP source and link libhata.so (always recompiles)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(min(len(SOURCES), 6)) as ex:
+    with ThreadPoolExecutor(min(len(SOURCES), 8)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]

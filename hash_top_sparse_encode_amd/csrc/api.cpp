@@ -196,6 +196,40 @@ hata_status hata_decode_step_static(const hata_cache *c, const uint16_t *k_new,
     return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
 }
 
+size_t hata_hash_train_workspace_bytes(int32_t n_q, int32_t n_k, int32_t n_bits) {
+    TrainPlan p;
+    return make_train_plan(n_q, n_k, n_bits, &p) ? p.total : 0;
+}
+
+hata_status hata_hash_labels(const uint16_t *q, int32_t n_q, const uint16_t *k, int32_t n_k,
+                             float *labels, void *stream) {
+    if (n_q < 0 || n_k < 0 || n_k > kMaxLabelKeys) return HATA_ERR_INVALID_ARG;
+    if (n_q == 0 || n_k == 0) return HATA_OK;
+    if (!q || !k || !labels) return HATA_ERR_INVALID_ARG;
+    hipError_t e = launch_hash_labels(q, n_q, k, n_k, labels, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
+}
+
+hata_status hata_hash_train_step(const uint16_t *q, int32_t n_q, const uint16_t *k, int32_t n_k,
+                                 const float *labels, int32_t n_bits, float *w_h, float *adam_m,
+                                 float *adam_v, int32_t step, const hata_train_params *params,
+                                 float *loss_out, float *grad_out, void *workspace,
+                                 size_t ws_bytes, void *stream) {
+    if (n_bits != 32 && n_bits != 64 && n_bits != 128 && n_bits != 256) return HATA_ERR_UNSUPPORTED;
+    if (!q || !k || !labels || !w_h || !params || !loss_out || step < 0) return HATA_ERR_INVALID_ARG;
+    if (step > 0 && (!adam_m || !adam_v)) return HATA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k)) return HATA_ERR_INVALID_ARG;
+    TrainPlan p;
+    if (!make_train_plan(n_q, n_k, n_bits, &p)) return HATA_ERR_INVALID_ARG;
+    if (!workspace || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return HATA_ERR_WORKSPACE;
+    const TrainHyper hp{params->sigma, params->epsilon, params->eta, params->lambda,
+                        params->lr, params->beta1, params->beta2, params->adam_eps};
+    hipError_t e = launch_hash_train_step(p, q, k, labels, w_h, adam_m, adam_v, step, hp, loss_out,
+                                          grad_out, workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
+}
+
 size_t hata_recall_workspace_bytes(const hata_cache *c) {
     if (!c) return 0;
     if (c->head_dim != kHeadDim || !supported_bits(c->n_bits)) return 0;

@@ -72,6 +72,31 @@ hipError_t launch_decode(const DecodePlan &p, uint16_t *k_cache, uint16_t *v_cac
                          const float *w, const int32_t *topk, int k_max, uint16_t *out, void *ws,
                          int32_t *sel_idx_out, uint16_t *scores_out, hipStream_t s);
 
+// ---- training of W_H (train.hip) ----
+
+constexpr int kMaxLabelKeys = 4096;  // keys per label batch (sorted in LDS)
+
+struct TrainPlan {
+    int n_q = 0, n_k = 0, n = 0, r = 0, n_parts = 0;
+    size_t off_x = 0, off_h = 0, off_slope = 0, off_sb = 0, off_sa = 0, off_rs = 0, off_cs = 0,
+           off_e = 0, off_mu = 0, off_gy = 0, off_grad = 0, off_colpart = 0, off_losspart = 0,
+           total = 0;
+};
+
+struct TrainHyper {
+    float sigma, epsilon, eta, lambda, lr, beta1, beta2, adam_eps;
+};
+
+bool make_train_plan(int n_q, int n_k, int n_bits, TrainPlan *p);
+
+hipError_t launch_hash_labels(const uint16_t *q, int n_q, const uint16_t *k, int n_k, float *labels,
+                              hipStream_t s);
+
+hipError_t launch_hash_train_step(const TrainPlan &p, const uint16_t *q, const uint16_t *k,
+                                  const float *labels, float *w, float *adam_m, float *adam_v,
+                                  int step, const TrainHyper &hp, float *loss_out, float *grad_out,
+                                  void *ws, hipStream_t s);
+
 // The allocation-free decode step's scratch: a static device array of
 // kStaticScratchBytes per GPU inside the library.
 constexpr size_t kStaticScratchBytes = (size_t)32 << 20;

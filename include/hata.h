@@ -324,6 +324,77 @@ hata_status hata_exact_topk_recall(const hata_cache *c, const uint16_t *q, const
                                    int32_t *tie_out, int32_t *exact_idx_out, void *workspace,
                                    size_t ws_bytes, void *stream);
 
+/*
+ * Training of the hash projection W_H: the learning-to-hash objective of the
+ * HATA review ("What carries the argument": the relaxed code
+ * h(x) = 2 Sigmoid(sigma x W_H) - 1 trained to minimise a similarity-weighted
+ * Hamming distance between query and key codes plus bit-balance and
+ * uncorrelation penalties; "Assumptions & free parameters": sigma = 0.1 and
+ * the weights epsilon = 0.01, eta = 2.0, lambda = 1.0; the labels as its
+ * circularity check restates them: the top 10 % of a query's keys by qk
+ * score positive with labels decaying linearly over [1, 20], the rest -1).
+ * The pages do not print the equations; the forms used (also in the oracle):
+ *   L_sim = (1 / n_q) sum_j sum_i s_ji |h(q_j) - h(k_i)|^2 / 4,
+ *   L_bal = sum_c (mean over the batch's n = n_q + n_k codes of bit c)^2,
+ *   L_unc = |H^T H / n - I|_F^2 (H the n x r relaxed codes),
+ *   L = epsilon L_sim + eta L_bal + lambda L_unc, and Adam updates.
+ */
+typedef struct {
+    float sigma;    /* sigmoid scale of the relaxed code, 0.1 */
+    float epsilon;  /* weight of L_sim, 0.01 */
+    float eta;      /* weight of L_bal, 2.0 */
+    float lambda;   /* weight of L_unc, 1.0 */
+    float lr;       /* Adam step size */
+    float beta1, beta2, adam_eps; /* Adam constants, e.g. 0.9, 0.999, 1e-8 */
+} hata_train_params;
+
+#define HATA_MAX_LABEL_KEYS 4096
+
+/* Bytes of device workspace hata_hash_train_step needs (0 for unsupported
+ * sizes: n_q and n_k must be positive multiples of 32, n_bits in
+ * {32, 64, 128, 256}). */
+size_t hata_hash_train_workspace_bytes(int32_t n_q, int32_t n_k, int32_t n_bits);
+
+/*
+ * Training labels of a batch.  q: device bf16 [n_q][128]; k: device bf16
+ * [n_k][128] with n_k <= HATA_MAX_LABEL_KEYS; labels: device fp32
+ * [n_q][n_k], fully overwritten.  For query j the keys are ranked by
+ * z = q_j . k_i, a sequential double sum over d = 0..127 (bf16 products are
+ * exact in double), larger z first and the lower index first among equal z;
+ * with m = ceil(n_k / 10) the key of rank t < m gets 20 - 19 t / (m - 1)
+ * (20 if m = 1), computed in double and rounded to float; every other key -1.
+ * Inputs must be finite.  Errors: HATA_ERR_INVALID_ARG, HATA_ERR_HIP.
+ */
+hata_status hata_hash_labels(const uint16_t *q, int32_t n_q, const uint16_t *k, int32_t n_k,
+                             float *labels, void *stream);
+
+/*
+ * One training step of W_H on a batch (all device pointers, 16-byte
+ * aligned q and k):
+ *   q, k      bf16 [n_q][128], [n_k][128]; n_q, n_k positive multiples of 32;
+ *   labels    fp32 [n_q][n_k] (hata_hash_labels, or any labels);
+ *   w_h       fp32 [128][n_bits], the weights; updated in place when step >= 1;
+ *   adam_m, adam_v fp32 [128][n_bits], Adam's moments, zero before step 1
+ *             (may be NULL when step = 0);
+ *   step      0: loss and gradient only; t >= 1: then the t-th Adam update
+ *             (bias corrections 1 - beta^t);
+ *   params    host pointer to the hyperparameters;
+ *   loss_out  fp32 [4]: (L, L_sim, L_bal, L_unc) at the weights before the
+ *             update;
+ *   grad_out  optional fp32 [128][n_bits]: dL/dW_H at those weights;
+ *   workspace >= hata_hash_train_workspace_bytes(n_q, n_k, n_bits) bytes,
+ *             256-byte aligned, no initial contents needed.
+ * Every contraction runs on the matrix cores in fp32; sums over rows are
+ * reduced in double in a fixed order (deterministic).
+ * Errors: HATA_ERR_INVALID_ARG, HATA_ERR_UNSUPPORTED (n_bits),
+ * HATA_ERR_WORKSPACE, HATA_ERR_HIP.
+ */
+hata_status hata_hash_train_step(const uint16_t *q, int32_t n_q, const uint16_t *k, int32_t n_k,
+                                 const float *labels, int32_t n_bits, float *w_h, float *adam_m,
+                                 float *adam_v, int32_t step, const hata_train_params *params,
+                                 float *loss_out, float *grad_out, void *workspace,
+                                 size_t ws_bytes, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *hata_status_string(hata_status s);
 

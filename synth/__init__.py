@@ -47,6 +47,7 @@ N_BITS = 128
 
 # tensor ids of the counter-based streams
 T_Q, T_W, T_K, T_V, T_PLANT_NOISE, T_PLANT_POS, T_KNEW, T_VNEW, T_LEN = range(1, 10)
+T_TR_BASIS, T_TR_OFFSET, T_TR_QZ, T_TR_QN, T_TR_KZ, T_TR_KN = range(20, 26)
 
 _lib = None
 
@@ -321,3 +322,37 @@ def unit_context(spec: Spec, b: int, kv: int, q=None, new=None):
     k = np.concatenate([gen_unit_k(spec, b, kv, q), new[0][b, 0, kv][None]], axis=0)
     v = np.concatenate([gen_unit_v(spec, b, kv), new[1][b, 0, kv][None]], axis=0)
     return k, v
+
+
+# --------------------------------------------------------------------------
+# structured queries and keys (training and evaluating W_H)
+# --------------------------------------------------------------------------
+
+TRAIN_RANK = 16
+
+
+def structured_basis(seed: int):
+    """The fixed structure of one synthetic attention head: TRAIN_RANK
+    directions G [16][128] (entries N(0, 1/128)) that carry the q.k signal,
+    and a key offset k0 [128] (entries N(0, 64/128), norm about 8) shared by
+    every key."""
+    G = normal_f64(seed, T_TR_BASIS, 0, TRAIN_RANK * HEAD_DIM,
+                   1.0 / math.sqrt(HEAD_DIM)).reshape(TRAIN_RANK, HEAD_DIM)
+    k0 = normal_f64(seed, T_TR_OFFSET, 0, HEAD_DIM, 8.0 / math.sqrt(HEAD_DIM))
+    return G, k0
+
+
+def gen_structured_qk(seed: int, block: int, n_q: int, n_k: int):
+    """Block `block` of queries and keys with the anisotropy seen in trained
+    heads: q = 3 z_q G + 0.3 n_q and k = z_k G + n_k + k0 (z ~ N(0, I_16),
+    n ~ N(0, I_128)), rounded to bf16 [n][128].  q.k varies with the z's; the
+    keys' noise and shared offset, which dominate their direction, do not
+    change a query's ranking of its keys."""
+    G, k0 = structured_basis(seed)
+    zq = normal_f64(seed, T_TR_QZ, block * n_q * TRAIN_RANK, n_q * TRAIN_RANK).reshape(n_q, TRAIN_RANK)
+    nq = normal_f64(seed, T_TR_QN, block * n_q * HEAD_DIM, n_q * HEAD_DIM).reshape(n_q, HEAD_DIM)
+    zk = normal_f64(seed, T_TR_KZ, block * n_k * TRAIN_RANK, n_k * TRAIN_RANK).reshape(n_k, TRAIN_RANK)
+    nk = normal_f64(seed, T_TR_KN, block * n_k * HEAD_DIM, n_k * HEAD_DIM).reshape(n_k, HEAD_DIM)
+    q = 3.0 * (zq @ G) + 0.3 * nq
+    k = zk @ G + nk + k0[None, :]
+    return f64_to_bf16(q), f64_to_bf16(k)

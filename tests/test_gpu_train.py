@@ -1,0 +1,112 @@
+"""GPU parity of the W_H trainer (train.hip, through the C ABI) against the
+oracle of the learning-to-hash objective (oracle/hash_train_oracle.c).
+
+Bars:
+  - labels: bit-exact (both sides rank exact double dot products and
+    compute each label in double before rounding to float);
+  - loss terms: relative error <= 1e-4 (fp32 codes and contractions, sums
+    over rows in double; the oracle is double throughout);
+  - gradient: max |gpu - oracle| <= 2e-3 max |oracle| (fp32 contractions of
+    up to n = n_q + n_k terms: the rounding bound gamma_n |x| |g| stays far
+    below this at these sizes, while a wrong or missing term moves entries by
+    a large fraction of the maximum);
+  - Adam updates: W after each step within lr / 50 of the oracle's wherever
+    the oracle's gradient entry is not tiny (larger than 1 % of the maximum;
+    there the sign of the first update is decided); elsewhere any change no
+    larger than one step size.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import hash_top_sparse_encode_amd as hata
+import oracle
+import synth
+from workload import bf16_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(a):
+    return (np.asarray(a, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("case", ["gauss 4096", "ties 1000", "struct 4096", "small 37"])
+def test_labels_bit_exact(gpu, case):
+    rng = np.random.default_rng(len(case))
+    if case.startswith("gauss"):
+        q, k = _bf16(rng.standard_normal((64, 128))), _bf16(rng.standard_normal((4096, 128)))
+    elif case.startswith("ties"):
+        qi = rng.integers(-2, 3, size=(32, 128))
+        ki = rng.integers(-1, 2, size=(1000, 128))
+        ki[500:] = ki[:500]
+        q, k = _bf16(qi), _bf16(ki)
+    elif case.startswith("struct"):
+        q, k = synth.gen_structured_qk(7, 0, 32, 4096)
+    else:
+        q, k = _bf16(rng.standard_normal((5, 128))), _bf16(rng.standard_normal((37, 128)))
+    got = hata.hata_hash_labels(bf16_dev(q, gpu), bf16_dev(k, gpu)).cpu().numpy()
+    want = oracle.hash_labels(q, k)
+    assert np.array_equal(got, want), int((got != want).sum())
+
+
+def _batch(seed, n_q, n_k):
+    q, k = synth.gen_structured_qk(seed, 0, n_q, n_k)
+    return q, k, oracle.hash_labels(q, k)
+
+
+@pytest.mark.parametrize("r", [32, 128, 256])
+@pytest.mark.parametrize("scale", [1.0, 8.0])
+def test_loss_and_gradient(gpu, r, scale):
+    # scale 8 pushes many codes towards saturation, as training does
+    n_q, n_k = 64, 512
+    q, k, lab = _batch(3 + r, n_q, n_k)
+    w = (synth.normal_f32(5, synth.T_W, 0, 128 * r, scale / math.sqrt(128))).reshape(128, r)
+    loss_o, grad_o = oracle.hash_loss_grad(q, k, w, lab)
+    tr = hata.HashTrainer(torch.from_numpy(w).to(gpu), n_q, n_k)
+    grad = torch.empty((128, r), dtype=torch.float32, device=gpu)
+    loss = tr.step(bf16_dev(q, gpu), bf16_dev(k, gpu), torch.from_numpy(lab).to(gpu),
+                   update=False, grad_out=grad).cpu().numpy().astype(np.float64)
+    for i in range(4):
+        assert abs(loss[i] - loss_o[i]) <= 1e-4 * max(abs(loss_o[i]), 1e-3), (i, loss[i], loss_o[i])
+    g = grad.cpu().numpy().astype(np.float64)
+    err = np.abs(g - grad_o).max()
+    assert err <= 2e-3 * np.abs(grad_o).max(), (err, np.abs(grad_o).max())
+    assert torch.equal(tr.w.cpu(), torch.from_numpy(w))  # step 0 leaves W alone
+
+
+def test_adam_steps_follow_the_oracle(gpu):
+    n_q, n_k, r, lr = 64, 256, 128, 0.01
+    q, k, lab = _batch(21, n_q, n_k)
+    w0 = (synth.normal_f32(6, synth.T_W, 0, 128 * r, 1 / math.sqrt(128))).reshape(128, r)
+    tr = hata.HashTrainer(torch.from_numpy(w0).to(gpu), n_q, n_k, hata.TrainParams(lr=lr))
+    qd, kd, ld = bf16_dev(q, gpu), bf16_dev(k, gpu), torch.from_numpy(lab).to(gpu)
+    w_o, m_o, v_o = w0.astype(np.float64), np.zeros((128, r)), np.zeros((128, r))
+    for step in (1, 2, 3):
+        # the oracle's gradient at its own weights (rounded to fp32 for the call)
+        _, g_o = oracle.hash_loss_grad(q, k, w_o.astype(np.float32), lab)
+        w_prev = w_o.copy()
+        w_o, m_o, v_o = oracle.adam(w_o, m_o, v_o, g_o, step, lr)
+        tr.step(qd, kd, ld)
+        w_g = tr.w.cpu().numpy().astype(np.float64)
+        firm = np.abs(g_o) > 1e-2 * np.abs(g_o).max()
+        assert np.abs(w_g - w_o)[firm].max() <= lr / 50, step
+        assert np.all(np.abs(w_g - w_prev)[~firm] <= step * lr * (1 + 1e-3))
+        w_o = np.where(firm, w_o, w_g)  # keep following the GPU where the sign is not decided
+
+
+def test_training_is_deterministic(gpu):
+    n_q, n_k, r = 64, 512, 64
+    q, k, lab = _batch(30, n_q, n_k)
+    w0 = torch.from_numpy(synth.normal_f32(8, synth.T_W, 0, 128 * r, 1 / math.sqrt(128))).to(gpu)
+    runs = []
+    for _ in range(2):
+        tr = hata.HashTrainer(w0.view(128, r), n_q, n_k)
+        for _ in range(4):
+            tr.step(bf16_dev(q, gpu), bf16_dev(k, gpu), torch.from_numpy(lab).to(gpu))
+        runs.append((tr.w.clone(), tr.loss.clone()))
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])

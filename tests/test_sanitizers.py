@@ -51,10 +51,11 @@ def test_oracle_under_address_and_ub_sanitizers(tmp_path):
     lib = tmp_path / "liboracle_san.so"
     subprocess.check_call(["gcc", "-O1", "-g", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
                            "-fno-fast-math", *SAN, os.path.join(ROOT, "oracle", "hata_oracle.c"),
+                           os.path.join(ROOT, "oracle", "hash_train_oracle.c"),
                            "-o", str(lib), "-lm"])
     out = _pytest_child(_child_env(HATA_ORACLE_LIB=str(lib)),
                         ["tests/test_oracle.py", "tests/test_oracle_bits.py",
-                         "tests/test_oracle_recall.py"], tmp_path)
+                         "tests/test_oracle_recall.py", "tests/test_oracle_train.py"], tmp_path)
     assert " passed" in out
 
 
