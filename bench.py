@@ -58,6 +58,8 @@ def parse():
                     help="the headline workload (3: 128K context, the metric's)")
     ap.add_argument("--configs", default="1,2,3,4,5",
                     help="configurations measured beside the headline ('none' to skip)")
+    ap.add_argument("--train-steps", type=int, default=300,
+                    help="W_H training steps for the hash_training block (0 to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--copy-probe", action="store_true",
@@ -689,6 +691,42 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(spec, args.cpu_reps)
+
+    # Training W_H (the learning-to-hash objective) on structured synthetic
+    # queries and keys, and the recall test of the review with the random
+    # projection it starts from and with the trained one, on a held-out cache.
+    if args.train_steps > 0:
+        import train_eval
+        print("[bench] training W_H", file=sys.stderr, flush=True)
+        ev_cache, ev_q = train_eval.eval_cache(dev)
+        k_ev = ev_cache.max_ctx // 64
+        w0 = torch.from_numpy(train_eval.initial_w()).to(dev)
+        rec0, tie0 = train_eval.recall(ev_cache, ev_q, w0, k_ev)
+        w1, losses, ms_step, ms_lab = train_eval.train(dev, args.train_steps)
+        rec1, tie1 = train_eval.recall(ev_cache, ev_q, w1, k_ev)
+        n_pairs = train_eval.N_Q * train_eval.N_K
+        # contraction flops of one step: X W, S B, S^T A, H^T H, H E, X^T G
+        n_all, r_b = train_eval.N_Q + train_eval.N_K, 128
+        flops = 2 * (n_all * 128 * r_b + 2 * n_pairs * r_b + n_all * r_b * r_b * 2 + 128 * n_all * r_b)
+        result["hash_training"] = {
+            "what": "W_H trained by hata_hash_train_step (Adam, lr 0.01) on structured synthetic "
+                    "queries/keys (16-dim signal subspace, key offset and noise), new batch every "
+                    f"{train_eval.NEW_BATCH_EVERY} steps; recall = share of each query's exact "
+                    f"top-{k_ev} found by the Hamming selection on a held-out cache of "
+                    f"{ev_cache.max_ctx} keys x {ev_cache.n_kv_heads} heads",
+            "steps": args.train_steps,
+            "batch_pairs": n_pairs,
+            "ms_per_step": ms_step,
+            "ms_per_label_batch": ms_lab,
+            "step_contraction_TFLOPs": flops / (ms_step * 1e-3) / 1e12,
+            "loss_first": losses[0][1],
+            "loss_last": losses[-1][1],
+            "recall_random_w": rec0,
+            "recall_trained_w": rec1,
+            "tie_bucket_random_w": tie0,
+            "tie_bucket_trained_w": tie1,
+        }
+        del ev_cache, ev_q
 
     # Every configuration, each with its own layer rotation; the headline's
     # own entry reuses the numbers above.

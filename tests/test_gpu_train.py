@@ -110,3 +110,17 @@ def test_training_is_deterministic(gpu):
             tr.step(bf16_dev(q, gpu), bf16_dev(k, gpu), torch.from_numpy(lab).to(gpu))
         runs.append((tr.w.clone(), tr.loss.clone()))
     assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+
+
+def test_training_raises_recall(gpu):
+    # The review's recall test on held-out structured data: the trained
+    # projection finds clearly more of each query's exact top-k than the
+    # random one it starts from (measured: about 0.2 -> 0.4 and more).
+    import train_eval
+    cache, q = train_eval.eval_cache(gpu, n_ctx=16384, heads=4)
+    r0, _ = train_eval.recall(cache, q, torch.from_numpy(train_eval.initial_w()).to(gpu), 256)
+    w, losses, _, _ = train_eval.train(gpu, 150, log=print)
+    r1, _ = train_eval.recall(cache, q, w, 256)
+    print(f"[train] recall random {r0:.3f} trained {r1:.3f}", flush=True)
+    assert r1 > r0 + 0.08, (r0, r1)
+    assert losses[-1][1][0] < losses[0][1][0]
