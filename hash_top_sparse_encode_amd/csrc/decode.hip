@@ -8,8 +8,7 @@
 //   PRO(u,p)   per unit u = (batch b, KV head g), four parts of 32 code
 //              bits each: exact codes of the G query heads and of the step's
 //              appended token, published as words tagged with the launch's
-//              tag; part 0 also appends the K/V row and clears the unit
-//              histogram (before any of the unit's words is published).
+//              tag; part 0 also appends the K/V row.
 //   WORK(u,c)  span c of the unit's keys (8192 keys, or a multiple of 8192
 //              when a unit would need more than 64 items), in two phases:
 //     scan     wave 0 polls the unit's tagged code words while waves 1-3
@@ -275,8 +274,8 @@ template <int G>
 struct SmemPro {
     float x[G + 1][kHeadDim];                   // query heads, then the appended key or zeros
     float w[kHeadDim][kBits / kProParts];       // this part's 32 columns of W_H
-    double py[4][G + 1][kBits / kProParts];     // per-wave partial sums
-    double pa[4][G + 1][kBits / kProParts];     // per-wave partial sums of |products|
+    float py[4][G + 1][kBits / kProParts];      // per-wave partial sums
+    float pa[4][G + 1][kBits / kProParts];      // per-wave partial sums of |products|
 };
 
 template <int G>
@@ -289,17 +288,21 @@ union Smem {
 // ---------------------------------------------------------------- PRO(u)
 
 // Part p of unit u computes code bits [32 p, 32 p + 32) of the G query heads
-// and of the appended key; part 0 also copies the appended K/V rows, clears
-// the unit histogram and writes the outputs of an empty selection.
+// and of the appended key; part 0 also copies the appended K/V rows and
+// writes the outputs of an empty selection.
 //
 // Each bit is sign(y) with y = sum_t x[t] W[t][j] evaluated as a sequential
 // double sum in ascending t (bf16 x fp32 products are exact in double).
-// Fast path: sixteen-row segments summed sequentially, then combined in a
-// fixed tree -- at most 18 roundings deep -- alongside A = sum |x[t] W[t][j]|.
-// Both the tree and the sequential sum lie within gamma_127 A and gamma_18 A
-// of the exact sum (Higham, Accuracy and Stability of Numerical Algorithms,
-// ch. 4), so when |y_tree| > 2^-45 A both have the exact sum's sign.  Any
-// other bit (including non-finite inputs) is recomputed sequentially.
+// Fast path in fp32: sixteen-row segments summed by fused multiply-adds
+// (the product is exact inside each), then combined in a fixed tree -- at
+// most 18 roundings deep -- alongside A = sum |x[t] W[t][j]| formed the same
+// way.  The fp32 result lies within gamma_18 A (u = 2^-24; about 2^-19.7 A)
+// of the exact sum, and the sequential double sum within gamma_127 A
+// (u = 2^-53) of it (Higham, Accuracy and Stability of Numerical Algorithms,
+// ch. 4); products or sums that underflow add at most 2^-119 in all.  So
+// when |y_f32| > 2^-16 A_f32 + 2^-100 the exact sum and the double sum both
+// have its sign.  Any other bit (including non-finite inputs, which fail
+// the test) is recomputed by the sequential double sum.
 template <int G>
 __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Smem<G> &sm) {
     constexpr int NB = G * kBits + 1;
@@ -307,7 +310,11 @@ __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Sm
     constexpr int NV = G + 1;                // query heads + appended key
     const int b = u / a.Hkv, kv = u % a.Hkv, Hq = a.Hkv * G;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    // This part's 128 x 32 slice of W_H, 16 bytes per load, before anything else.
+    // Every load the part needs is issued before any is used, so they share
+    // one round trip: its 128 x 32 slice of W_H (16 bytes per load), the x
+    // rows (query heads, then the token's key: one 16-byte load per thread,
+    // 16 threads per row), the unit's generation and the entry's length, and
+    // for part 0 the top-k and the token's K/V words to append.
     fvec4 wq[kHeadDim * COLS / 4 / kThreads];  // 4
     {
         const float *wk = a.w + (int64_t)kv * kHeadDim * kBits + part * COLS;
@@ -317,46 +324,54 @@ __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Sm
             wq[r] = *reinterpret_cast<const fvec4 *>(wk + (f >> 3) * kBits + 4 * (f & 7));
         }
     }
+    // (Loads are issued by every lane, those with nothing to load reading the
+    // unit's first query row, so that no branch separates them.)
+    const int xv = t >> 4, d0 = (t & 15) * 8;
+    const int64_t src = ((int64_t)b * a.Hkv + kv) * kHeadDim;
+    const uint16_t *qrow = a.q + ((int64_t)b * Hq + kv * G) * kHeadDim;
+    const uint16_t *xp = xv < G ? qrow + xv * kHeadDim + d0
+                                : (xv == G && a.k_new ? a.k_new + src + d0 : qrow);
+    const uint4 xr = *reinterpret_cast<const uint4 *>(xp);
+    // the new K and V rows: 32 + 32 eight-byte words (threads 0-63)
+    const uint16_t *kvp = t < 64 && a.k_new ? (t < 32 ? a.k_new + src + 4 * t : a.v_new + src + 4 * (t - 32)) : qrow;
+    const uint64_t kvw = *reinterpret_cast<const uint64_t *>(kvp);
+    const int32_t topk_b = a.topk[b];
     const uint32_t tag = ld_dev(a.gen + u) + 1u;
     const int64_t raw = a.seq_len[b];
-    const StepLen sl = step_len(a, b);
+    StepLen sl;
+    sl.l0 = clamp_len(raw, a.max_ctx);
+    sl.app = a.k_new != nullptr && sl.l0 + 1 <= a.max_ctx;
+    sl.len = sl.l0 + (sl.app ? 1 : 0);
     const int nvec = G + (sl.app ? 1 : 0);
-    // x rows (query heads, then the appended key or zeros): one 16-byte load
-    // per thread, 16 threads per row
     if (t < NV * 16) {
-        const int v = t >> 4, d0 = (t & 15) * 8;
-        uint4 r = make_uint4(0, 0, 0, 0);
-        if (v < G) r = *reinterpret_cast<const uint4 *>(a.q + ((int64_t)b * Hq + kv * G + v) * kHeadDim + d0);
-        else if (sl.app) r = *reinterpret_cast<const uint4 *>(a.k_new + ((int64_t)b * a.Hkv + kv) * kHeadDim + d0);
-        const uint32_t wds[4] = {r.x, r.y, r.z, r.w};
+        const uint32_t wds[4] = {xr.x, xr.y, xr.z, xr.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            sm.pro.x[v][d0 + 2 * e] = __uint_as_float(wds[e] << 16);
-            sm.pro.x[v][d0 + 2 * e + 1] = __uint_as_float(wds[e] & 0xFFFF0000u);
+            sm.pro.x[xv][d0 + 2 * e] = __uint_as_float(wds[e] << 16);
+            sm.pro.x[xv][d0 + 2 * e + 1] = __uint_as_float(wds[e] & 0xFFFF0000u);
         }
     }
+    fvec4 *wl = reinterpret_cast<fvec4 *>(&sm.pro.w[0][0]);
+#pragma unroll
+    for (int r = 0; r < kHeadDim * COLS / 4 / kThreads; ++r) wl[r * kThreads + t] = wq[r];
+    // Part 0's stores: nothing in this launch waits for them (the unit's
+    // attention reads the token's K/V from k_new / v_new, and its code word
+    // from the published words), so they are issued and left in flight.
     if (part == 0) {
+        int64_t k_eff = topk_b < 0 ? 0 : (topk_b > a.k_max ? a.k_max : topk_b);
+        k_eff = k_eff < sl.len ? k_eff : sl.len;
         if (kv == 0 && t == 0) {
             int flags = 0;
             if (raw < 0 || raw > a.max_ctx) flags |= HATA_DEV_BAD_LENGTH;
             if (a.k_new != nullptr && !sl.app) flags |= HATA_DEV_APPEND_OVERFLOW;
-            if (a.topk[b] > a.k_max) flags |= HATA_DEV_TOPK_CLAMPED;
+            if (topk_b > a.k_max) flags |= HATA_DEV_TOPK_CLAMPED;
             if (flags) atomicOr(&a.ctrl[kCtrlStatus], flags);
         }
         if (sl.app && t < 64) {
-            // the new K and V rows: 32 + 32 eight-byte words
             const int64_t row = (int64_t)u * a.max_ctx + sl.l0;
-            const int64_t src = ((int64_t)b * a.Hkv + kv) * kHeadDim;
-            if (t < 32) {
-                st_dev(reinterpret_cast<uint64_t *>(a.k_cache + row * kHeadDim) + t,
-                       reinterpret_cast<const uint64_t *>(a.k_new + src)[t]);
-            } else {
-                st_dev(reinterpret_cast<uint64_t *>(a.v_cache + row * kHeadDim) + (t - 32),
-                       reinterpret_cast<const uint64_t *>(a.v_new + src)[t - 32]);
-            }
+            if (t < 32) st_dev(reinterpret_cast<uint64_t *>(a.k_cache + row * kHeadDim) + t, kvw);
+            else st_dev(reinterpret_cast<uint64_t *>(a.v_cache + row * kHeadDim) + (t - 32), kvw);
         }
-        for (int i = t; i < NB + 1; i += kThreads) st_dev(a.unit_hist + (int64_t)u * (NB + 1) + i, 0u);
-        const int64_t k_eff = step_keff(a, b, sl.len);
         if (a.sel_out) {
             int32_t *su = a.sel_out + (int64_t)u * a.k_max;
             for (int64_t p = k_eff + t; p < a.k_max; p += kThreads) su[p] = -1;
@@ -366,44 +381,38 @@ __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Sm
                 a.out[((int64_t)b * Hq + kv * G) * kHeadDim + i] = 0;
         }
     }
-    fvec4 *wl = reinterpret_cast<fvec4 *>(&sm.pro.w[0][0]);
-#pragma unroll
-    for (int r = 0; r < kHeadDim * COLS / 4 / kThreads; ++r) wl[r * kThreads + t] = wq[r];
     __syncthreads();
     // Segment sums: lane col = lane & 31 of wave w covers rows
     // [16 seg, 16 seg + 16) with seg = 2 w + (lane >> 5).
     {
         const int col = lane & 31, seg = 2 * wv + (lane >> 5);
-        double ys[NV], as[NV];
+        float ys[NV], as[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            ys[v] = 0.0;
-            as[v] = 0.0;
+            ys[v] = 0.f;
+            as[v] = 0.f;
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = 16 * seg + r;
-            const double wd = (double)sm.pro.w[row][col];
+            const float wf = sm.pro.w[row][col];
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                const double pr = (double)sm.pro.x[v][row] * wd;  // exact
-                ys[v] += pr;
-                as[v] += fabs(pr);
+                const float xf = sm.pro.x[v][row];
+                ys[v] = fmaf(xf, wf, ys[v]);
+                as[v] = fmaf(fabsf(xf), fabsf(wf), as[v]);
             }
         }
         // pair the wave's two segments, then park the wave's partials
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            const double yo = __shfl_xor(ys[v], 32, 64), ao = __shfl_xor(as[v], 32, 64);
+            const float yo = __shfl_xor(ys[v], 32, 64), ao = __shfl_xor(as[v], 32, 64);
             if (lane < 32) {
                 sm.pro.py[wv][v][col] = ys[v] + yo;  // lower segment first
                 sm.pro.pa[wv][v][col] = as[v] + ao;
             }
         }
     }
-    // Part 0's clearing of the unit histogram is complete before any code
-    // word of the unit is published.
-    if (part == 0) drain_memory();
     __syncthreads();
     // Decide bit (v, col) for v = t >> 5 (and v = 8 + (t >> 5) on a second
     // pass for G = 8): tree over the four waves, then the sign test.
@@ -412,12 +421,12 @@ __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Sm
         const int v = pass * 8 + (t >> 5), col = t & 31;
         bool bit = false;
         if (v < NV) {
-            const double y = (sm.pro.py[0][v][col] + sm.pro.py[1][v][col]) +
-                             (sm.pro.py[2][v][col] + sm.pro.py[3][v][col]);
-            const double A = ((sm.pro.pa[0][v][col] + sm.pro.pa[1][v][col]) +
-                              (sm.pro.pa[2][v][col] + sm.pro.pa[3][v][col])) * (1.0 + 0x1p-40);
-            if (fabs(y) > 0x1p-45 * A) {
-                bit = y > 0.0;
+            const float y = (sm.pro.py[0][v][col] + sm.pro.py[1][v][col]) +
+                            (sm.pro.py[2][v][col] + sm.pro.py[3][v][col]);
+            const float A = (sm.pro.pa[0][v][col] + sm.pro.pa[1][v][col]) +
+                            (sm.pro.pa[2][v][col] + sm.pro.pa[3][v][col]);
+            if (fabsf(y) > fmaf(0x1p-16f, A, 0x1p-100f)) {
+                bit = y > 0.f;
             } else {
                 double ysq = 0.0;  // the defining sequential sum
                 for (int row = 0; row < kHeadDim; ++row)
@@ -553,7 +562,10 @@ __device__ __forceinline__ Slot slot_of(const FusedArgs &a, int u, int c) {
 
 // Issue the 16-byte code loads of sub-batch sb of a chunk (thread t: keys
 // p0 + 256 (kSub sb + r) + t, r < kSub: each instruction reads 1 KB per
-// wave, contiguous).
+// wave, contiguous).  A lane past the span re-reads the span's last key:
+// every load is issued on every path, so the compiler's wait before a
+// sub-batch is used counts exactly the loads issued after it (a load that
+// some path skips would make it wait for every load in flight).
 __device__ __forceinline__ void slot_issue(const FusedArgs &a, const Slot &s, int sb,
                                            uvec4 (&buf)[kSub]) {
     const int t = threadIdx.x;
@@ -561,15 +573,15 @@ __device__ __forceinline__ void slot_issue(const FusedArgs &a, const Slot &s, in
 #pragma unroll
     for (int r = 0; r < kSub; ++r) {
         const int64_t i = s.p0 + (int64_t)(kSub * sb + r) * kThreads + t;
-        buf[r] = i < s.p1 ? kc[i] : uvec4{0u, 0u, 0u, 0u};
+        buf[r] = kc[i < s.p1 ? i : s.p1 - 1];
     }
 }
 
 // Wave 0 only: the unit's generation and its PRO parts' tagged code words
 // (query heads, then the appended key), re-read until every word carries
-// this launch's tag (generation + 1), into LDS.  Loads complete in order
-// within a wave, so this runs in a wave with no code loads outstanding; the
-// other waves' code streams are already in flight.
+// this launch's tag (generation + 1), into LDS.  It runs after the wave has
+// issued its first code loads: a workgroup's loads leave the CU in order,
+// so the first read returns no later than those would anyway.
 template <int G>
 __device__ __forceinline__ void slot_fetch_qcodes(const FusedArgs &a, const Slot &s, Smem<G> &sm) {
     constexpr int NW = (G + 1) * kWords;
@@ -729,6 +741,16 @@ __device__ __forceinline__ int slot_publish(const FusedArgs &a, const Slot &s, u
     return tc;
 }
 
+// The unit's last WORK item, once every item of the unit has signalled (no
+// item reads the unit histogram again in this launch, and every item's
+// counts were added before its signal): the histogram is cleared for the
+// unit's next launch.  The workspace's zero fill clears it before the first.
+template <int G>
+__device__ __forceinline__ void unit_hist_clear(const FusedArgs &a, int u) {
+    constexpr int NB = G * kBits + 1;
+    for (int i = threadIdx.x; i < NB + 1; i += kThreads) st_dev(a.unit_hist + (int64_t)u * (NB + 1) + i, 0u);
+}
+
 // Thread 0 of the unit's last WORK item, once it knows it is the last: every
 // item of the unit is past its waits and past reading the length, so the
 // unit's counters are reset for the next launch, its generation advances,
@@ -751,34 +773,41 @@ __device__ __forceinline__ void entry_done(const FusedArgs &a, int b, const Step
 }
 
 // Scan phase of work item (u, c): its span's codes in sub-batches of 16 KB,
-// kScanDepth in flight; wave 0 fetches the unit's code words first (see
-// slot_fetch_qcodes) while the other waves' first sub-batches are on their
-// way.  Scores go to LDS (or the workspace), the histograms are published.
-// Returns the span's candidate cut; *gen gets the launch's tag.
+// kScanDepth in flight, issued in groups of kScanDepth: every group but the
+// last issues the next group's sub-batch in the slot it has just scored
+// (sub-batches past the span re-read its last key and are not scored), so
+// each sub-batch's wait leaves the later ones in flight.  Wave 0 then
+// fetches the unit's code words (see slot_fetch_qcodes).  Scores go to LDS
+// (or the workspace), the histograms are published.  Returns the span's
+// candidate cut; *gen gets the launch's tag.
 template <int G>
 __device__ __forceinline__ int scan_phase(const FusedArgs &a, const Slot &cur, uint32_t &gen, Smem<G> &sm) {
     constexpr int NB = G * kBits + 1;
-    const int n_sub = (int)((cur.p1 - cur.p0 + kSub * kThreads - 1) / (kSub * kThreads));
     constexpr int D = kScanDepth;
+    const int n_sub = (int)((cur.p1 - cur.p0 + kSub * kThreads - 1) / (kSub * kThreads));
+    const int n_grp = (n_sub + D - 1) / D;
     const int wv = threadIdx.x >> 6;
     uvec4 buf[D][kSub];
-    for (int i = threadIdx.x; i < SmemScan<G>::NH * NB; i += kThreads) (&sm.scan.hist[0][0])[i] = 0u;
-    if (wv == 0) slot_fetch_qcodes<G>(a, cur, sm);
 #pragma unroll
     for (int d = 0; d < D; ++d) slot_issue(a, cur, d, buf[d]);
+    for (int i = threadIdx.x; i < SmemScan<G>::NH * NB; i += kThreads) (&sm.scan.hist[0][0])[i] = 0u;
+    if (wv == 0) slot_fetch_qcodes<G>(a, cur, sm);
     __syncthreads();
     gen = sm.scan.gen;
     uint32_t qc[G][4];
     qcodes_sgpr<G>(sm, qc);
     QPlanes<G> qp;
     query_planes<G>(qc, qp);
-    for (int sb = 0; sb < n_sub; sb += D) {
+    for (int g = 0; g + 1 < n_grp; ++g) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            slot_score<G>(a, cur, sb + d, buf[d], qp, sm);
-            if (sb + d + D < n_sub) slot_issue(a, cur, sb + d + D, buf[d]);
+            slot_score<G>(a, cur, g * D + d, buf[d], qp, sm);
+            slot_issue(a, cur, (g + 1) * D + d, buf[d]);
         }
     }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if ((n_grp - 1) * D + d < n_sub) slot_score<G>(a, cur, (n_grp - 1) * D + d, buf[d], qp, sm);
     return slot_publish<G>(a, cur, gen, sm);
 }
 
@@ -1199,7 +1228,10 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
         const int prev = wg_signal(unit_ctr(a, u, kAttn));
         if (t == 0) sm.sel.last = (prev == n_splits_u - 1);
         __syncthreads();
-        if (sm.sel.last && t == 0) entry_done(a, b, sl, unit_done(a, u));
+        if (sm.sel.last) {
+            unit_hist_clear<G>(a, u);
+            if (t == 0) entry_done(a, b, sl, unit_done(a, u));
+        }
         return sm.sel.last;
     }
 
@@ -1469,6 +1501,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     if (t == 0) sm.sel.last = (prev == n_splits_u - 1);
     __syncthreads();
     if (!sm.sel.last) return false;
+    unit_hist_clear<G>(a, u);
     // Per split x and head h: weight w = exp2(m_x - M) with M the maximum
     // over splits; out = sum_x w o_x / sum_x w l_x.  Thread 0 first does the
     // unit's bookkeeping (its count returns with the loads below and is used

@@ -183,6 +183,67 @@ def test_many_units_dense_and_sparse(gpu):
     run_spec(spec, gpu, units=[(0, 0), (0, 15), (1, 3), (30, 7), (31, 0)])
 
 
+def _bf16_bits_of(x: np.ndarray) -> np.ndarray:
+    """bf16 bits of float32 values that are exactly representable in bf16."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0)
+    return (u >> 16).astype(np.uint16)
+
+
+def test_query_codes_in_band(gpu):
+    # Code bits whose sum x . W_j is zero or tiny next to A = sum_t |x_t W_tj|
+    # cannot be decided by the kernel's fp32 sum and go to the defining
+    # sequential double sum.  W's rows 2i and 2i + 1 agree in every even
+    # column, and the query heads and the step's new keys are antisymmetric
+    # over those pairs (x_{2i+1} = -x_{2i}, |x| in [1, 16)), so their even
+    # bits sum to exactly zero (bit 0); every other head, and the second
+    # batch entry's new keys, carry one imbalance, x_1 = -(1 - 2^-8) against
+    # x_0 = 1, which leaves a sum of 2^-8 W_1j against an A near 2^10 |W|.
+    spec = synth.custom("in band", 2, 8, 2, [5000, 1200], [64, 16], [5, 2], seed=13)
+    wl = GpuWorkload(spec, gpu, extra_ctx=2, encode_prefill=False)
+    q_keys = wl.q_host.copy()  # the keys of the context were planted from these
+    w = wl.w_host.copy()
+    w[:, 1::2, 0::2] = w[:, 0::2, 0::2]
+    rng = np.random.default_rng(13)
+
+    def pairs(shape, imbalance):
+        mag = ((1.0 + rng.integers(0, 128, size=shape + (64,)) / 128.0)
+               * 2.0 ** rng.integers(0, 4, size=shape + (64,))).astype(np.float32)
+        sign = np.where(rng.random(shape + (64,)) < 0.5, -1.0, 1.0).astype(np.float32)
+        x = np.empty(shape + (128,), dtype=np.float32)
+        x[..., 0::2] = mag * sign
+        x[..., 1::2] = -mag * sign
+        x[..., 0] = np.where(imbalance, 1.0, x[..., 0])
+        x[..., 1] = np.where(imbalance, -(1.0 - 2.0 ** -8), x[..., 1])
+        return _bf16_bits_of(x)
+
+    heads = np.arange(spec.Hq) % 2 == 1
+    q = pairs((spec.B, spec.Hq), np.broadcast_to(heads, (spec.B, spec.Hq)))
+    kn = pairs((spec.B, 1, spec.Hkv),
+               np.broadcast_to((np.arange(spec.B) == 1)[:, None, None], (spec.B, 1, spec.Hkv)))
+    new = (kn, wl.new_host[1])
+    wl.w_host, wl.q_host, wl.new_host = w, q, new
+    wl.w = torch.from_numpy(w).to(gpu)
+    wl.q = torch.from_numpy(q.view(np.int16)).to(gpu).view(torch.bfloat16)
+    wl.k_new = torch.from_numpy(kn.view(np.int16)).to(gpu).view(torch.bfloat16)
+    wl.encode_prefill()
+    out, sel, sc = wl.step(debug=True)
+    torch.cuda.synchronize()
+    assert wl.cache.status() == 0
+    G = spec.G
+    for b in range(spec.B):
+        for kv in range(spec.Hkv):
+            K, V = synth.unit_context(spec, b, kv, q_keys, new)
+            ref = oracle.decode_unit(q[b, kv * G:(kv + 1) * G], w[kv], K, V, spec.topk[b])
+            # the even bits of the antisymmetric vectors are all zero
+            qc = oracle.encode(q[b, kv * G:(kv + 1) * G], w[kv])
+            even = np.uint32(0x55555555)
+            for h in range(G):
+                if not heads[kv * G + h]:
+                    assert not np.any(qc[h] & even)
+            check_unit(spec, wl, b, kv, out, sel, sc, ref=ref)
+
+
 def test_determinism(gpu):
     spec = synth.custom("det", 2, 8, 2, [20000, 7000], [300, 100], [20, 7], seed=5)
     wl = GpuWorkload(spec, gpu, extra_ctx=1)
