@@ -37,9 +37,10 @@
 //
 // Ordering: a PRO part waits for nothing; a WORK item's scan waits for the
 // PRO parts of its unit (smaller block indices), and its selection for the
-// scans of every WORK item of its unit.  Workgroups of a grid are started in
-// block order within each XCD, and a finished workgroup frees its slot.  Take
-// the smallest unfinished block X: every PRO part is done, so if X is
+// scans of every WORK item of its unit.  Workgroups of a grid are dealt to
+// the eight XCDs in turn (block b to XCD b mod 8) and started in block order
+// within each XCD, and a finished workgroup frees its slot.  Take the
+// smallest unfinished block X: every PRO part is done, so if X is
 // WORK(u, c), every workgroup that started after the finished ones holds an
 // item of unit u or a later one, and the unit's unstarted items (at most 63)
 // are the next in line on their XCDs; an XCD holds at least 64 of these
@@ -48,7 +49,10 @@
 // grid, see item_of, the host has checked that every workgroup of the launch
 // is resident at once, so no wait depends on a workgroup yet to start.)
 // Every wait also gives up after a bound (HATA_DEV_STALL), so the kernel
-// always terminates.
+// always terminates, and no result depends on where a workgroup runs.  A
+// unit's consecutive items land on different XCDs, which spreads each
+// unit's traffic over all of them (keeping each unit on one XCD was
+// measured slower: every XCD's share of the memory bandwidth is capped).
 //
 // Coherence across the eight XCDs without cache flushes: every value one
 // workgroup produces for another is written with a device-scope relaxed
@@ -199,8 +203,7 @@ __device__ __forceinline__ StepLen step_len(const FusedArgs &a, int b) {
     return s;
 }
 
-__device__ __forceinline__ int64_t step_keff(const FusedArgs &a, int b, int64_t len) {
-    int64_t k = a.topk[b];
+__device__ __forceinline__ int64_t step_keff_of(const FusedArgs &a, int64_t k, int64_t len) {
     if (k < 0) k = 0;
     if (k > a.k_max) k = a.k_max;
     return k < len ? k : len;
@@ -358,8 +361,7 @@ __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Sm
     // attention reads the token's K/V from k_new / v_new, and its code word
     // from the published words), so they are issued and left in flight.
     if (part == 0) {
-        int64_t k_eff = topk_b < 0 ? 0 : (topk_b > a.k_max ? a.k_max : topk_b);
-        k_eff = k_eff < sl.len ? k_eff : sl.len;
+        const int64_t k_eff = step_keff_of(a, topk_b, sl.len);
         if (kv == 0 && t == 0) {
             int flags = 0;
             if (raw < 0 || raw > a.max_ctx) flags |= HATA_DEV_BAD_LENGTH;
@@ -548,16 +550,28 @@ struct Slot {
     int u, c;
     int64_t p0, p1;  // key range, empty if p0 >= p1
     StepLen sl;
+    int64_t k_eff;   // the entry's top-k, clamped to [0, min(k_max, len)]
 };
 
-__device__ __forceinline__ Slot slot_of(const FusedArgs &a, int u, int c) {
+// The item's span within its cache row, before the entry's length is known
+// (so its first code loads can be issued at once).
+__device__ __forceinline__ Slot slot_row(const FusedArgs &a, int u, int c) {
     Slot s;
     s.u = u;
     s.c = c;
-    s.sl = step_len(a, s.u / a.Hkv);
-    s.p0 = (int64_t)s.c * a.span;
-    s.p1 = s.p0 + a.span < s.sl.len ? s.p0 + a.span : s.sl.len;
+    s.p0 = (int64_t)c * a.span;
+    s.p1 = s.p0 + a.span < a.max_ctx ? s.p0 + a.span : a.max_ctx;
+    s.k_eff = 0;
     return s;
+}
+
+// The entry's length and top-k: the span cut to the length, k_eff.
+__device__ __forceinline__ void slot_len(const FusedArgs &a, Slot &s) {
+    const int b = s.u / a.Hkv;
+    const int32_t topk_b = a.topk[b];
+    s.sl = step_len(a, b);
+    s.p1 = s.p0 + a.span < s.sl.len ? s.p0 + a.span : s.sl.len;
+    s.k_eff = step_keff_of(a, topk_b, s.sl.len);
 }
 
 // Issue the 16-byte code loads of sub-batch sb of a chunk (thread t: keys
@@ -614,14 +628,14 @@ __device__ __forceinline__ void qcodes_sgpr(const Smem<G> &sm, uint32_t (&qc)[G]
 // Scores of sub-batch sb, counted into the LDS sub-histograms and kept in
 // LDS (spans of kSpanUnit keys) or stored to the workspace two to a 32-bit
 // word.
-template <int G>
+template <int G, bool LDS>
 __device__ __forceinline__ void slot_score(const FusedArgs &a, const Slot &s, int sb,
                                            const uvec4 (&buf)[kSub], const QPlanes<G> &qp,
                                            Smem<G> &sm) {
     const int t = threadIdx.x, wv = t >> 6;
     constexpr int HPW = SmemScan<G>::NH / 4;  // sub-histograms per wave
     uint32_t *wh = sm.scan.hist[wv * HPW + (t & (HPW - 1))];
-    const bool in_lds = a.span <= kSpanUnit;
+    constexpr bool in_lds = LDS;
     const int n_span = (int)(s.p1 - s.p0);
     const int sub_lo = kSub * sb * kThreads;
     const int app_ii = s.sl.app ? (int)(s.sl.l0 - s.p0) : -1;
@@ -692,7 +706,7 @@ __device__ __forceinline__ int slot_publish(const FusedArgs &a, const Slot &s, u
     // The candidate cut: the first bin at which the span's cumulative count
     // reaches 1.5 times its proportional share of k_eff, plus 32.
     const int n_span = (int)(s.p1 - s.p0);
-    const int64_t k_eff = step_keff(a, s.u / a.Hkv, s.sl.len);
+    const int64_t k_eff = s.k_eff;
     const int64_t share = (k_eff * n_span + s.sl.len - 1) / s.sl.len;
     const int64_t target = share + share / 2 + 32 < n_span ? share + share / 2 + 32 : n_span;
 #pragma unroll
@@ -772,24 +786,32 @@ __device__ __forceinline__ void entry_done(const FusedArgs &a, int b, const Step
     st_dev(batch_ctr(a, b), 0);
 }
 
-// Scan phase of work item (u, c): its span's codes in sub-batches of 16 KB,
-// kScanDepth in flight, issued in groups of kScanDepth: every group but the
-// last issues the next group's sub-batch in the slot it has just scored
-// (sub-batches past the span re-read its last key and are not scored), so
-// each sub-batch's wait leaves the later ones in flight.  Wave 0 then
-// fetches the unit's code words (see slot_fetch_qcodes).  Scores go to LDS
-// (or the workspace), the histograms are published.  Returns the span's
-// candidate cut; *gen gets the launch's tag.
-template <int G>
-__device__ __forceinline__ int scan_phase(const FusedArgs &a, const Slot &cur, uint32_t &gen, Smem<G> &sm) {
+// Scan phase of work item (u, c), which also sets up its slot (cur): the
+// span's codes in sub-batches of 16 KB, kScanDepth in flight, issued in
+// groups of kScanDepth: every group but the last issues the next group's
+// sub-batch in the slot it has just scored (sub-batches past the span
+// re-read its last key and are not scored), so each sub-batch's wait leaves
+// the later ones in flight.  Wave 0 then fetches the unit's code words (see
+// slot_fetch_qcodes).  Scores go to LDS (or the workspace), the histograms
+// are published.  Returns the span's candidate cut (-1 for an empty span);
+// *gen gets the launch's tag.
+template <int G, bool LDS>
+__device__ __forceinline__ int scan_phase(const FusedArgs &a, int u, int c, Slot &cur, uint32_t &gen,
+                                          Smem<G> &sm) {
     constexpr int NB = G * kBits + 1;
     constexpr int D = kScanDepth;
-    const int n_sub = (int)((cur.p1 - cur.p0 + kSub * kThreads - 1) / (kSub * kThreads));
-    const int n_grp = (n_sub + D - 1) / D;
     const int wv = threadIdx.x >> 6;
+    // The first group's loads leave before the entry's length is read (they
+    // stay inside the span's cache row; keys past the length are never
+    // scored), the length and the top-k with them.
+    cur = slot_row(a, u, c);
     uvec4 buf[D][kSub];
 #pragma unroll
     for (int d = 0; d < D; ++d) slot_issue(a, cur, d, buf[d]);
+    slot_len(a, cur);
+    if (cur.p0 >= cur.p1) return -1;
+    const int n_sub = (int)((cur.p1 - cur.p0 + kSub * kThreads - 1) / (kSub * kThreads));
+    const int n_grp = (n_sub + D - 1) / D;
     for (int i = threadIdx.x; i < SmemScan<G>::NH * NB; i += kThreads) (&sm.scan.hist[0][0])[i] = 0u;
     if (wv == 0) slot_fetch_qcodes<G>(a, cur, sm);
     __syncthreads();
@@ -801,13 +823,13 @@ __device__ __forceinline__ int scan_phase(const FusedArgs &a, const Slot &cur, u
     for (int g = 0; g + 1 < n_grp; ++g) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            slot_score<G>(a, cur, g * D + d, buf[d], qp, sm);
+            slot_score<G, LDS>(a, cur, g * D + d, buf[d], qp, sm);
             slot_issue(a, cur, (g + 1) * D + d, buf[d]);
         }
     }
 #pragma unroll
     for (int d = 0; d < D; ++d)
-        if ((n_grp - 1) * D + d < n_sub) slot_score<G>(a, cur, (n_grp - 1) * D + d, buf[d], qp, sm);
+        if ((n_grp - 1) * D + d < n_sub) slot_score<G, LDS>(a, cur, (n_grp - 1) * D + d, buf[d], qp, sm);
     return slot_publish<G>(a, cur, gen, sm);
 }
 
@@ -831,17 +853,16 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 // The query heads as the A operand of v_mfma_f32_16x16x32_bf16: lane l holds
-// row l % 16 (head; zero for heads >= G) and, for MFMA j, dims
+// row l % 16 (head; a copy of head G - 1 for rows >= G) and, for MFMA j, dims
 // 32 j + 8 (l / 16) .. + 8 (the same dims its B operand brings for a key).
 template <int G>
 __device__ __forceinline__ void load_q_operand(const uint16_t *qg, bf16x8 (&qa)[4]) {
-    const int lane = threadIdx.x & 63, h = lane & 15, grp = lane >> 4;
+    // Rows h >= G repeat head G - 1 (their logits are never used), so every
+    // lane loads and nothing waits for these loads before their first use.
+    const int lane = threadIdx.x & 63, h = (lane & 15) < G ? (lane & 15) : G - 1, grp = lane >> 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uvec4 v = {0u, 0u, 0u, 0u};
-        if (h < G) v = *reinterpret_cast<const uvec4 *>(qg + h * kHeadDim + 32 * j + 8 * grp);
-        qa[j] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int j = 0; j < 4; ++j)
+        qa[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uvec4 *>(qg + h * kHeadDim + 32 * j + 8 * grp));
 }
 
 // s_waitcnt immediates (gfx9 encoding): wait for LDS operations only, or
@@ -886,17 +907,17 @@ __device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
     for (int base = 32 * wv; base < n; base += 128) {
         const int kc = n - base < 32 ? n - base : 32;
         // K rows: key 16 tau + c, dims 32 j + 8 grp .. + 8 for MFMA j
+        // (keys past kc read the round's first key: every lane loads, so no
+        // branch separates these loads from the V loads below, and their
+        // logits are masked)
         uvec4 kr[2][4];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
             const int kk = 16 * tau + c;
-            const int off = kk < kc ? (int)list[base + kk] : -1;
+            const int off = (int)list[base + (kk < kc ? kk : 0)];
             const uint16_t *row = off == app_off ? kapp : Kb + off * kHeadDim;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                kr[tau][j] = uvec4{0u, 0u, 0u, 0u};
-                if (off >= 0) kr[tau][j] = *reinterpret_cast<const uvec4 *>(row + 32 * j + 8 * grp);
-            }
+            for (int j = 0; j < 4; ++j) kr[tau][j] = *reinterpret_cast<const uvec4 *>(row + 32 * j + 8 * grp);
         }
         // V rows straight into LDS: 16 bytes per lane, and one instruction
         // fills four consecutive 256-byte rows (lane l writes piece l), so
@@ -917,6 +938,8 @@ __device__ __forceinline__ void attend_mfma(const uint16_t *__restrict__ Kb,
         for (int r = 0; r < 8; ++r)
             __builtin_amdgcn_global_load_lds(vrow[r], (__attribute__((address_space(3))) void *)&vst[4 * r][0],
                                              16, 0, 0);
+        // nothing that waits for the K rows is moved above the V loads
+        __builtin_amdgcn_sched_barrier(0);
         // logits
         f32x4 acc[2];
 #pragma unroll
@@ -1205,7 +1228,7 @@ __device__ __forceinline__ int block_excl_count(bool f, int *tmp, int *total) {
 // selected keys compacted in index order (in batches of kListCap keys),
 // gathered and attended; the (m, l, o) partials of the items are merged in
 // item order by the last one.
-template <int G>
+template <int G, bool LDS>
 __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, int tc, uint32_t gen,
                                           Smem<G> &sm) {
     constexpr int D = kSelRounds;  // selection rounds of scores in flight
@@ -1221,7 +1244,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const StepLen sl = cur.sl;
     const int64_t len = sl.len;
-    const int64_t k_eff = step_keff(a, b, len);
+    const int64_t k_eff = cur.k_eff;
     const int64_t s0 = cur.p0, s1 = cur.p1;
     const int n_splits_u = (int)((len + a.span - 1) / a.span);
     if (k_eff == 0) {  // the outputs are zero (written by PRO part 0)
@@ -1235,15 +1258,11 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
         return sm.sel.last;
     }
 
-    // the query heads as MFMA operands
-    bf16x8 qa[4];
-    load_q_operand<G>(a.q + ((int64_t)b * Hq + kv * G) * kHeadDim, qa);
-
     const uint16_t *su = a.scores + (int64_t)u * a.sstride;
     // batch layout: wave w holds keys [rb + 2048 w, rb + 2048 (w + 1)), lane
     // `lane` of it keys rb + 2048 w + 512 d + 8 lane + e (d < D, e < 8)
     const int woff = wv * (kSelRounds * kSelRound / 4) + 8 * lane;
-    const bool in_lds = a.span <= kSpanUnit;
+    constexpr bool in_lds = LDS;
     uint4 pf[D];
 #pragma unroll
     for (int d = 0; d < D; ++d)
@@ -1256,19 +1275,28 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     const uint64_t *chu = a.chunk_hist + (int64_t)u * a.n_chunks * NB;
     const uint64_t tag = (uint64_t)gen << 32;
     const int wlo = tc - (kWin - 1);
-    uint32_t loc[PER];
-    uint64_t win[WPT];
+    uint32_t loc[PER] = {};
+    uint64_t win[WPT] = {};
+    // Every lane of waves 0-2 issues every read (entries it does not own
+    // re-read word 0 and are masked where used: loc_ok, win_ok), so the
+    // reads are all in flight before the first is waited for.
     auto read_state = [&]() {
+        if (uni(t) >= kPoll) return;
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
             const int bin = t * PER + e;
-            loc[e] = (t < kPoll && bin < NB) ? ld_dev(uhr + bin) : 0u;
+            loc[e] = ld_dev(uhr + (bin < NB ? bin : 0));
         }
 #pragma unroll
         for (int k = 0; k < WPT; ++k) {
             const int i = t + k * kPoll, cc = i / kWin, bin = wlo + i % kWin;
-            win[k] = (t < kPoll && cc < s && bin >= 0) ? ld_dev(chu + (int64_t)cc * NB + bin) : tag;
+            win[k] = ld_dev(chu + ((cc < s && bin >= 0) ? (int64_t)cc * NB + bin : 0));
         }
+    };
+    auto loc_ok = [&](int e) { return t < kPoll && t * PER + e < NB; };
+    auto win_ok = [&](int k) {
+        const int i = t + k * kPoll;
+        return t < kPoll && i / kWin < s && wlo + i % kWin >= 0;
     };
     read_state();
     // ---- meanwhile the span's candidates: every key up to the candidate
@@ -1279,7 +1307,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     for (int spins = 0;; ++spins) {
         int tsum = 0;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) tsum += (int)loc[e];
+        for (int e = 0; e < PER; ++e) tsum += loc_ok(e) ? (int)loc[e] : 0;
         if (t == 0) {
             sm.sel.T = NB - 1;
             sm.sel.below = 0;
@@ -1291,7 +1319,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
             // count under T
 #pragma unroll
             for (int e = 0; e < PER; ++e) {
-                const int nxt = run + (int)loc[e];
+                const int nxt = run + (loc_ok(e) ? (int)loc[e] : 0);
                 if ((int64_t)run < k_eff && (int64_t)nxt >= k_eff) {
                     sm.sel.T = t * PER + e;
                     sm.sel.below = run;
@@ -1309,6 +1337,10 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     }
     __syncthreads();
     const int T = uni(sm.sel.T);
+    // the query heads as MFMA operands (they arrive during the selection; read
+    // earlier, the candidate pass would wait for them)
+    bf16x8 qa[4];
+    load_q_operand<G>(a.q + ((int64_t)b * Hq + kv * G) * kHeadDim, qa);
     // ---- score-T and below-T keys in the items before this one: from the
     // window when it holds bins T - 1 and T, else read (again) until every
     // entry carries this launch's tag
@@ -1318,8 +1350,8 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     if (in_win) {
 #pragma unroll
         for (int k = 0; k < WPT; ++k) {
-            const int i = t + k * kPoll, cc = i / kWin, bin = wlo + i % kWin;
-            if (t < kPoll && cc < s) {
+            const int i = t + k * kPoll, bin = wlo + i % kWin;
+            if (win_ok(k)) {
                 bad |= (win[k] & ~0xFFFFFFFFull) != tag;
                 const long long cum = (uint32_t)win[k];
                 if (bin == T) tie += cum;
@@ -1590,15 +1622,15 @@ struct Item {
     int u, i;
 };
 
-// PRO(u, p) for every unit and part, then WORK(u, c) unit by unit.  With
-// tails_last (set by the host only when the whole grid is resident at once),
-// each unit's last item, which often holds just the few keys past a multiple
-// of the span, comes after every other item instead: blocks are dealt to the
-// XCDs in turn and to their CUs in order, so the grid's last blocks are the
-// ones that land as a third workgroup on a CU, and the light items are then
-// the ones sharing a CU with two full ones.
-__device__ __forceinline__ Item item_of(const FusedArgs &a, int tk) {
-    const int U = a.B * a.Hkv;
+// The tk-th item of a list of U units: PRO(u, p) for every unit and part,
+// then WORK(u, c) unit by unit.  With tails_last (set by the host only when
+// the whole grid is resident at once), each unit's last item, which often
+// holds just the few keys past a multiple of the span, comes after every
+// other item instead: blocks are dealt to the XCDs in turn and to their CUs
+// in order, so an XCD's last blocks are the ones that land as a third
+// workgroup on a CU, and the light items are then the ones sharing a CU
+// with two full ones.
+__device__ __forceinline__ Item item_in(const FusedArgs &a, int U, int tk) {
     Item it;
     if (tk < kProParts * U) {
         it.kind = 0; it.u = tk / kProParts; it.i = tk % kProParts;
@@ -1617,25 +1649,29 @@ __device__ __forceinline__ Item item_of(const FusedArgs &a, int tk) {
     return it;
 }
 
+__device__ __forceinline__ Item item_of(const FusedArgs &a, int tk) {
+    return item_in(a, a.B * a.Hkv, tk);
+}
+
 // WORK(u, c): scan the span, wait for the unit, select, gather, attend.
-template <int G>
+template <int G, bool LDS>
 __device__ __forceinline__ void item_work(const FusedArgs &a, int u, int c, Smem<G> &sm) {
-    const Slot cur = slot_of(a, u, c);
-    if (cur.p0 >= cur.p1) return;
+    Slot cur;
     uint32_t gen;
-    const int tc = scan_phase<G>(a, cur, gen, sm);
+    const int tc = scan_phase<G, LDS>(a, u, c, cur, gen, sm);
+    if (tc < 0) return;
     __syncthreads();  // the LDS histograms and the selection state share memory
-    sel_phase<G>(a, cur, uni(tc), (uint32_t)uni((int)gen), sm);
+    sel_phase<G, LDS>(a, cur, uni(tc), (uint32_t)uni((int)gen), sm);
 }
 
 // Three workgroups per CU (two for G = 8): the register budget the
 // compiler must meet.
-template <int G>
+template <int G, bool LDS>
 __global__ __launch_bounds__(kThreads, G <= 4 ? 3 : 2) void k_decode_fused(FusedArgs a) {
     __shared__ Smem<G> sm;
     const Item it = item_of(a, blockIdx.x);
     if (it.kind == 0) item_pro<G>(a, it.u, it.i, sm);
-    else item_work<G>(a, it.u, it.i, sm);
+    else item_work<G, LDS>(a, it.u, it.i, sm);
 }
 
 // ---------------------------------------------------------------- plan + launch
@@ -1700,9 +1736,11 @@ static hipError_t launch_g(const DecodePlan &p, FusedArgs &a, hipStream_t s) {
     a.tails_last = 0;
     if (a.n_chunks > 1 && hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_fused<G>, kThreads, 0) == hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_fused<G, true>, kThreads, 0) == hipSuccess)
         a.tails_last = (int64_t)a.n_items + kTailHeadroom <= (int64_t)per_cu * n_cu;
-    hipLaunchKernelGGL(k_decode_fused<G>, dim3(a.n_items), dim3(kThreads), 0, s, a);
+    // spans of kSpanUnit keys keep their scores in LDS between the phases
+    if (a.span <= kSpanUnit) hipLaunchKernelGGL((k_decode_fused<G, true>), dim3(a.n_items), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_decode_fused<G, false>), dim3(a.n_items), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
