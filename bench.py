@@ -571,13 +571,11 @@ def main():
     del off, off_ws
 
     # Other code lengths (the hash-length ablation): the same workload with
-    # r-bit codes over the same K/V rows, one cache (the codes of r = 32 and
-    # 64 bits, 17 and 34 MB, fit in the last-level cache, so they are
-    # flattered), prefill encode in place, then decode steps on the
-    # multi-launch path.
-    # Each code length gets its own rotation of layer caches (K/V copies and
-    # r-bit codes) sized as for the configurations, so that its codes are
-    # read from HBM and not the last-level cache.
+    # r-bit codes over the same K/V rows, prefill encode in place, then
+    # decode steps (the same single-launch kernel at every length).  Each
+    # code length gets its own rotation of layer caches (K/V copies and r-bit
+    # codes) sized as for the configurations, so that its codes are read
+    # from HBM and not the last-level cache.
     code_lengths = []
     for r in (32, 64, 256):
         w_r = torch.from_numpy(synth.gen_w_bits(spec, r)).to(dev)

@@ -10,7 +10,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libhata.so")
 
-SOURCES = ["api.cpp", "encode_exact.hip", "encode_rows.hip", "decode.hip", "recall.hip", "bits.hip",
+SOURCES = ["api.cpp", "encode_exact.hip", "encode_rows.hip", "decode.hip", "decode_r32.hip",
+           "decode_r64.hip", "decode_r128.hip", "decode_r256.hip", "recall.hip", "bits.hip",
            "train.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -122,15 +122,8 @@ hata_status hata_append(const hata_cache *c, const uint16_t *k_new, const uint16
 size_t hata_decode_workspace_bytes(const hata_cache *c, int32_t k_max) {
     if (!c || k_max < 0) return 0;
     if (c->head_dim != kHeadDim || !supported_bits(c->n_bits)) return 0;
-    if (c->n_bits != kBits) {
-        BitsPlan bp;
-        if (!make_bits_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, c->n_bits, k_max,
-                            &bp))
-            return 0;
-        return bp.total;
-    }
     DecodePlan p;
-    if (!make_decode_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, &p)) return 0;
+    if (!make_decode_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, c->n_bits, &p)) return 0;
     return p.total;
 }
 
@@ -143,21 +136,9 @@ static hata_status decode_common(const hata_cache *c, const uint16_t *k_new,
     if (st != HATA_OK) return st;
     if (!q || !w_h || !topk || !out || k_max < 0) return HATA_ERR_INVALID_ARG;
     if (!aligned16(q)) return HATA_ERR_INVALID_ARG;
-    if (c->n_bits != kBits) {
-        if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return HATA_ERR_INVALID_ARG;
-        BitsPlan bp;
-        if (!make_bits_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, c->n_bits, k_max,
-                            &bp))
-            return HATA_ERR_UNSUPPORTED;
-        if (!workspace || ws_bytes < bp.total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
-            return HATA_ERR_WORKSPACE;
-        hipError_t e = launch_decode_bits(bp, c->k, c->v, c->codes, c->seq_len, c->ctrl, k_new,
-                                          v_new, q, w_h, topk, out, workspace, sel_idx_out,
-                                          scores_out, static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
-    }
+    if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return HATA_ERR_INVALID_ARG;
     DecodePlan p;
-    if (!make_decode_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, &p))
+    if (!make_decode_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, c->n_bits, &p))
         return HATA_ERR_UNSUPPORTED;
     if (!workspace || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return HATA_ERR_WORKSPACE;
@@ -190,11 +171,10 @@ hata_status hata_decode_step_static(const hata_cache *c, const uint16_t *k_new,
                                     int32_t *sel_idx_out, uint16_t *scores_out, void *stream) {
     hata_status st = check_cache(c);
     if (st != HATA_OK) return st;
-    if (c->n_bits != kBits) return HATA_ERR_UNSUPPORTED;
     if (!k_new || !v_new || !q || !w_h || !topk || !out || k_max < 0) return HATA_ERR_INVALID_ARG;
-    if (!aligned16(q)) return HATA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new)) return HATA_ERR_INVALID_ARG;
     DecodePlan p;
-    if (!make_decode_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, &p))
+    if (!make_decode_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, c->n_bits, &p))
         return HATA_ERR_UNSUPPORTED;
     if (p.used > kStaticScratchBytes) return HATA_ERR_SCRATCH_LIMIT;
     hipError_t e = launch_decode_static(p, c->k, c->v, c->codes, c->seq_len, c->ctrl, k_new, v_new,

@@ -21,10 +21,10 @@ constexpr int kCtrlUnitBase = 16;
 
 // Decode-step plan: how the context is cut into scan chunks and attention
 // splits, and where each buffer sits in the workspace.  A pure function of
-// (batch, heads, max_ctx) so hata_decode_workspace_bytes and
+// (batch, heads, max_ctx, code length) so hata_decode_workspace_bytes and
 // hata_decode_attn agree.
 struct DecodePlan {
-    int B = 0, Hq = 0, Hkv = 0, G = 0, NB = 0;
+    int B = 0, Hq = 0, Hkv = 0, G = 0, R = 0, NB = 0;
     int64_t max_ctx = 0;
     int64_t span = 0;    // keys per work item (scan and selection of one span)
     int n_chunks = 0;    // work items per unit: ceil(max_ctx / span)
@@ -37,7 +37,7 @@ struct DecodePlan {
     size_t used = 0;
 };
 
-bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, DecodePlan *p);
+bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, int n_bits, DecodePlan *p);
 
 // ---- launchers (return hipSuccess or the launch error) ----
 

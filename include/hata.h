@@ -27,10 +27,9 @@
  *     unchanged or clamped as documented below.
  *   - Supported shapes: head_dim = 128, n_bits in {32, 64, 128, 256}, query
  *     heads a multiple G of KV heads with G in {1, 2, 4, 8}.  Other shapes
- *     return HATA_ERR_UNSUPPORTED.  n_bits = 128 (the pages' choice) runs
- *     the fused single-launch decode; the other code lengths (the pages'
- *     hash-length ablation, "Free parameters") run a multi-launch path with
- *     the same results by definition.
+ *     return HATA_ERR_UNSUPPORTED.  Every code length (128 is the pages'
+ *     choice; the others are their hash-length ablation, "Free
+ *     parameters") runs the same single-launch decode.
  *   - bf16 values are passed as their 16-bit patterns (uint16_t).
  *   - Reentrant: the library keeps no mutable global state.  Calls that use
  *     the same cache or workspace must be ordered by the caller (same
@@ -197,9 +196,8 @@ hata_status hata_append(const hata_cache *c, const uint16_t *k_new, const uint16
                         const int32_t *n_new, int32_t t_max, const float *w_h, void *stream);
 
 /* Bytes of device workspace hata_decode_attn / hata_decode_step need for
- * this cache: at n_bits = 128 a function of batch, heads and max_ctx; for
- * the other code lengths also of n_bits and k_max.  Returns 0 for an
- * unsupported or invalid cache. */
+ * this cache: a function of batch, heads, max_ctx and n_bits (k_max only
+ * has to be valid).  Returns 0 for an unsupported or invalid cache. */
 size_t hata_decode_workspace_bytes(const hata_cache *c, int32_t k_max);
 
 /*
@@ -266,7 +264,7 @@ hata_status hata_decode_step(const hata_cache *c, const uint16_t *k_new, const u
  * zero (a small fill kernel on `stream`), so calls may alternate between
  * caches of any shape; calls that overlap in time on one GPU (other streams,
  * other threads) share the array and race -- order them.
- * n_bits must be 128.  The array holds the decode workspace minus the score
+ * The array holds the decode workspace minus the score
  * rows of items longer than 8192 keys; caches whose layout needs more (for
  * example 64 sequences x 8 KV heads beyond 64K context) return
  * HATA_ERR_SCRATCH_LIMIT before anything is enqueued.  Arguments, results

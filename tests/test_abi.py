@@ -137,18 +137,26 @@ def test_workspace_plan(B, Hq, Hkv, N):
     assert hata.lib().hata_decode_workspace_bytes(None, 1) == 0
 
 
-@pytest.mark.parametrize("n_bits", [32, 64, 256])
-def test_workspace_plan_other_code_lengths(n_bits):
-    B, Hq, Hkv, N, k_max = 4, 32, 8, 131072, 2048
+@pytest.mark.parametrize("n_bits", [32, 64, 128, 256])
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(4, 32, 8, 131072), (1, 8, 2, 1000), (2, 16, 2, 600000)])
+def test_workspace_plan_code_lengths(n_bits, B, Hq, Hkv, N):
+    # Every code length runs the same step, so the workspace is one layout:
+    # per unit the launch generation, the tagged query and new-key code
+    # words ((G + 1) r / 32 of them), the unit histogram (G r + 2 words), per
+    # work item (spans of 8192 keys, or multiples of it past 64 items) a
+    # tagged cumulative histogram (G r + 1 bins) and the softmax partials,
+    # then the u16 score rows; each section 256-byte aligned.
     c = cache(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, max_ctx=N, n_bits=n_bits)
-    n = hata.lib().hata_decode_workspace_bytes(ctypes.byref(c), k_max)
+    n = hata.lib().hata_decode_workspace_bytes(ctypes.byref(c), 2048)
     units, G = B * Hkv, Hq // Hkv
-    # u16 scores, per-span histograms (8192-key spans, G r + 1 bins), the
-    # selection, per-chunk softmax states (256 keys, G heads x 130 floats)
-    span_hist = units * (N // 8192) * ((G * n_bits + 1 + 63) // 64 * 64) * 4
-    lo = units * N * 2 + span_hist + units * k_max * 4 + units * (k_max // 256) * G * 130 * 4
-    assert lo <= n <= lo + (1 << 20)
-    assert n % 256 == 0
+    span = -(-N // (64 * 8192)) * 8192
+    C = -(-N // span)
+    NB = G * n_bits + 1
+    a256 = lambda x: -(-x // 256) * 256
+    sections = [units * 4, units * (G + 1) * (n_bits // 32) * 8, units * (NB + 1) * 4,
+                units * C * NB * 8, units * C * G * 2 * 4, units * C * G * 128 * 4,
+                units * (-(-N // 64) * 64) * 2]
+    assert n == sum(a256(x) for x in sections)
 
 
 def recall(c, q=FAKE, topk=FAKE, k_max=16, sel=FAKE, sc=FAKE, ov=FAKE, tie=FAKE, ex=None,
@@ -197,15 +205,18 @@ def test_static_step_validation():
     # Every failure below is decided on the host before anything is enqueued
     # (and before the scratch's address is looked up).
     E = hata
-    assert static_step(cache(n_bits=64)) == E.HATA_ERR_UNSUPPORTED
+    assert static_step(cache(n_bits=48)) == E.HATA_ERR_UNSUPPORTED
     assert static_step(cache(head_dim=64)) == E.HATA_ERR_UNSUPPORTED
     assert static_step(cache(k=0)) == E.HATA_ERR_INVALID_ARG
     assert static_step(cache(), k_new=0) == E.HATA_ERR_INVALID_ARG
     assert static_step(cache(), v_new=0) == E.HATA_ERR_INVALID_ARG
     assert static_step(cache(), q=FAKE + 8) == E.HATA_ERR_INVALID_ARG
+    assert static_step(cache(), k_new=FAKE + 8) == E.HATA_ERR_INVALID_ARG
     assert static_step(cache(), k_max=-1) == E.HATA_ERR_INVALID_ARG
     # 64 sequences x 8 KV heads at 200K context: the span histograms alone
     # take 512 units x 25 items x 513 bins x 8 B = 52 MB > the 32 MiB scratch
     big = cache(batch=64, n_q_heads=32, n_kv_heads=8, max_ctx=200000)
     assert static_step(big) == E.HATA_ERR_SCRATCH_LIMIT
+    assert static_step(cache(batch=64, n_q_heads=32, n_kv_heads=8, max_ctx=200000,
+                             n_bits=32)) == E.HATA_ERR_SCRATCH_LIMIT
     assert "scratch" in hata.hata_status_string(E.HATA_ERR_SCRATCH_LIMIT)

@@ -2,8 +2,7 @@
 never synchronises and launches only on the given stream): every replay
 equals the same step run eagerly on a twin workload -- outputs, selection,
 codes and lengths bit-identical -- with eager work and synchronisations
-between the replays.  Both the fused 128-bit kernel and the multi-launch
-path of the other code lengths are captured.
+between the replays, at two code lengths (one kernel serves every length).
 """
 from __future__ import annotations
 
