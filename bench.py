@@ -69,6 +69,12 @@ def parse():
                     help="print the HBM traffic block from two rocprofv3 --pmc "
                          "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of "
                          "'bench.py --copy-probe' runs, then exit")
+    ap.add_argument("--phases", action="store_true",
+                    help="print the decode step's per-phase breakdown (device timestamps "
+                         "from the trace build of the library) and exit")
+    ap.add_argument("--phases-child", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--phases-raw", default=None, help="with --phases: also save the raw "
+                    "timestamps (steps x workgroups x 16, uint64) to this .npy file")
     return ap.parse_args()
 
 
@@ -351,10 +357,119 @@ def _cpu_model():
     return None
 
 
+PHASES = [  # (index, name) of the decode kernel's phase marks (Phase in decode_fused.h)
+    (1, "query codes in LDS"), (2, "span scanned"), (3, "histograms published"),
+    (4, "candidates listed"), (5, "cut T known"), (6, "earlier spans' counts known"),
+    (7, "selection made"), (8, "attention done"), (9, "partial stored"),
+    (11, "item done")]
+
+
+def phases_child(args):
+    """Run under libhata_trace.so: the headline workload's decode steps,
+    back to back over the layer rotation, each writing its workgroups' phase
+    timestamps (100 MHz device clock) into a buffer of its own; prints the
+    per-phase breakdown as a markdown table."""
+    import ctypes
+    import numpy as np
+    import torch
+    import hash_top_sparse_encode_amd as hata
+    import synth
+    from workload import GpuWorkload, bf16_dev
+
+    lib = hata.lib()
+    if not hasattr(lib, "hata_phase_trace"):
+        raise SystemExit(f"{hata.LIB_PATH} is not the trace build (libhata_trace.so)")
+    lib.hata_phase_trace.restype = ctypes.c_int64
+    lib.hata_phase_trace.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+    dev = torch.device("cuda:0")
+    spec = synth.config(args.config)
+    B, Hkv = spec.B, spec.Hkv
+    L = max(1, args.layers)
+    n = args.steps
+    base = GpuWorkload(spec, dev, extra_ctx=(args.warmup + n) // L + 2)
+    caches = [(base.cache, base.ws)]
+    for i in range(1, L):
+        c = hata.HataCache(B, spec.Hq, Hkv, base.max_ctx, device=dev, k=base.cache.k.clone(),
+                           v=base.cache.v.clone(), codes=base.cache.codes.clone(),
+                           seq_len=base.n_pre.clone())
+        caches.append((c, hata.alloc_workspace(c, base.k_max)))
+    base.cache.seq_len.copy_(base.n_pre)
+    k_new, v_new = base.k_new.view(B, Hkv, 128), base.v_new.view(B, Hkv, 128)
+    queries = [base.q] + [bf16_dev(synth.gen_q(spec, i), dev) for i in range(1, QUERIES)]
+    out = torch.empty_like(base.out)
+    items = lib.hata_phase_trace(ctypes.byref(base.cache.c_struct()), None, 0)
+    buf = torch.zeros((n, items, 16), dtype=torch.int64, device=dev)
+
+    def step(s):
+        c, ws = caches[s % L]
+        hata.hata_decode_step(c, k_new, v_new, queries[s % QUERIES], base.w, base.topk,
+                              base.k_max, out, ws)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    for s in range(n):
+        lib.hata_phase_trace(ctypes.byref(caches[s % L][0].c_struct()), buf[s].data_ptr(), items)
+        step(args.warmup + s)
+    lib.hata_phase_trace(None, None, 0)
+    torch.cuda.synchronize()
+    if any(c.status() for c, _ in caches):
+        raise SystemExit("device status flags set")
+    tr = buf.cpu().numpy().view(np.uint64)
+    if args.phases_raw:
+        np.save(args.phases_raw, tr)
+    kind = (tr[0, :, 15] >> 31) & 1
+    work, pro = kind == 1, kind == 0
+    med, last, cnt, prod, pros = ({k: [] for k, _ in PHASES}, {k: [] for k, _ in PHASES},
+                                  {k: [] for k, _ in PHASES}, [], [])
+    for s in range(n):
+        t = tr[s].astype(np.int64)
+        t0 = t[:, 0].min()
+        us = (t - t0) * 0.01
+        for k, _ in PHASES:
+            col = us[work, k][t[work, k] >= t0]  # marks this launch wrote
+            cnt[k].append(len(col))
+            if len(col):
+                med[k].append(np.median(col))
+                last[k].append(col.max())
+        prod.append(np.median(us[pro, 1]))
+        pros.append(us[pro, 1].max())
+    m = lambda v: f"{np.median(v):.2f}" if len(v) else "-"
+    rows = [("first workgroup starts", "0.00", "0.00", int(len(kind))),
+            ("PRO: query and new-key codes published", m(prod), m(pros), int(pro.sum()))]
+    rows += [(f"WORK: {name}", m(med[k]), m(last[k]), int(np.median(cnt[k]))) for k, name in PHASES]
+    print(f"Decode-step phases, {spec.name} (r = 128, {L} layer caches, {n} steps traced "
+          f"after {args.warmup}); microseconds from the launch's first workgroup start, "
+          "median over the steps.\n")
+    print("| phase | median work item | last work item | items with the mark |")
+    print("|---|---:|---:|---:|")
+    for name, a, b, c in rows:
+        print(f"| {name} | {a} | {b} | {c} |")
+    print(f"\n{int(work.sum())} work items and {int(pro.sum())} query-code parts per launch; "
+          "'last' of 'item done' is the end of the step's last workgroup.")
+
+
+def phases_parent(args):
+    """--phases: the breakdown runs in a child process that loads the trace
+    build of the library (nothing here touches the GPU)."""
+    import subprocess
+    from hash_top_sparse_encode_amd import _build
+    env = dict(os.environ, HATA_LIB_PATH=_build.TRACE_LIB_PATH)
+    cmd = [sys.executable, os.path.abspath(__file__), "--phases-child", "--config",
+           str(args.config), "--steps", str(args.steps), "--warmup", str(args.warmup),
+           "--layers", str(args.layers)] + (["--phases-raw", args.phases_raw] if args.phases_raw else [])
+    sys.exit(subprocess.run(cmd, env=env).returncode)
+
+
 def main():
     args = parse()
     if args.pmc_summary:
         print(pmc_summary(*args.pmc_summary))
+        return
+    if args.phases:
+        phases_parent(args)
+    if args.phases_child:
+        phases_child(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path "

@@ -10,6 +10,13 @@
 
 namespace hata {
 
+#ifdef HATA_PHASE_TRACE
+// The trace buffer of the next launches (hata_phase_trace); a diagnostic of
+// the trace build only.
+static uint64_t *g_trace = nullptr;
+static int g_trace_items = 0;
+#endif
+
 // ---------------------------------------------------------------- plan + launch
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -100,6 +107,10 @@ hipError_t launch_decode(const DecodePlan &p, uint16_t *k_cache, uint16_t *v_cac
     // both so that the waits give up and the stall path can be exercised.
     a.spin_limit = kSpinLimit;
     a.poll_limit = kPollLimit;
+#ifdef HATA_PHASE_TRACE
+    a.trace = g_trace;
+    a.trace_items = g_trace_items;
+#endif
     if (const char *e = getenv("HATA_DECODE_WAIT_LIMIT")) {
         const long v = strtol(e, nullptr, 10);
         if (v >= 0 && v < a.poll_limit) a.spin_limit = a.poll_limit = (int)v;
@@ -179,3 +190,19 @@ hipError_t launch_decode_static(const DecodePlan &p, uint16_t *k_cache, uint16_t
 }
 
 }  // namespace hata
+
+#ifdef HATA_PHASE_TRACE
+// Trace build only: the decode launches that follow write their phase
+// timestamps (see Phase in decode_fused.h) into buf, a device array of
+// n_items x 16 uint64 (rows of workgroups beyond n_items are not written);
+// null stops tracing.  Returns the workgroups of a launch for this cache
+// (0 if the cache is not supported), so a caller can size buf first.
+extern "C" int64_t hata_phase_trace(const hata_cache *c, uint64_t *buf, int64_t n_items) {
+    hata::g_trace = buf;
+    hata::g_trace_items = buf ? (int)(n_items < INT32_MAX ? n_items : INT32_MAX) : 0;
+    hata::DecodePlan p;
+    if (!c || !hata::make_decode_plan(c->batch, c->n_q_heads, c->n_kv_heads, c->max_ctx, c->n_bits, &p))
+        return 0;
+    return p.n_items;
+}
+#endif

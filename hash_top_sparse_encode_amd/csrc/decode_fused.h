@@ -129,7 +129,41 @@ struct FusedArgs {
     int n_items;
     int spin_limit;          // bound of the query-code wait (re-reads by one wave)
     int poll_limit;          // bound of the histogram waits (block-wide re-reads)
+    uint64_t *trace;         // phase timestamps (HATA_PHASE_TRACE builds), null: none
+    int trace_items;         // workgroups the trace buffer has rows for
 };
+
+// Phase timestamps: in builds with HATA_PHASE_TRACE (libhata_trace.so),
+// thread 0 of each workgroup writes the 100 MHz real-time clock at each of
+// these points into trace[block][phase] (16 words per block), and the item
+// it runs into word 15 (kind << 31 | unit << 8 | part or span).  Other
+// builds compile the markers to nothing.
+enum Phase {
+    kPhStart = 0,      // first instruction
+    kPhCodes = 1,      // PRO: code words published; WORK: query codes in LDS
+    kPhScanned = 2,    // WORK: the span's scores counted
+    kPhPublished = 3,  // WORK: histograms published
+    kPhListed = 4,     // WORK: candidates listed
+    kPhCut = 5,        // WORK: the unit's cut T known
+    kPhTies = 6,       // WORK: the earlier items' below-T and score-T counts known
+    kPhSelected = 7,   // WORK: the span's selection made (attention starts)
+    kPhAttended = 8,   // WORK: attention done
+    kPhPartial = 9,    // WORK: partial stored and counted
+    kPhMerged = 10,    // the unit's last item: every partial read
+    kPhEnd = 11,       // the workgroup's item done
+    kPhItem = 15,
+};
+#ifdef HATA_PHASE_TRACE
+#define HATA_PHASE(a, k)                                                                        \
+    do {                                                                                        \
+        if ((a).trace && threadIdx.x == 0 && (int)blockIdx.x < (a).trace_items)                 \
+            (a).trace[(int64_t)blockIdx.x * 16 + (k)] = __builtin_amdgcn_s_memrealtime();        \
+    } while (0)
+#else
+#define HATA_PHASE(a, k) \
+    do {                 \
+    } while (0)
+#endif
 
 // ---------------------------------------------------------------- coherent access
 
@@ -438,6 +472,7 @@ __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Sm
             if (v == G && sl.app) st_dev(a.codes + ((int64_t)u * a.max_ctx + sl.l0) * W + part, word);
         }
     }
+    HATA_PHASE(a, kPhCodes);
 }
 
 // ---------------------------------------------------------------- scanners
@@ -865,6 +900,7 @@ __device__ __forceinline__ int scan_phase(const FusedArgs &a, int u, int c, Slot
     if (wv == 0) slot_fetch_qcodes<G, R>(a, cur, sm);
     __syncthreads();
     gen = sm.scan.gen;
+    HATA_PHASE(a, kPhCodes);
     uint32_t qc[G][W];
     qcodes_sgpr<G, R>(sm, qc);
     QPlanes<G, W> qp;
@@ -879,6 +915,7 @@ __device__ __forceinline__ int scan_phase(const FusedArgs &a, int u, int c, Slot
 #pragma unroll
     for (int d = 0; d < D; ++d)
         if ((n_grp - 1) * D + d < n_sub) slot_score<G, R, LDS>(a, cur, (n_grp - 1) * D + d, buf[d], qp, sm);
+    HATA_PHASE(a, kPhScanned);
     return slot_publish<G, R>(a, cur, gen, sm);
 }
 
@@ -1351,6 +1388,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     // ---- meanwhile the span's candidates: every key up to the candidate
     // cut tc, in index order (spans kept in LDS)
     const int n_cand = in_lds ? uni(list_candidates<G, R>(pf, tc, woff, sm)) : -1;
+    HATA_PHASE(a, kPhListed);
     // ---- the cut T, once every item of the unit has added its counts
     // (they then sum to len)
     for (int spins = 0;; ++spins) {
@@ -1386,6 +1424,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     }
     __syncthreads();
     const int T = uni(sm.sel.T);
+    HATA_PHASE(a, kPhCut);
     // the query heads as MFMA operands (they arrive during the selection; read
     // earlier, the candidate pass would wait for them)
     bf16x8 qa[4];
@@ -1434,6 +1473,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     int ties_s, below_s;  // both at most the context length
     block_sum2_256((int)tie, (int)lo, sm.sel.red, &ties_s, &below_s);
     const int64_t ties_b = uni(ties_s), below_b = uni(below_s);
+    HATA_PHASE(a, kPhTies);
     const int64_t quota = k_eff - uni(sm.sel.below);  // keys of score T to take, lowest index first
     const int64_t rem_quota = quota - ties_b > 0 ? quota - ties_b : 0;
     int64_t out_pos = below_b + (ties_b < quota ? ties_b : quota);
@@ -1496,6 +1536,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
                 if (gp >= 0 && gp < a.k_max) sel_u[gp] = (int32_t)(s0 + sm.sel.list[i]);
             }
         }
+        HATA_PHASE(a, kPhSelected);
         const int app_off = (app_row >= s0 && app_row < s1) ? (int)(app_row - s0) : -1;
         attend_mfma<G>(Ku + s0 * kHeadDim, Vu + s0 * kHeadDim, kapp, vapp, app_off, sm.sel.list,
                        n_sel, qa, sm.sel.vst[wv], sm.sel.pb[wv], m, l, o);
@@ -1521,6 +1562,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
             out_pos += batch_sel;
             ties_acc += batch_eq;
             // the batch's selections through the attention
+            if (rb == s0) HATA_PHASE(a, kPhSelected);
             const int app_off = (app_row >= rb && app_row < rb + kListCap) ? (int)(app_row - rb) : -1;
             attend_mfma<G>(Ku + rb * kHeadDim, Vu + rb * kHeadDim, kapp, vapp, app_off, sm.sel.list,
                            batch_sel, qa, sm.sel.vst[wv], sm.sel.pb[wv], m, l, o);
@@ -1528,6 +1570,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
         }
     }
 
+    HATA_PHASE(a, kPhAttended);
     // ---- the waves' states into LDS, then combined per output
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -1579,6 +1622,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
 
     // ---- the last split of the unit merges all partials in split order
     const int prev = wg_signal(unit_ctr(a, u, kAttn));
+    HATA_PHASE(a, kPhPartial);
     if (t == 0) sm.sel.last = (prev == n_splits_u - 1);
     __syncthreads();
     if (!sm.sel.last) return false;
@@ -1625,6 +1669,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
         L += __shfl_xor(L, 16, 64);
         Lk[k] = L + __shfl_xor(L, 32, 64);
     }
+    HATA_PHASE(a, kPhMerged);
     float O[PPT][2];
 #pragma unroll
     for (int k = 0; k < PPT; ++k) O[k][0] = O[k][1] = 0.f;
@@ -1712,6 +1757,7 @@ __device__ __forceinline__ void item_work(const FusedArgs &a, int u, int c, Smem
     uint32_t gen;
     const int tc = scan_phase<G, R, LDS>(a, u, c, cur, gen, sm);
     if (tc < 0) return;
+    HATA_PHASE(a, kPhPublished);
     __syncthreads();  // the LDS histograms and the selection state share memory
     sel_phase<G, R, LDS>(a, cur, uni(tc), (uint32_t)uni((int)gen), sm);
 }
@@ -1721,9 +1767,16 @@ __device__ __forceinline__ void item_work(const FusedArgs &a, int u, int c, Smem
 template <int G, int R, bool LDS>
 __global__ __launch_bounds__(kThreads, G <= 4 ? 3 : 2) void k_decode_fused(FusedArgs a) {
     __shared__ Smem<G, R> sm;
+    HATA_PHASE(a, kPhStart);
     const Item it = item_of<R>(a, blockIdx.x);
     if (it.kind == 0) item_pro<G, R>(a, it.u, it.i, sm);
     else item_work<G, R, LDS>(a, it.u, it.i, sm);
+#ifdef HATA_PHASE_TRACE
+    HATA_PHASE(a, kPhEnd);
+    if (a.trace && threadIdx.x == 0 && (int)blockIdx.x < a.trace_items)
+        a.trace[(int64_t)blockIdx.x * 16 + kPhItem] =
+            ((uint64_t)it.kind << 31) | ((uint64_t)it.u << 8) | (uint64_t)it.i;
+#endif
 }
 
 // ---------------------------------------------------------------- launch
