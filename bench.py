@@ -44,8 +44,9 @@ LAYERS = 8
 QUERIES = 7  # distinct step queries, coprime with LAYERS: 56 (layer, query) pairs
 COPY_PROBE_BYTES = 256 << 20
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_decode_fused_cfg3_hbm_traffic.md")
-DECODE_SOURCES = ("decode.hip", "device_util.h", "hata_internal.h")
-DECODE_KERNEL = "k_decode_fused<4>"
+DECODE_SOURCES = ("decode.hip", "decode_fused.h", "decode_r128.hip", "device_util.h",
+                  "hata_internal.h")
+DECODE_KERNEL = "k_decode_fused<4, 128, true>"
 
 
 def parse():
@@ -773,7 +774,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_decode_fused<4> (hata_decode_step: append, query codes, Hamming "
+            "kernel": "k_decode_fused<4, 128, true> (hata_decode_step: append, query codes, Hamming "
                       "scan, select, gather-attention, merge)",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
