@@ -79,13 +79,14 @@ typedef enum {
 #define HATA_DEV_STALL 0x10          /* a decode wait timed out: outputs of that call invalid */
 
 /*
- * Scheduling assumption of the 128-bit decode (hata_decode_attn and
- * hata_decode_step at n_bits = 128).  The step is one kernel launch whose
+ * Scheduling assumption of the decode (hata_decode_attn and
+ * hata_decode_step, every code length).  The step is one kernel launch whose
  * workgroups hand results to each other: a work item waits for the query
  * codes of its (sequence, KV head) unit and, before it selects, for the
  * histogram counts of every other work item of that unit.  This needs those
  * other items to be running: workgroups start in block order and a unit's
- * items (at most 68) fit on the GPU together.  When the whole launch fits on
+ * items (at most 72: up to 8 query-code parts and 64 spans) fit on the GPU
+ * together.  When the whole launch fits on
  * the GPU with 64 workgroup slots to spare, the items are also reordered for
  * balance, which needs every workgroup of the launch resident at once.  Both
  * hold on a GPU that no other kernel occupies while the step runs; kernels
