@@ -125,6 +125,16 @@ def test_config2_r256_sampled(gpu):
     run_spec(synth.config(2), gpu, 256, units=[(0, 0), (7, 7)])
 
 
+@pytest.mark.parametrize("n_bits", [64, 256])
+def test_long_context_other_lengths(gpu, n_bits):
+    # Past 512K keys a work item spans 16384 keys and keeps its scores in
+    # the workspace instead of LDS (the kernel's second form); G = 8 at 256
+    # bits has 2049 score bins.
+    G = 4 if n_bits == 64 else 8
+    spec = synth.custom(f"long r{n_bits}", 1, 2 * G, 2, [600000], [9375], [600], seed=50 + n_bits)
+    run_spec(spec, gpu, n_bits, units=[(0, 1)])
+
+
 def test_recall_r256_g8(gpu):
     # 8 x 256 + 1 = 2049 score bins in the tie bucket
     spec = SPECS[3]

@@ -22,9 +22,9 @@ def _static_step(wl, sel, sc):
                                         wl.k_max, wl.out, sel_idx_out=sel, scores_out=sc)
 
 
-def _compare(spec, gpu, first_static=False):
-    ref = GpuWorkload(spec, gpu, extra_ctx=2)
-    got = GpuWorkload(spec, gpu, extra_ctx=2)
+def _compare(spec, gpu, n_bits=128):
+    ref = GpuWorkload(spec, gpu, extra_ctx=2, n_bits=n_bits)
+    got = GpuWorkload(spec, gpu, extra_ctx=2, n_bits=n_bits)
     out_r, sel_r, sc_r = ref.step(debug=True)
     sel, sc = got.debug_buffers()
     _static_step(got, sel, sc)
@@ -52,3 +52,14 @@ def test_static_step_matches_workspace_step_two_calls(gpu):
     _compare(big, gpu)
     print("[no-alloc] second call: 2 x 4 units, G = 2", flush=True)
     _compare(small, gpu)
+
+
+def test_static_step_other_code_lengths(gpu):
+    # every code length runs the same step on the static scratch: 256-bit
+    # codes, then a smaller 32-bit cache on what the first call left
+    big = synth.custom("static r256", 2, 32, 8, [30000, 12000], [470, 190], [30, 12], seed=43)
+    small = synth.custom("static r32", 2, 8, 2, [5000, 700], [80, 11], [5, 1], seed=44)
+    print("[no-alloc] r = 256: 2 x 8 units up to 30K keys", flush=True)
+    _compare(big, gpu, n_bits=256)
+    print("[no-alloc] r = 32: 2 x 2 units, G = 4", flush=True)
+    _compare(small, gpu, n_bits=32)
