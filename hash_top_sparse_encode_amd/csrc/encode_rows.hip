@@ -4,37 +4,53 @@
 // Algorithm 1 in the Figure 2 caption).  Used for hata_encode_keys,
 // hata_encode_keys_nbits and prefill appends from 64 rows on.
 //
-// Exactness.  W_H is split into two bf16 terms, W = W_hi + W_lo + res with
-// |res| <= 2^-16 |W|, and y' = x W_hi + x W_lo is accumulated in fp32 by
+// Exactness.  Column j of W_H is scaled to unit norm, W'_j = fl(W_j 2^e_j m_j)
+// (a power of two, exact unless an element drops below the normal range, then
+// a factor m_j in [1, 2), one rounding of 2^-24 per element), so that
+// ||W'_j||_2 <= 1 + 2^-16; a sign is unchanged by a positive scale.  W' is
+// split into two bf16 terms, W' = W'_hi + W'_lo + res with
+// |res| <= 2^-16 |W'|, and y' = x W'_hi + x W'_lo is accumulated in fp32 by
 // v_mfma_f32_16x16x32_bf16 (bf16 x bf16 products are exact in fp32), so
-// |y' - x W| <= (2^-16 + gamma_256 (1 + 2^-7)) sum_t |x_t||W_tj|
-//            <= 3.1e-5 ||x||_2 ||W_:j||_2,
-// and the sequential double sum that defines a bit is within 1.5e-14 of the
-// same quantity (Higham, Accuracy and Stability of Numerical Algorithms,
-// ch. 3-4).  A bit with |y'| > 2^-14 ||x|| ||W_:j|| + 2^-100 has the sign of
-// y'.  Every other bit is recomputed: the defining sequential double sum
-// itself, one lane per bit.  Rows or columns of zeros give exactly 0 (bit 0)
-// and skip the band test.
+//   |y' - 2^e_j m_j x W_j| <= (2^-16 + 2^-24 + gamma_256 (1 + 2^-7))
+//                             sum_t |x_t||W'_tj| <= 3.2e-5 ||x||_2
+// (Cauchy-Schwarz; Higham, Accuracy and Stability of Numerical Algorithms,
+// ch. 3-4), and the sequential double sum that defines a bit is within
+// 1.5e-14 of x W.  So a
+// bit with |y'| > th(x) = 2^-14 (1 + 2^-10) sqrt(ss) + 2^-72, ss the fp32 sum
+// of squares of the row, has the sign of y'.  (The 2^-72 covers squares and
+// products below the normal range, flushed or not.)  Every other bit is
+// recomputed: the defining sequential double sum itself, one lane per bit.
+// Rows of zeros give 0 (every bit 0), columns of zeros give 0, and a row with
+// a non-finite value (threshold +inf) or a column with one (its W' taken as
+// 0) sends its bits to the exact sum.
 //
-// Work split.  One 768-thread workgroup per CU for one head (grid.y); its
-// twelve waves work independently, with no barrier after the set-up: wave w
-// takes 32-row groups w, w + 12 P, ... of the head (P workgroups per head),
+// Work split.  One 512-thread workgroup per CU for one head (grid.y); its
+// eight waves work independently, with no barrier after the set-up: wave w
+// takes 64-row groups w, w + 8 P, ... of the head (P workgroups per head),
 // and while it computes one group the next group's rows are already loading
-// into a second set of registers.  For a group, lane (g, c) of M tile m holds
-// row 16 m + c, dims 32 j + 8 g .. + 8 for k step j (eight 16-byte loads,
-// each instruction reading 64 contiguous bytes of 16 rows); the row norms
-// follow, then r / 16 column tiles: the B operands of a tile (bf16 high and
-// low parts of W_H, laid out per lane in LDS at the set-up) are read from
-// LDS, 2 M tiles x 4 k steps x 2 parts of MFMA give y' for 32 rows x 16
-// bits, the band test decides the bits by ballot, and lane L collects the
-// bits of row L, then stores row L's r / 32 code words.  In-band bits are
-// stored as 0 and listed in LDS (group, row, column); between groups, once
-// the list is half full, and at the end, the wave resolves them (one lane per
-// bit runs the defining sequential double sum, with W_H's column from LDS
-// for r <= 128 or from memory for r = 256) and sets the bits that are 1.
+// into a second set of registers.  The product is taken transposed,
+// y'^T = W'^T x^T: the A operand is a 16-column tile of W'^T (its bf16 high
+// and low parts, laid out per lane in LDS at the set-up and read once per
+// tile for all 64 rows), the B operand the rows: lane (g, c) of row tile t
+// holds row 16 t + c, dims 32 j + 8 g .. + 8 for k step j.  The result then
+// gives lane (g, c) the values of row 16 t + c at columns 16 n + 4 g + i,
+// i < 4, so the threshold is one per lane and row tile.  Per column tile,
+// the band test is one min over the lane's four |y'| per row tile; the sign
+// bits are shifted into a per-lane word (v_alignbit), two column tiles per
+// code word; after the last tile, lane swaps across the four lanes of a row
+// (v_permlane32_swap, v_permlane16_swap) OR the pieces so that lane (g, c)
+// holds code word g (r <= 128) or words 2 g, 2 g + 1 (r = 256) of its row,
+// which it stores.  In-band bits get the provisional sign of y' and are
+// listed in LDS (group, row, column); between groups, once the list is half
+// full, and at the end, the wave resolves them (one lane per bit runs the
+// defining sequential double sum, with W_H's column from LDS for r <= 128 or
+// from memory for r = 256) and sets or clears the bit.  A group with more
+// in-band bits than the list holds is computed entirely by the exact sum.
 #include "device_util.h"
 #include "hata_internal.h"
 #include "../../include/hata.h"
+
+#include <climits>
 
 namespace hata {
 
@@ -45,11 +61,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t uvec4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRThreads = 768;
+constexpr int kRThreads = 512;
 constexpr int kRWaves = kRThreads / 64;
-constexpr int kRGroup = 32;      // rows per wave group (two M tiles)
+constexpr int kRTiles = 4;                 // row tiles of 16 per group
+constexpr int kRGroup = 16 * kRTiles;      // rows per wave group
 constexpr int kRSegLds = 1024;   // batch entries whose lengths are kept in LDS
 constexpr int kRList = 128;      // in-band bits a wave lists before resolving them
+// s_waitcnt vmcnt(16) (vmcnt low bits 3:0, high bits 15:14), expcnt and
+// lgkmcnt left at their maxima
+constexpr int kWaitAllButPrefetch = (1 << 14) | (0x7 << 4) | (0xF << 8);
 
 struct RowsArgs {
     int mode;  // 0: flat rows, 1: cache append
@@ -74,15 +94,28 @@ struct RowsArgs {
 
 template <int R>
 struct RowsSmem {
-    uvec4 bop[R / 16][4][2][64];   // B operands: column tile, k step, high / low part, lane
-    float wt[R <= 128 ? R : 1][kHeadDim];  // W_H transposed (exact path, r <= 128)
-    float wnorm[R];                // column norms ||W_:j|| (1 + 2^-10); -inf: a zero column
+    uvec4 aop[R / 16][4][2][64];   // A operands: column tile, k step, high / low part, lane
+    // W_H transposed (exact path, r <= 128); rows padded so that lanes on
+    // different columns read different banks
+    float wt[R <= 128 ? R : 1][kHeadDim + 1];
+    int col_exp[R];                // column scale: a power of two 2^e_j (INT_MIN: W' taken as 0) ...
+    float col_mul[R];              // ... then a factor m_j in [1, 2)
+    uint32_t zcol[R / 32];         // columns of W_H that are all zero, a bit per column
     uint32_t lgrp[kRWaves][kRList];  // listed in-band bits: the group ...
     uint16_t lrc[kRWaves][kRList];   // ... and row << 8 | column
-    uint32_t xrow[kRWaves][64];    // a row staged for the exact path (bf16 pairs)
     int64_t seg_l0[kRSegLds];      // mode 1: each entry's length ...
     int32_t seg_rows[kRSegLds];    // ... and the rows it appends
     int last;
+};
+
+// Columns of W_H that are all zero, as one lane (g, c) needs them: the bits
+// of the code word(s) it stores (word 4 p + q(g) of pass p), and its columns
+// 16 (p PT + k) + 4 g + i of pass p at bit 4 (PT - 1 - k) + i (the layout of
+// the band flags).
+template <int R>
+struct ZeroCols {
+    uint32_t word[R == 256 ? 2 : 1];
+    uint32_t flags[R == 256 ? 2 : 1];
 };
 
 __device__ __forceinline__ bool rows_append_ok(int64_t len, int n, int t_max, int64_t max_ctx) {
@@ -97,6 +130,14 @@ struct RGroup {
     int nr;
 };
 
+// A value the whole wave reads at one address, through the scalar cache (a
+// vector load here would put an unknown number of loads in flight on some
+// paths, and the compiler would then wait for every load before the next use
+// of a prefetched group).  The lengths are not written while they are read.
+__device__ __forceinline__ int32_t uniform_load(const int32_t *p) {
+    return *(const __attribute__((address_space(4))) int32_t *)p;
+}
+
 template <int R>
 __device__ __forceinline__ RGroup group_of(const RowsArgs &a, const RowsSmem<R> &sm, int64_t gi) {
     RGroup e{0, 0, 0, 0};
@@ -109,8 +150,8 @@ __device__ __forceinline__ RGroup group_of(const RowsArgs &a, const RowsSmem<R> 
         e.l0 = sm.seg_l0[e.s];
         rows = sm.seg_rows[e.s];
     } else {
-        e.l0 = a.seq_len[e.s];
-        const int n = a.n_new[e.s];
+        e.l0 = uniform_load(a.seq_len + e.s);
+        const int n = uniform_load(a.n_new + e.s);
         rows = rows_append_ok(e.l0, n, a.t_max, a.max_ctx) ? n : 0;
     }
     e.nr = e.r0 < rows ? (int)(rows - e.r0 < kRGroup ? rows - e.r0 : kRGroup) : 0;
@@ -131,238 +172,393 @@ __device__ __forceinline__ int64_t cache_row(const RowsArgs &a, int h, const RGr
     return ((int64_t)e.s * a.Hkv + h) * a.max_ctx + e.l0 + e.r0 + r;
 }
 
-// Sum over the 64 lanes, in every lane: DPP within rows of 16 (xor 1, xor 2,
-// half-row and row mirrors), then the four row sums in order.
-__device__ __forceinline__ double dpp_f64(double v, int ctrl_id) {
-    const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
-    switch (ctrl_id) {
-        case 0: lo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false);
-                hi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, false); break;
-        case 1: lo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, false);
-                hi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, false); break;
-        case 2: lo = __builtin_amdgcn_update_dpp(0, lo, 0x141, 0xF, 0xF, false);
-                hi = __builtin_amdgcn_update_dpp(0, hi, 0x141, 0xF, 0xF, false); break;
-        default: lo = __builtin_amdgcn_update_dpp(0, lo, 0x140, 0xF, 0xF, false);
-                 hi = __builtin_amdgcn_update_dpp(0, hi, 0x140, 0xF, 0xF, false); break;
-    }
-    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-}
-__device__ __forceinline__ double lane_f64(double v, int l) {
-    const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
-    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ double dsum64(double v) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) v += dpp_f64(v, k);
-    return ((lane_f64(v, 0) + lane_f64(v, 16)) + lane_f64(v, 32)) + lane_f64(v, 48);
-}
-
-// Lane L keeps the code words of row L; set bit `col` of them to `bit` (col
-// and bit uniform).
+// The code words of row r of a group.
 template <int R>
-__device__ __forceinline__ void put_bit(uint32_t (&wd)[R / 32], int col, bool bit, bool mine) {
-#pragma unroll
-    for (int k = 0; k < R / 32; ++k)
-        if (mine && k == (col >> 5)) wd[k] = bit ? (wd[k] | (1u << (col & 31))) : (wd[k] & ~(1u << (col & 31)));
+__device__ __forceinline__ uint32_t *code_row(const RowsArgs &a, int h, const RGroup &e, int r) {
+    return a.mode == 0 ? a.codes_out + ((e.r0 + r) * a.n_heads + h) * (R / 32)
+                       : a.codes + cache_row(a, h, e, r) * (R / 32);
 }
 
-// The eight 16-byte A-operand loads of a group (lane (g, c): rows c and
-// 16 + c, dims 32 j + 8 g .. + 8).
+// The sixteen 16-byte B-operand loads of a group (lane (g, c): rows 16 t + c,
+// dims 32 j + 8 g .. + 8; each instruction reads 64 contiguous bytes of 16
+// rows).  A group without rows reads row 0 of the first entry instead.
 __device__ __forceinline__ void load_group(const RowsArgs &a, int h, const RGroup &e, int g, int c,
-                                           uvec4 (&xa)[2][4]) {
+                                           uvec4 (&xa)[kRTiles][4]) {
+    const RGroup ee = e.nr > 0 ? e : RGroup{0, 0, 0, 0};
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const uint16_t *src = src_row(a, h, e, 16 * m + c) + 8 * g;
+    for (int t = 0; t < kRTiles; ++t) {
+        const uint16_t *src = src_row(a, h, ee, 16 * t + c) + 8 * g;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xa[m][j] = *reinterpret_cast<const uvec4 *>(src + 32 * j);
+        for (int j = 0; j < 4; ++j) xa[t][j] = *reinterpret_cast<const uvec4 *>(src + 32 * j);
+    }
+}
+
+// Sum over the four lanes (g, c), g = 0 .. 3, of a column c, in every one of
+// them (the same association in each).
+__device__ __forceinline__ float sum_over_g(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const uint32_t su = __float_as_uint(s);
+    const auto q = __builtin_amdgcn_permlane16_swap(su, su, false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ uint32_t or_over_g(uint32_t v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    const uint32_t s = p[0] | p[1];
+    const auto q = __builtin_amdgcn_permlane16_swap(s, s, false, false);
+    return q[0] | q[1];
+}
+
+// Four words u0..u3 in each lane (g, c) -> the OR over g of u_g, in lane
+// (g, c): rows 0-1 and 2-3 of the wave trade halves, then rows 0/1 and 2/3.
+__device__ __forceinline__ uint32_t or_transpose4(uint32_t u0, uint32_t u1, uint32_t u2, uint32_t u3) {
+    const auto p = __builtin_amdgcn_permlane32_swap(u0, u2, false, false);
+    const uint32_t a = p[0] | p[1];   // rows 0, 1: u0 over g and g ^ 2; rows 2, 3: u2
+    const auto q = __builtin_amdgcn_permlane32_swap(u1, u3, false, false);
+    const uint32_t b = q[0] | q[1];   // rows 0, 1: u1; rows 2, 3: u3
+    const auto s = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    return s[0] | s[1];               // row g: u_g over all g
+}
+
+// The defining sum of bit `col` of a row (sequential, d = 0 .. 127; every
+// product of a bf16 and an fp32 value is exact in double).
+template <int R>
+__device__ __forceinline__ double exact_sum(const RowsSmem<R> &sm, const float *W, const uint16_t *xr,
+                                            int col) {
+    double y = 0.0;
+#pragma unroll 1
+    for (int d0 = 0; d0 < kHeadDim; d0 += 8) {
+        const uvec4 xv = *reinterpret_cast<const uvec4 *>(xr + d0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int d = d0 + 2 * q;
+            float w0, w1;
+            if constexpr (R <= 128) {
+                w0 = sm.wt[col][d];
+                w1 = sm.wt[col][d + 1];
+            } else {
+                w0 = W[(int64_t)d * R + col];
+                w1 = W[(int64_t)(d + 1) * R + col];
+            }
+            y = fma((double)__uint_as_float(xv[q] << 16), (double)w0, y);
+            y = fma((double)__uint_as_float(xv[q] & 0xFFFF0000u), (double)w1, y);
+        }
+    }
+    return y;
+}
+
+// Resolve a wave's listed in-band bits: one lane per bit runs the defining
+// sum and sets or clears the bit in the code word the wave has already stored
+// (with the provisional sign of y').  The wave first waits for its own
+// stores, so the word is in memory.
+template <int R>
+__device__ __forceinline__ void flush_list(const RowsArgs &a, RowsSmem<R> &sm, const float *W, int h, int count) {
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll 1
+    for (int b = lane; b < count; b += 64) {
+        const int64_t gi = sm.lgrp[wv][b];
+        const int rc = sm.lrc[wv][b], row = rc >> 8, col = rc & 255;
+        const RGroup e = group_of<R>(a, sm, gi);
+        const double y = exact_sum<R>(sm, W, src_row(a, h, e, row), col);
+        uint32_t *word = code_row<R>(a, h, e, row) + (col >> 5);
+        const uint32_t bit = 1u << (col & 31);
+        if (y > 0.0)
+            atomicOr(word, bit);
+        else
+            atomicAnd(word, ~bit);
+    }
+}
+
+// Every code word of a group by the defining sums (a group with more in-band
+// bits than the list holds: rows with a non-finite value, degenerate rows):
+// one lane per word.
+template <int R>
+__device__ __forceinline__ void exact_group(const RowsArgs &a, const RowsSmem<R> &sm, const float *W, int h,
+                                            const RGroup &e) {
+    constexpr int NW = R / 32;
+    const int lane = threadIdx.x & 63;
+#pragma unroll 1
+    for (int w = lane; w < e.nr * NW; w += 64) {
+        const int row = w / NW, k = w % NW;
+        const uint16_t *xr = src_row(a, h, e, row);
+        uint32_t word = 0u;
+#pragma unroll 1
+        for (int b = 0; b < 32; ++b)
+            if (exact_sum<R>(sm, W, xr, 32 * k + b) > 0.0) word |= 1u << b;
+        code_row<R>(a, h, e, row)[k] = word;
+    }
+}
+
+// Column tiles per pass: a pass yields four code words (two for r = 64, one
+// for r = 32) per row; r = 256 takes two passes over the group's registers.
+template <int R>
+constexpr int pass_tiles() { return R >= 128 ? 8 : R / 16; }
+
+// The A operands of column tile n, k steps j0 and j0 + 1, into ah / al.
+template <int R>
+__device__ __forceinline__ void load_aop(const RowsSmem<R> &sm, int n, int j0, int lane, bf16x8 (&ah)[4],
+                                         bf16x8 (&al)[4]) {
+#pragma unroll
+    for (int j = j0; j < j0 + 2; ++j) {
+        ah[j] = __builtin_bit_cast(bf16x8, sm.aop[n][j][0][lane]);
+        al[j] = __builtin_bit_cast(bf16x8, sm.aop[n][j][1][lane]);
+    }
+}
+
+// y'^T of column tile n for the 64 rows: four independent accumulator chains
+// (row tiles), the high and the low part of W' into the same one; k steps
+// j0, j0 + 1.
+__device__ __forceinline__ void tile_mfma(const bf16x8 (&ah)[4], const bf16x8 (&al)[4],
+                                          const uvec4 (&xa)[kRTiles][4], int j0, f32x4 (&acc)[kRTiles]) {
+#pragma unroll
+    for (int j = j0; j < j0 + 2; ++j) {
+#pragma unroll
+        for (int t = 0; t < kRTiles; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[j], __builtin_bit_cast(bf16x8, xa[t][j]), acc[t],
+                                                             0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < kRTiles; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[j], __builtin_bit_cast(bf16x8, xa[t][j]), acc[t],
+                                                             0, 0, 0);
     }
 }
 
 // Codes of one group whose rows are in xa (see the header comment).
 template <int R>
 __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm, const float *W, int h,
-                                             int64_t gi, const RGroup &e, const uvec4 (&xa)[2][4],
-                                             int &n_list) {
-    constexpr int NT = R / 16;   // column tiles
-    constexpr int NW = R / 32;   // code words per row
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
-    // ---- row norms: lane (g, c) sums its 32 dims of row 16 m + c, the four
-    // lanes of a row add theirs; lane L then takes 2^-14 ||x|| of rows
-    // 16 m + 4 g + i (negative for a row of zeros, whose sums are exactly 0)
-    float tx[2][4];
+                                             int64_t gi, const RGroup &e, uvec4 (&xa)[kRTiles][4],
+                                             const ZeroCols<R> &zc, int &n_list) {
+    constexpr int NT = R / 16;          // column tiles
+    constexpr int NW = R / 32;          // code words per row
+    constexpr int PT = pass_tiles<R>();
+    constexpr int NPASS = NT / PT;
+    constexpr int PW = PT / 2;          // code words per pass (1, 2 or 4)
+    constexpr int NPAIR = PW >= 2 ? PW / 2 : 1;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), g = lane >> 4, c = lane & 15;
+    // The next group's sixteen loads were the last memory operations issued:
+    // wait for everything before them (this group's rows, the previous
+    // group's stores).  With no store left in flight the compiler's own waits
+    // on this group's registers need not assume out-of-order completion
+    // (which would make them wait for the prefetch too).
+    __builtin_amdgcn_s_waitcnt(kWaitAllButPrefetch);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int t = 0; t < kRTiles; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(xa[t][j]));   // uses stay after the wait
+    // ---- thresholds: lane (g, c) sums the squares of its 32 dims of row
+    // 16 t + c, the four lanes of the row add theirs.  A sum of 0 is a row of
+    // zeros (threshold -1: every bit 0, decided) or of values too small to
+    // square (threshold 2^-72); a non-finite sum gives +inf (the group goes
+    // to the exact sums).
+    float th[kRTiles];
+    bool small = false, nonfinite = false;
+#pragma unroll
+    for (int t = 0; t < kRTiles; ++t) {
         float ss = 0.f;
-        uint32_t nz = 0u;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const bf16x2 p = __builtin_bit_cast(bf16x2, xa[m][j][q]);
+                // the element goes through a scalar: a bit cast of the vector
+                // element expression itself reads element 0 with this compiler
+                const uint32_t u = xa[t][j][q];
+                const bf16x2 p = __builtin_bit_cast(bf16x2, u);
                 ss = __builtin_amdgcn_fdot2_f32_bf16(p, p, ss, false);
-                nz |= xa[m][j][q] & 0x7FFF7FFFu;
             }
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
-        nz |= (uint32_t)__shfl_xor((int)nz, 16, 64);
-        nz |= (uint32_t)__shfl_xor((int)nz, 32, 64);
-        const float xn = nz ? sqrtf(ss) * (1.f + 0x1p-10f) * 0x1p-14f : -1.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tx[m][i] = __shfl(xn, 4 * g + i, 64);
+        ss = sum_over_g(ss);
+        // v_sqrt_f32 (1 ulp; the 2^-10 margin covers it)
+        th[t] = ss < INFINITY ? fmaf(__builtin_amdgcn_sqrtf(ss), (1.f + 0x1p-10f) * 0x1p-14f, 0x1p-72f) : INFINITY;
+        small |= ss == 0.f;
+        nonfinite |= !(ss < INFINITY);
     }
-    // lane L (< 32) keeps row L = 16 mL + 4 gL + iL
-    const int mL = (lane >> 4) & 1, gL = (lane >> 2) & 3, iL = lane & 3;
-    uint32_t wd[NW];
+    if (__builtin_amdgcn_ballot_w64(small) != 0) {
 #pragma unroll
-    for (int k = 0; k < NW; ++k) wd[k] = 0u;
-    const int list0 = n_list;  // this group's entries start here (uniform)
-    bool overflow = false;
-#pragma unroll 1
-    for (int n = 0; n < NT; ++n) {
-        bf16x8 bh[4], bl[4];
+        for (int t = 0; t < kRTiles; ++t) {
+            uint32_t nz = 0u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            bh[j] = __builtin_bit_cast(bf16x8, sm.bop[n][j][0][lane]);
-            bl[j] = __builtin_bit_cast(bf16x8, sm.bop[n][j][1][lane]);
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) nz |= xa[t][j][q];
+            if (or_over_g(nz & 0x7FFF7FFFu) == 0u) th[t] = -1.f;
         }
-        const float wn = sm.wnorm[16 * n + c];
-        // four independent accumulator chains: the high and the low parts of
-        // each M tile (their sum is one more rounding within the same bound)
-        f32x4 ah[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        f32x4 al[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    }
+    bool overflow = __builtin_amdgcn_ballot_w64(nonfinite) != 0;
+
+    // ---- column tiles, in passes of PT.  Per tile: sign bits (1 for a
+    // negative y') go in at bit 0 of the word being built: after the even
+    // tile of a code word the lane holds its four bits at i, shifted up by
+    // 12; after the odd one, at 16 + i and i, and rotating right by 16 - 4 g
+    // puts them at 4 g + i and 16 + 4 g + i, their places in the word.
+    // Completed words are paired across the two halves of the wave at once.
+    // The band flags (sign of th - |y'|: 1 where the bit is decided) go into
+    // dec[t], four bits per tile.  Tile n's band test and sign bits run while
+    // tile n + 1's matrix products issue (the two are interleaved in the
+    // schedule), and tile n + 2's A operands load behind them.
+    const uint32_t rot = 16 - 4 * g;
+    const int q = ((g & 1) << 1) | (g >> 1);
+    uint32_t word[kRTiles][NPASS];   // lane (g, c): word q(g) of the pass, row 16 t + c
+    uint32_t dec[kRTiles][NPASS];
+    bf16x8 ah[4], al[4];
+    f32x4 acc[kRTiles], nxt[kRTiles];
+    load_aop<R>(sm, 0, 0, lane, ah, al);
+    load_aop<R>(sm, 0, 2, lane, ah, al);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+    for (int t = 0; t < kRTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    tile_mfma(ah, al, xa, 0, acc);
+    tile_mfma(ah, al, xa, 2, acc);
+    if (NT > 1) {
+        load_aop<R>(sm, NT > 1 ? 1 : 0, 0, lane, ah, al);
+        load_aop<R>(sm, NT > 1 ? 1 : 0, 2, lane, ah, al);
+    }
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                ah[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[m][j]), bh[j],
-                                                                ah[m], 0, 0, 0);
-                al[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[m][j]), bl[j],
-                                                                al[m], 0, 0, 0);
+    for (int t = 0; t < kRTiles; ++t) asm volatile("" : "+v"(acc[t]));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+        uint32_t cur[kRTiles], held[kRTiles], pair[kRTiles][NPAIR];
+#pragma unroll
+        for (int t = 0; t < kRTiles; ++t) dec[t][p] = 0u;
+#pragma unroll
+        for (int k = 0; k < PT; ++k) {
+            const int n = p * PT + k;
+            // tile n + 1's products, then tile n + 2's operands
+            if (n + 1 < NT) {
+#pragma unroll
+                for (int t = 0; t < kRTiles; ++t) nxt[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                tile_mfma(ah, al, xa, 0, nxt);
+                if (n + 2 < NT) load_aop<R>(sm, n + 2 < NT ? n + 2 : 0, 0, lane, ah, al);
+                tile_mfma(ah, al, xa, 2, nxt);
+                if (n + 2 < NT) load_aop<R>(sm, n + 2 < NT ? n + 2 : 0, 2, lane, ah, al);
             }
-        }
-        // y' = ah + al: row 16 m + 4 g + i, column 16 n + c.  The band: a
-        // zero row (tx < 0) or column (wn = -inf) gives a negative threshold,
-        // so its exact 0 counts as decided; both zero gives +inf and the exact
-        // path (which finds 0).  A bit is 1 where y' > max(threshold, 0), and
-        // unsure where |y'| does not exceed the threshold.  Rows past the
-        // group's count repeat row 0.
-        uint32_t piece = 0u;
-        bool unsure = false;
-        float yv[2][4], th[2][4];
+            // tile n: band flags and sign bits
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+            for (int t = 0; t < kRTiles; ++t) {
+                uint32_t d = dec[t][p], s = (k & 1) ? cur[t] : 0u;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                yv[m][i] = ah[m][i] + al[m][i];
-                th[m][i] = fmaf(tx[m][i], wn, 0x1p-100f);
-            }
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint64_t pos = __builtin_amdgcn_ballot_w64(yv[m][i] > fmaxf(th[m][i], 0.f));
-                unsure |= !(fabsf(yv[m][i]) > th[m][i]);
-                if (mL == m && iL == i) piece = (uint32_t)(pos >> (16 * gL)) & 0xFFFFu;
-            }
-#pragma unroll
-        for (int k = 0; k < NW; ++k)
-            if (k == (n >> 1)) wd[k] |= piece << (16 * (n & 1));
-        if (__builtin_amdgcn_ballot_w64(unsure) != 0) {
-            // list the in-band bits (about 0.05 % of bits; their provisional
-            // bit is 0), to be resolved later by flush_list
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    uint64_t uns = __builtin_amdgcn_ballot_w64(!(fabsf(yv[m][i]) > th[m][i]));
-                    while (uns) {
-                        const int lb = __builtin_ctzll(uns);
-                        uns &= uns - 1;
-                        const int row = 16 * m + 4 * (lb >> 4) + i;
-                        if (row >= e.nr) continue;  // a repeat of row 0 past the group's count
-                        if (n_list < kRList) {
-                            if (lane == 0) {
-                                sm.lgrp[wv][n_list] = (uint32_t)gi;
-                                sm.lrc[wv][n_list] = (uint16_t)((row << 8) | (16 * n + (lb & 15)));
-                            }
-                            ++n_list;
-                        } else {
-                            overflow = true;
-                        }
+                for (int i = 3; i >= 0; --i) {
+                    d = __builtin_amdgcn_alignbit(d, __float_as_uint(th[t] - fabsf(acc[t][i])), 31);
+                    s = __builtin_amdgcn_alignbit(s, __float_as_uint(acc[t][i]), 31);
+                }
+                dec[t][p] = d;
+                if ((k & 1) == 0) {
+                    cur[t] = s << 12;
+                } else {
+                    s = __builtin_amdgcn_alignbit(s, s, rot);
+                    const int w = k >> 1;
+                    if (PW == 1 || (w & 1)) {
+                        const auto sw = __builtin_amdgcn_permlane32_swap(PW == 1 ? s : held[t], PW == 1 ? 0u : s,
+                                                                         false, false);
+                        pair[t][w >> 1] = sw[0] | sw[1];
+                    } else {
+                        held[t] = s;
                     }
                 }
-        }
-    }
-    // ---- a group with more in-band bits than the list holds (degenerate
-    // rows): its listed entries are dropped and every bit of it is decided
-    // here, exactly, by the wave (the row through the wave's LDS row buffer,
-    // lane l holding dims 2 l and 2 l + 1; W_H's column from LDS for
-    // r <= 128, else from memory)
-    if (overflow) {
-        n_list = list0;
-        const int total = e.nr * R;
-        for (int b = 0; b < total; ++b) {
-            const int row = b / R, col = b % R;
-            if (c == (row & 15)) {
-                const int m = row >> 4;
+            }
+            // keep each tile's work in its own stretch of the schedule, the
+            // products and band test interleaved, the operand loads after the
+            // products that read the registers they replace
+            if (n + 1 < NT) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<uvec4 *>(&sm.xrow[wv][16 * j + 4 * g]) = m ? xa[1][j] : xa[0][j];
-            }
-            __builtin_amdgcn_wave_barrier();
-            const uint32_t xp = sm.xrow[wv][lane];
-            float w0, w1;
-            if constexpr (R <= 128) {
-                const float2 wp = *reinterpret_cast<const float2 *>(&sm.wt[col][2 * lane]);
-                w0 = wp.x;
-                w1 = wp.y;
-            } else {
-                w0 = W[(int64_t)(2 * lane) * R + col];
-                w1 = W[(int64_t)(2 * lane + 1) * R + col];
-            }
-            __builtin_amdgcn_wave_barrier();
-            const double p0 = (double)__uint_as_float(xp << 16) * (double)w0;
-            const double p1 = (double)__uint_as_float(xp & 0xFFFF0000u) * (double)w1;
-            const double sum = dsum64(p0 + p1);
-            const double A = dsum64(fabs(p0) + fabs(p1));
-            bool bit = sum > 0.0;
-            if (!(fabs(sum) > 0x1p-44 * A)) {
-                // the defining sequential sum, d = 0 .. 127 in order
-                double ysq = 0.0;
-                for (int l = 0; l < 64; ++l) {
-                    const uint32_t xl = (uint32_t)__builtin_amdgcn_readlane((int)xp, l);
-                    const float wa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0), l));
-                    const float wb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w1), l));
-                    ysq = fma((double)__uint_as_float(xl << 16), (double)wa, ysq);
-                    ysq = fma((double)__uint_as_float(xl & 0xFFFF0000u), (double)wb, ysq);
+                for (int m = 0; m < 16; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one product
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two vector ALU
                 }
-                bit = ysq > 0.0;
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // operand loads
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
             }
-            put_bit<R>(wd, col, bit, lane == row);
+#pragma unroll
+            for (int t = 0; t < kRTiles; ++t) {
+                asm volatile("" ::"v"(dec[t][p]));
+                if (k & 1) {
+                    if (PW == 1 || ((k >> 1) & 1)) asm volatile("" ::"v"(pair[t][k >> 2]));
+                    else asm volatile("" ::"v"(held[t]));
+                } else {
+                    asm volatile("" ::"v"(cur[t]));
+                }
+                if (n + 1 < NT) asm volatile("" : "+v"(nxt[t]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < kRTiles; ++t) acc[t] = nxt[t];
+        }
+        // ---- the second lane swap: lane (g, c) of row tile t ends with word
+        // q(g) = {0, 2, 1, 3}[g] of the pass's four words of row 16 t + c
+#pragma unroll
+        for (int t = 0; t < kRTiles; ++t) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(pair[t][0], NPAIR > 1 ? pair[t][NPAIR > 1 ? 1 : 0] : 0u,
+                                                             false, false);
+            word[t][p] = sw[0] | sw[1];
         }
     }
-    // ---- row L's code words
-    if (lane < e.nr) {
-        uint32_t *dst = a.mode == 0 ? a.codes_out + ((e.r0 + lane) * a.n_heads + h) * NW
-                                    : a.codes + cache_row(a, h, e, lane) * NW;
-        if constexpr (NW == 1) {
-            dst[0] = wd[0];
-        } else if constexpr (NW == 2) {
-            *reinterpret_cast<uint2 *>(dst) = make_uint2(wd[0], wd[1]);
-        } else {
+
+    // ---- list the in-band bits: band flag 0, columns of zeros excepted
+    // (their bit is 0), rows past the group's count skipped.  Flag bit
+    // 4 (PT - 1 - k) + i of pass p is column 16 (p PT + k) + 4 g + i.
+    const int list0 = n_list;  // this group's entries start here (uniform)
+    constexpr uint32_t kFlagMask = PT == 8 ? 0xFFFFFFFFu : (1u << (4 * PT)) - 1u;
 #pragma unroll
-            for (int k = 0; k < NW; k += 4)
-                *reinterpret_cast<uvec4 *>(dst + k) = uvec4{wd[k], wd[k + 1], wd[k + 2], wd[k + 3]};
+    for (int p = 0; p < NPASS; ++p)
+#pragma unroll
+        for (int t = 0; t < kRTiles; ++t) {
+            const uint32_t inb = ~dec[t][p] & kFlagMask & ~zc.flags[p];
+            uint64_t lanes = __builtin_amdgcn_ballot_w64(inb != 0u);
+            while (lanes) {
+                const int l = __builtin_ctzll(lanes);
+                lanes &= lanes - 1;
+                const int row = 16 * t + (l & 15);
+                if (row >= e.nr) continue;  // a repeat of row 0 past the group's count
+                uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)inb, l);
+                while (bits) {
+                    const int b = __builtin_ctz(bits);
+                    bits &= bits - 1;
+                    const int col = 16 * (p * PT + PT - 1 - (b >> 2)) + 4 * (l >> 4) + (b & 3);
+                    if (n_list < kRList) {
+                        if (lane == 0) {
+                            sm.lgrp[wv][n_list] = (uint32_t)gi;
+                            sm.lrc[wv][n_list] = (uint16_t)((row << 8) | col);
+                        }
+                        ++n_list;
+                    } else {
+                        overflow = true;
+                    }
+                }
+            }
+        }
+
+    if (overflow) {
+        // too many in-band bits, or a non-finite row: every word of the group
+        // by the exact sums
+        n_list = list0;
+        exact_group<R>(a, sm, W, h, e);
+    } else {
+        // ---- store: lane (g, c) of row tile t writes word 4 p + q(g) of row
+        // 16 t + c.  Codes are 1 for y' > 0: the complement of the sign bits,
+        // with columns of zeros and rows of zeros at 0.
+#pragma unroll
+        for (int t = 0; t < kRTiles; ++t) {
+            const int row = 16 * t + c;
+            uint32_t *dst = code_row<R>(a, h, e, row);
+            const bool live = row < e.nr;
+#pragma unroll
+            for (int p = 0; p < NPASS; ++p) {
+                const uint32_t o = th[t] < 0.f ? 0u : ~(word[t][p] | zc.word[p]);
+                if (live && 4 * p + q < NW) dst[4 * p + q] = o;
+            }
         }
     }
     // ---- appended rows into the cache: K from the registers, V copied
     if (a.mode == 1 && a.k_new) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int r = 16 * m + c;
+        for (int t = 0; t < kRTiles; ++t) {
+            const int r = 16 * t + c;
             if (r < e.nr) {
                 uint16_t *kd = a.k_cache + cache_row(a, h, e, r) * kHeadDim + 8 * g;
                 uint16_t *vd = a.v_cache + cache_row(a, h, e, r) * kHeadDim + 8 * g;
@@ -372,51 +568,10 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
                 for (int j = 0; j < 4; ++j) vv[j] = *reinterpret_cast<const uvec4 *>(vs + 32 * j);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    *reinterpret_cast<uvec4 *>(kd + 32 * j) = xa[m][j];
+                    *reinterpret_cast<uvec4 *>(kd + 32 * j) = xa[t][j];
                     *reinterpret_cast<uvec4 *>(vd + 32 * j) = vv[j];
                 }
             }
-        }
-    }
-}
-
-// Resolve a wave's listed in-band bits: one lane per bit runs the defining
-// sequential double sum (d = 0 .. 127 in order; every product of a bf16 and
-// an fp32 value is exact in double) and, where it is positive, sets the bit
-// in the code word the wave has already stored (provisional bit 0).  The
-// wave first waits for its own stores, so the word is in memory.
-template <int R>
-__device__ __forceinline__ void flush_list(const RowsArgs &a, RowsSmem<R> &sm, const float *W, int h, int count) {
-    constexpr int NW = R / 32;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    __builtin_amdgcn_s_waitcnt(0);
-    for (int b = lane; b < count; b += 64) {
-        const int64_t gi = sm.lgrp[wv][b];
-        const int rc = sm.lrc[wv][b], row = rc >> 8, col = rc & 255;
-        const RGroup e = group_of<R>(a, sm, gi);
-        const uint16_t *xr = src_row(a, h, e, row);
-        double y = 0.0;
-        for (int d0 = 0; d0 < kHeadDim; d0 += 8) {
-            const uvec4 xv = *reinterpret_cast<const uvec4 *>(xr + d0);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int d = d0 + 2 * q;
-                float w0, w1;
-                if constexpr (R <= 128) {
-                    w0 = sm.wt[col][d];
-                    w1 = sm.wt[col][d + 1];
-                } else {
-                    w0 = W[(int64_t)d * R + col];
-                    w1 = W[(int64_t)(d + 1) * R + col];
-                }
-                y = fma((double)__uint_as_float(xv[q] << 16), (double)w0, y);
-                y = fma((double)__uint_as_float(xv[q] & 0xFFFF0000u), (double)w1, y);
-            }
-        }
-        if (row < e.nr && y > 0.0) {
-            uint32_t *word = (a.mode == 0 ? a.codes_out + ((e.r0 + row) * a.n_heads + h) * NW
-                                          : a.codes + cache_row(a, h, e, row) * NW) + (col >> 5);
-            atomicOr(word, 1u << (col & 31));
         }
     }
 }
@@ -426,43 +581,80 @@ __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
     constexpr int NT = R / 16;   // column tiles
     __shared__ RowsSmem<R> sm;
     const int h = blockIdx.y;
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, g = lane >> 4, c = lane & 15;
+    const int t = threadIdx.x, lane = t & 63, wv = __builtin_amdgcn_readfirstlane(t >> 6), g = lane >> 4, c = lane & 15;
     const float *W = a.w + (int64_t)h * kHeadDim * R;
 
-    // ---- set-up: B operands (lane (g, c) of column tile n, k step j holds
-    // W[32 j + 8 g + e][16 n + c], e < 8, as bf16 high and low parts), W_H
-    // transposed, the column norms, the entries' lengths
+    // ---- set-up 1: per column, the scale that brings ||W_:j|| to 1: first a
+    // power of two (from the largest element, exponent e: W 2^-e has elements
+    // below 1 and a sum of squares that fp32 holds), then a factor in [1, 2);
+    // and the zero columns
+    if (t < R / 32) sm.zcol[t] = 0u;
+    __syncthreads();
+    for (int col = t; col < R; col += kRThreads) {
+        float mx = 0.f;
+        bool finite = true;
+        for (int d = 0; d < kHeadDim; ++d) {
+            const float v = fabsf(W[(int64_t)d * R + col]);
+            finite = finite && v < INFINITY;
+            mx = fmaxf(mx, v);
+        }
+        int s = INT_MIN;
+        float m = 1.f;
+        if (!finite) {
+            // W' taken as 0: every bit of the column goes to the exact sum
+        } else if (mx == 0.f) {
+            atomicOr(&sm.zcol[col >> 5], 1u << (col & 31));
+        } else {
+            int e;
+            frexpf(mx, &e);
+            float ss = 0.f;
+            for (int d = 0; d < kHeadDim; ++d) {
+                const float v = ldexpf(W[(int64_t)d * R + col], -e);
+                ss = fmaf(v, v, ss);
+            }
+            int f;
+            frexpf(sqrtf(ss) * (1.f + 0x1p-10f), &f);
+            s = -e - f;
+            // W 2^s has a norm in (1/2, 1]; m = 1 / that norm brings it to 1
+            float ss2 = 0.f;
+            for (int d = 0; d < kHeadDim; ++d) {
+                const float v = ldexpf(W[(int64_t)d * R + col], s);
+                ss2 = fmaf(v, v, ss2);
+            }
+            m = 1.f / sqrtf(ss2);
+        }
+        sm.col_exp[col] = s;
+        sm.col_mul[col] = m;
+    }
+    __syncthreads();
+    // ---- set-up 2: A operands (lane (g, c) of column tile n, k step j holds
+    // W'[32 j + 8 g + e][16 n + c], e < 8, as bf16 high and low parts), W_H
+    // transposed, the entries' lengths
     for (int i = t; i < NT * 4 * 64; i += kRThreads) {
         const int l = i & 63, j = (i >> 6) & 3, n = i >> 8;
         const int col = 16 * n + (l & 15), d0 = 32 * j + 8 * (l >> 4);
+        const int s = sm.col_exp[col];
+        const float m = sm.col_mul[col];
         float wf[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wf[e] = W[(int64_t)(d0 + e) * R + col];
+        for (int q = 0; q < 8; ++q) wf[q] = W[(int64_t)(d0 + q) * R + col];
         uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            const uint16_t h0 = f32_to_bf16(wf[e]), h1 = f32_to_bf16(wf[e + 1]);
-            const uint16_t l0 = f32_to_bf16(wf[e] - __uint_as_float((uint32_t)h0 << 16));
-            const uint16_t l1 = f32_to_bf16(wf[e + 1] - __uint_as_float((uint32_t)h1 << 16));
-            hw[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            lw[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        for (int q = 0; q < 8; q += 2) {
+            const float v0 = s == INT_MIN ? 0.f : ldexpf(wf[q], s) * m;
+            const float v1 = s == INT_MIN ? 0.f : ldexpf(wf[q + 1], s) * m;
+            const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
+            const uint16_t l0 = f32_to_bf16(v0 - __uint_as_float((uint32_t)h0 << 16));
+            const uint16_t l1 = f32_to_bf16(v1 - __uint_as_float((uint32_t)h1 << 16));
+            hw[q / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            lw[q / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
         }
-        sm.bop[n][j][0][l] = uvec4{hw[0], hw[1], hw[2], hw[3]};
-        sm.bop[n][j][1][l] = uvec4{lw[0], lw[1], lw[2], lw[3]};
+        sm.aop[n][j][0][l] = uvec4{hw[0], hw[1], hw[2], hw[3]};
+        sm.aop[n][j][1][l] = uvec4{lw[0], lw[1], lw[2], lw[3]};
         if constexpr (R <= 128) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm.wt[col][d0 + e] = wf[e];
+            for (int q = 0; q < 8; ++q) sm.wt[col][d0 + q] = wf[q];
         }
-    }
-    for (int col = t; col < R; col += kRThreads) {
-        float ss = 0.f;
-        uint32_t nz = 0u;
-        for (int d = 0; d < kHeadDim; ++d) {
-            const float wf = W[(int64_t)d * R + col];
-            ss = fmaf(wf, wf, ss);
-            nz |= __float_as_uint(wf) & 0x7FFFFFFFu;
-        }
-        sm.wnorm[col] = nz ? sqrtf(ss) * (1.f + 0x1p-10f) : -INFINITY;
     }
     if (a.mode == 1) {
         for (int s = t; s < a.n_seg && s < kRSegLds; s += kRThreads) {
@@ -473,6 +665,24 @@ __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
         }
     }
     __syncthreads();
+    ZeroCols<R> zc;
+    {
+        constexpr int PT = pass_tiles<R>();
+        const int q = ((g & 1) << 1) | (g >> 1);
+#pragma unroll
+        for (int p = 0; p < NT / PT; ++p) {
+            zc.word[p] = sm.zcol[4 * p + q < R / 32 ? 4 * p + q : 0];
+            uint32_t f = 0u;
+#pragma unroll
+            for (int k = 0; k < PT; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int col = 16 * (p * PT + k) + 4 * g + i;
+                    f |= ((sm.zcol[col >> 5] >> (col & 31)) & 1u) << (4 * (PT - 1 - k) + i);
+                }
+            zc.flags[p] = f;
+        }
+    }
 
     // ---- the wave's groups, two register buffers: the next group loads
     // while this one is computed
@@ -480,23 +690,27 @@ __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
     const int64_t stride = (int64_t)gridDim.x * kRWaves;
     const RGroup none{0, 0, 0, 0};
     int64_t gi = (int64_t)blockIdx.x * kRWaves + wv;
-    uvec4 xa0[2][4], xa1[2][4];
+    uvec4 xa0[kRTiles][4], xa1[kRTiles][4];
     int n_list = 0;  // in-band bits listed by this wave, not yet resolved (uniform)
+    // The loads are issued whether or not the group has rows (one past the
+    // work, or skipped, reads row 0 of the head: a valid address), so that
+    // the count of loads in flight is the same on every path and a group's
+    // use waits only for its own loads.
     RGroup e0 = gi < n_groups ? group_of<R>(a, sm, gi) : none;
-    if (e0.nr > 0) load_group(a, h, e0, g, c, xa0);
+    load_group(a, h, e0, g, c, xa0);
     while (gi < n_groups) {
         const int64_t gi1 = gi + stride;
         const RGroup e1 = gi1 < n_groups ? group_of<R>(a, sm, gi1) : none;
-        if (e1.nr > 0) load_group(a, h, e1, g, c, xa1);
-        if (e0.nr > 0) encode_group<R>(a, sm, W, h, gi, e0, xa0, n_list);
+        load_group(a, h, e1, g, c, xa1);
+        if (e0.nr > 0) encode_group<R>(a, sm, W, h, gi, e0, xa0, zc, n_list);
         if (n_list > kRList / 2) {
             flush_list<R>(a, sm, W, h, n_list);
             n_list = 0;
         }
         const int64_t gi2 = gi1 + stride;
         e0 = gi2 < n_groups ? group_of<R>(a, sm, gi2) : none;
-        if (e0.nr > 0) load_group(a, h, e0, g, c, xa0);
-        if (e1.nr > 0) encode_group<R>(a, sm, W, h, gi1, e1, xa1, n_list);
+        load_group(a, h, e0, g, c, xa0);
+        if (e1.nr > 0) encode_group<R>(a, sm, W, h, gi1, e1, xa1, zc, n_list);
         if (n_list > kRList / 2) {
             flush_list<R>(a, sm, W, h, n_list);
             n_list = 0;

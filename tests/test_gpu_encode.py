@@ -97,6 +97,41 @@ def test_encode_keys_band_cases(gpu):
     assert np.all(ref[264:300] == 0)
 
 
+@pytest.mark.parametrize("n_bits", [32, 64, 128, 256])
+def test_encode_keys_scaled_columns_and_tiny_rows(gpu, n_bits):
+    # W_H columns the matrix-core path rescales by powers of two: a zero
+    # column, columns scaled by 2^40 and 2^-40, one element 2^30 among
+    # ordinary ones, columns below fp32's normal range (2^-120 scale) and a
+    # column with a single nonzero element.  Rows whose squares leave the
+    # normal range (2^-70, 2^-100 scale), rows with one subnormal bf16 entry,
+    # rows of zeros.  650 rows: ten full 64-row groups and a ragged one.
+    rng = np.random.default_rng(300 + n_bits)
+    n, H = 650, 2
+    w = (rng.standard_normal((H, 128, n_bits)) / np.sqrt(128.0)).astype(np.float32)
+    w[0, :, 3] = 0.0
+    w[0, :, 7] *= np.float32(2.0 ** 40)
+    w[0, :, 9] *= np.float32(2.0 ** -40)
+    w[0, 17, 11] = np.float32(2.0 ** 30)
+    w[1, :, 20:24] = (w[1, :, 20:24].astype(np.float64) * 2.0 ** -120).astype(np.float32)
+    w[1, :, 30] = 0.0
+    w[1, 5, 30] = np.float32(-3e-30)
+    x = rng.standard_normal((n, H, 128))
+    x[0:64] *= 2.0 ** -70
+    x[64:100] *= 2.0 ** -100
+    x[100:120] = 0.0
+    x[100:120, :, 9] = 2.0 ** -130
+    x[120:130] = 0.0
+    keys = _bf16(x)
+    got = hata.hata_encode_keys(_dev_bf16(keys, gpu), torch.from_numpy(w).to(gpu))
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().view(np.uint32)
+    for h in range(H):
+        want = oracle.encode(np.ascontiguousarray(keys[:, h]), w[h])
+        assert np.array_equal(got[:, h], want), f"r={n_bits} head {h}: " \
+            f"{int((got[:, h] != want).any(1).sum())} rows differ"
+    assert np.all(got[120:130] == 0)
+
+
 def test_append_prefill_uses_matrix_cores_and_matches(gpu):
     # A prefill append with new rows given (k_new / v_new): codes, K and V
     # rows land in the cache, lengths advance.
