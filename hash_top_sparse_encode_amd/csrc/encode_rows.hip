@@ -222,28 +222,35 @@ __device__ __forceinline__ uint32_t or_transpose4(uint32_t u0, uint32_t u1, uint
 }
 
 // The defining sum of bit `col` of a row (sequential, d = 0 .. 127; every
-// product of a bf16 and an fp32 value is exact in double).
+// product of a bf16 and an fp32 value is exact in double).  The row is read
+// in quarters of four 16-byte loads issued together.
 template <int R>
 __device__ __forceinline__ double exact_sum(const RowsSmem<R> &sm, const float *W, const uint16_t *xr,
                                             int col) {
     double y = 0.0;
 #pragma unroll 1
-    for (int d0 = 0; d0 < kHeadDim; d0 += 8) {
-        const uvec4 xv = *reinterpret_cast<const uvec4 *>(xr + d0);
+    for (int d0 = 0; d0 < kHeadDim; d0 += 32) {
+        uvec4 xv[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int d = d0 + 2 * q;
-            float w0, w1;
-            if constexpr (R <= 128) {
-                w0 = sm.wt[col][d];
-                w1 = sm.wt[col][d + 1];
-            } else {
-                w0 = W[(int64_t)d * R + col];
-                w1 = W[(int64_t)(d + 1) * R + col];
+        for (int k = 0; k < 4; ++k) xv[k] = *reinterpret_cast<const uvec4 *>(xr + d0 + 8 * k);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int d = d0 + 8 * k + 2 * q;
+                float w0, w1;
+                if constexpr (R <= 128) {
+                    w0 = sm.wt[col][d];
+                    w1 = sm.wt[col][d + 1];
+                } else {
+                    w0 = W[(int64_t)d * R + col];
+                    w1 = W[(int64_t)(d + 1) * R + col];
+                }
+                // the element goes through a scalar (see the row norms)
+                const uint32_t u = xv[k][q];
+                y = fma((double)__uint_as_float(u << 16), (double)w0, y);
+                y = fma((double)__uint_as_float(u & 0xFFFF0000u), (double)w1, y);
             }
-            y = fma((double)__uint_as_float(xv[q] << 16), (double)w0, y);
-            y = fma((double)__uint_as_float(xv[q] & 0xFFFF0000u), (double)w1, y);
-        }
     }
     return y;
 }
@@ -329,25 +336,38 @@ __device__ __forceinline__ void tile_mfma(const bf16x8 (&ah)[4], const bf16x8 (&
 template <int R>
 __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm, const float *W, int h,
                                              int64_t gi, const RGroup &e, uvec4 (&xa)[kRTiles][4],
-                                             const ZeroCols<R> &zc, int &n_list) {
+                                             const ZeroCols<R> &zc, int wv, int &n_list) {
     constexpr int NT = R / 16;          // column tiles
     constexpr int NW = R / 32;          // code words per row
     constexpr int PT = pass_tiles<R>();
     constexpr int NPASS = NT / PT;
     constexpr int PW = PT / 2;          // code words per pass (1, 2 or 4)
     constexpr int NPAIR = PW >= 2 ? PW / 2 : 1;
-    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), g = lane >> 4, c = lane & 15;
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     // The next group's sixteen loads were the last memory operations issued:
     // wait for everything before them (this group's rows, the previous
     // group's stores).  With no store left in flight the compiler's own waits
     // on this group's registers need not assume out-of-order completion
     // (which would make them wait for the prefetch too).
     __builtin_amdgcn_s_waitcnt(kWaitAllButPrefetch);
+    // (an instruction between this wait and the first use below, so that the
+    // compiler applies the wait before working out the use's own)
+    asm volatile("s_nop 0");
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < kRTiles; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(xa[t][j]));   // uses stay after the wait
+    // ---- tile 0's products, interleaved with the row norms below (the two
+    // are independent; the norms' branch for rows of zeros comes after)
+    bf16x8 ah[4], al[4];
+    f32x4 acc[kRTiles], nxt[kRTiles];
+    load_aop<R>(sm, 0, 0, lane, ah, al);
+    load_aop<R>(sm, 0, 2, lane, ah, al);
+#pragma unroll
+    for (int t = 0; t < kRTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    tile_mfma(ah, al, xa, 0, acc);
+    tile_mfma(ah, al, xa, 2, acc);
     // ---- thresholds: lane (g, c) sums the squares of its 32 dims of row
     // 16 t + c, the four lanes of the row add theirs.  A sum of 0 is a row of
     // zeros (threshold -1: every bit 0, decided) or of values too small to
@@ -373,6 +393,13 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
         th[t] = ss < INFINITY ? fmaf(__builtin_amdgcn_sqrtf(ss), (1.f + 0x1p-10f) * 0x1p-14f, 0x1p-72f) : INFINITY;
         small |= ss == 0.f;
         nonfinite |= !(ss < INFINITY);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // tile 0's operands
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+#pragma unroll
+    for (int m = 0; m < 8 * kRTiles; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
     }
     if (__builtin_amdgcn_ballot_w64(small) != 0) {
 #pragma unroll
@@ -401,14 +428,6 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
     const int q = ((g & 1) << 1) | (g >> 1);
     uint32_t word[kRTiles][NPASS];   // lane (g, c): word q(g) of the pass, row 16 t + c
     uint32_t dec[kRTiles][NPASS];
-    bf16x8 ah[4], al[4];
-    f32x4 acc[kRTiles], nxt[kRTiles];
-    load_aop<R>(sm, 0, 0, lane, ah, al);
-    load_aop<R>(sm, 0, 2, lane, ah, al);
-#pragma unroll
-    for (int t = 0; t < kRTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    tile_mfma(ah, al, xa, 0, acc);
-    tile_mfma(ah, al, xa, 2, acc);
     if (NT > 1) {
         load_aop<R>(sm, NT > 1 ? 1 : 0, 0, lane, ah, al);
         load_aop<R>(sm, NT > 1 ? 1 : 0, 2, lane, ah, al);
@@ -501,36 +520,34 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
 
     // ---- list the in-band bits: band flag 0, columns of zeros excepted
     // (their bit is 0), rows past the group's count skipped.  Flag bit
-    // 4 (PT - 1 - k) + i of pass p is column 16 (p PT + k) + 4 g + i.
+    // 4 (PT - 1 - k) + i of pass p is column 16 (p PT + k) + 4 g + i.  Each
+    // lane writes its own entries, at its place in the wave's prefix sum.
     const int list0 = n_list;  // this group's entries start here (uniform)
     constexpr uint32_t kFlagMask = PT == 8 ? 0xFFFFFFFFu : (1u << (4 * PT)) - 1u;
 #pragma unroll
     for (int p = 0; p < NPASS; ++p)
 #pragma unroll
         for (int t = 0; t < kRTiles; ++t) {
-            const uint32_t inb = ~dec[t][p] & kFlagMask & ~zc.flags[p];
-            uint64_t lanes = __builtin_amdgcn_ballot_w64(inb != 0u);
-            while (lanes) {
-                const int l = __builtin_ctzll(lanes);
-                lanes &= lanes - 1;
-                const int row = 16 * t + (l & 15);
-                if (row >= e.nr) continue;  // a repeat of row 0 past the group's count
-                uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)inb, l);
-                while (bits) {
-                    const int b = __builtin_ctz(bits);
-                    bits &= bits - 1;
-                    const int col = 16 * (p * PT + PT - 1 - (b >> 2)) + 4 * (l >> 4) + (b & 3);
-                    if (n_list < kRList) {
-                        if (lane == 0) {
-                            sm.lgrp[wv][n_list] = (uint32_t)gi;
-                            sm.lrc[wv][n_list] = (uint16_t)((row << 8) | col);
-                        }
-                        ++n_list;
-                    } else {
-                        overflow = true;
-                    }
-                }
+            const int row = 16 * t + c;
+            uint32_t inb = row < e.nr ? ~dec[t][p] & kFlagMask & ~zc.flags[p] : 0u;
+            if (__builtin_amdgcn_ballot_w64(inb != 0u) == 0) continue;
+            const int cnt = __builtin_popcount(inb);
+            const int incl = wave_incl_scan(cnt);
+            const int total = __builtin_amdgcn_readlane(incl, 63);
+            if (n_list + total > kRList) {
+                overflow = true;
+                continue;
             }
+            int pos = n_list + incl - cnt;
+            while (inb) {
+                const int b = __builtin_ctz(inb);
+                inb &= inb - 1;
+                const int col = 16 * (p * PT + PT - 1 - (b >> 2)) + 4 * g + (b & 3);
+                sm.lgrp[wv][pos] = (uint32_t)gi;
+                sm.lrc[wv][pos] = (uint16_t)((row << 8) | col);
+                ++pos;
+            }
+            n_list += total;
         }
 
     if (overflow) {
@@ -702,7 +719,7 @@ __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
         const int64_t gi1 = gi + stride;
         const RGroup e1 = gi1 < n_groups ? group_of<R>(a, sm, gi1) : none;
         load_group(a, h, e1, g, c, xa1);
-        if (e0.nr > 0) encode_group<R>(a, sm, W, h, gi, e0, xa0, zc, n_list);
+        if (e0.nr > 0) encode_group<R>(a, sm, W, h, gi, e0, xa0, zc, wv, n_list);
         if (n_list > kRList / 2) {
             flush_list<R>(a, sm, W, h, n_list);
             n_list = 0;
@@ -710,7 +727,7 @@ __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
         const int64_t gi2 = gi1 + stride;
         e0 = gi2 < n_groups ? group_of<R>(a, sm, gi2) : none;
         load_group(a, h, e0, g, c, xa0);
-        if (e1.nr > 0) encode_group<R>(a, sm, W, h, gi1, e1, xa1, zc, n_list);
+        if (e1.nr > 0) encode_group<R>(a, sm, W, h, gi1, e1, xa1, zc, wv, n_list);
         if (n_list > kRList / 2) {
             flush_list<R>(a, sm, W, h, n_list);
             n_list = 0;
