@@ -70,6 +70,10 @@ def parse():
                     help="print the HBM traffic block from two rocprofv3 --pmc "
                          "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of "
                          "'bench.py --copy-probe' runs, then exit")
+    ap.add_argument("--pmc-table", nargs="+", metavar=("KERNEL", "CSV"),
+                    help="print, for every kernel whose name contains KERNEL, each "
+                         "counter's dispatch count and median per dispatch over the "
+                         "given rocprofv3 counter_collection.csv files, then exit")
     ap.add_argument("--phases", action="store_true",
                     help="print the decode step's per-phase breakdown (device timestamps "
                          "from the trace build of the library) and exit")
@@ -130,6 +134,24 @@ def pmc_summary(fetch_csv, write_csv):
     return "\n".join(lines)
 
 
+def pmc_table(kernel, paths):
+    """| kernel | counter | dispatches | median | rows over the counter files:
+    one row per (kernel containing `kernel`, counter), the median of the
+    counter's per-dispatch values."""
+    per = {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            if kernel in r["Kernel_Name"]:
+                per.setdefault((r["Kernel_Name"], r["Counter_Name"]), {})[int(r["Dispatch_Id"])] = \
+                    float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no dispatch of a kernel containing {kernel!r}")
+    lines = ["| kernel | counter | dispatches | median per dispatch |", "|---|---|---|---|"]
+    for (name, counter), d in sorted(per.items()):
+        lines.append(f"| `{name}` | {counter} | {len(d)} | {statistics.median(d.values()):.1f} |")
+    return "\n".join(lines)
+
+
 def measured_traffic_bytes():
     """HBM bytes per decode launch from the committed counter summary:
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) each scaled by copy_bytes
@@ -151,6 +173,21 @@ def measured_traffic_bytes():
         return total
     except (KeyError, ValueError, ZeroDivisionError):
         return None
+
+
+def encode_intervals(call, n, stream):
+    """ms of each of n calls of `call` queued behind one untimed call, with an
+    event recorded between consecutive calls; the host issues each call while
+    the device still runs the one before, so the intervals are device time."""
+    import torch
+    call()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    for i in range(n):
+        ev[i].record(stream)
+        call()
+    ev[n].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
 
 
 def cpu_baseline(spec, reps):
@@ -467,6 +504,11 @@ def main():
     if args.pmc_summary:
         print(pmc_summary(*args.pmc_summary))
         return
+    if args.pmc_table:
+        if len(args.pmc_table) < 2:
+            raise SystemExit("--pmc-table KERNEL CSV [CSV ...]")
+        print(pmc_table(args.pmc_table[0], args.pmc_table[1:]))
+        return
     if args.phases:
         phases_parent(args)
     if args.phases_child:
@@ -582,17 +624,11 @@ def main():
         sys.exit(1)
 
     # The prefill encode of the same workload (hata_append over the N - 1
-    # prefilled rows of every sequence, codes computed in place): events
-    # around each call, after one warm-up.
-    enc_ms = []
-    for r in range(4):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        base.encode_prefill()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        if r > 0:
-            enc_ms.append(e0.elapsed_time(e1))
+    # prefilled rows of every sequence, codes computed in place): calls queued
+    # back to back behind an untimed one, an event between each pair, so that
+    # each interval is the device's time for one call (its seq_len fill and
+    # the encode) and not the host's time to issue it.
+    enc_ms = encode_intervals(base.encode_prefill, 3, stream)
     enc_rows = Hkv * sum(n - 1 for n in spec.lengths)
     enc_s = statistics.mean(enc_ms) * 1e-3
     prefill = {
@@ -698,15 +734,11 @@ def main():
         L_r = rotation_layers(spec_alg_bytes(spec, 0, r))
         c_r = hata.HataCache(B, Hq, Hkv, base.max_ctx, device=dev, k=base.cache.k.clone(),
                              v=base.cache.v.clone(), n_bits=r)
-        enc_t = []
-        for rep_i in range(2):
+        def encode_r():
             c_r.seq_len.zero_()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
             hata.hata_append(c_r, None, None, base.n_pre, spec.max_len - 1, w_r)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            enc_t.append(e0.elapsed_time(e1))
+
+        enc_t = encode_intervals(encode_r, 2, stream)
         rot = [(c_r, hata.alloc_workspace(c_r, base.k_max))]
         for i in range(1, L_r):
             c = hata.HataCache(B, Hq, Hkv, base.max_ctx, device=dev, k=base.cache.k.clone(),

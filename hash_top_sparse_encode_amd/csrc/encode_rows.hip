@@ -86,6 +86,7 @@ struct RowsArgs {
     int B, Hkv, t_max;
     int64_t max_ctx;
     // both
+    uint32_t *codes_base;  // codes_out (mode 0) or codes (mode 1), chosen on the host
     const float *w;  // [heads][128][R]
     int n_heads;
     int64_t groups_per_seg;
@@ -172,11 +173,14 @@ __device__ __forceinline__ int64_t cache_row(const RowsArgs &a, int h, const RGr
     return ((int64_t)e.s * a.Hkv + h) * a.max_ctx + e.l0 + e.r0 + r;
 }
 
-// The code words of row r of a group.
+// The code words of row r of a group.  One base pointer and a row index per
+// mode: a choice between two pointer fields of the argument block would be
+// made by the compiler through a private copy of it (a scratch load before
+// each store, and flat stores that also hold up the LDS waits).
 template <int R>
 __device__ __forceinline__ uint32_t *code_row(const RowsArgs &a, int h, const RGroup &e, int r) {
-    return a.mode == 0 ? a.codes_out + ((e.r0 + r) * a.n_heads + h) * (R / 32)
-                       : a.codes + cache_row(a, h, e, r) * (R / 32);
+    const int64_t row = a.mode == 0 ? (e.r0 + r) * a.n_heads + h : cache_row(a, h, e, r);
+    return a.codes_base + row * (R / 32);
 }
 
 // The sixteen 16-byte B-operand loads of a group (lane (g, c): rows 16 t + c,
@@ -559,6 +563,13 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
         // ---- store: lane (g, c) of row tile t writes word 4 p + q(g) of row
         // 16 t + c.  Codes are 1 for y' > 0: the complement of the sign bits,
         // with columns of zeros and rows of zeros at 0.
+        // (the lane's word offset is formed here from the lane number, per
+        // group: hoisted out of the loop, base + offset would hold two more
+        // registers throughout)
+        int lane;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+        const int gg = (lane >> 4) & 3;
+        const int qq = ((gg & 1) << 1) | (gg >> 1);
 #pragma unroll
         for (int t = 0; t < kRTiles; ++t) {
             const int row = 16 * t + c;
@@ -567,7 +578,7 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
 #pragma unroll
             for (int p = 0; p < NPASS; ++p) {
                 const uint32_t o = th[t] < 0.f ? 0u : ~(word[t][p] | zc.word[p]);
-                if (live && 4 * p + q < NW) dst[4 * p + q] = o;
+                if (live && 4 * p + qq < NW) dst[4 * p + qq] = o;
             }
         }
     }
@@ -802,6 +813,7 @@ hipError_t launch_encode_rows(const uint16_t *keys, int64_t n_rows, int n_heads,
     a.head_stride = head_stride;
     a.n_rows = n_rows;
     a.codes_out = codes;
+    a.codes_base = codes;
     a.w = w;
     a.n_heads = n_heads;
     a.n_seg = 1;
@@ -818,6 +830,7 @@ hipError_t launch_append_rows(uint16_t *k_cache, uint16_t *v_cache, uint32_t *co
     a.k_cache = k_cache;
     a.v_cache = v_cache;
     a.codes = codes;
+    a.codes_base = codes;
     a.seq_len = seq_len;
     a.ctrl = ctrl;
     a.n_new = n_new;
