@@ -93,6 +93,16 @@ struct RowsArgs {
     int n_seg;
 };
 
+// Columns of W_H that are all zero, as the lanes of group g = lane / 16 need
+// them: the bits of the code word(s) such a lane stores (word 4 p + q(g) of
+// pass p), and its columns 16 (p PT + k) + 4 g + i of pass p at bit
+// 4 (PT - 1 - k) + i (the layout of the band flags).
+template <int R>
+struct ZeroCols {
+    uint32_t word[R == 256 ? 2 : 1];
+    uint32_t flags[R == 256 ? 2 : 1];
+};
+
 template <int R>
 struct RowsSmem {
     uvec4 aop[R / 16][4][2][64];   // A operands: column tile, k step, high / low part, lane
@@ -102,21 +112,12 @@ struct RowsSmem {
     int col_exp[R];                // column scale: a power of two 2^e_j (INT_MIN: W' taken as 0) ...
     float col_mul[R];              // ... then a factor m_j in [1, 2)
     uint32_t zcol[R / 32];         // columns of W_H that are all zero, a bit per column
+    ZeroCols<R> zlane[4];          // ... and as lane group g needs them
     uint32_t lgrp[kRWaves][kRList];  // listed in-band bits: the group ...
     uint16_t lrc[kRWaves][kRList];   // ... and row << 8 | column
     int64_t seg_l0[kRSegLds];      // mode 1: each entry's length ...
     int32_t seg_rows[kRSegLds];    // ... and the rows it appends
     int last;
-};
-
-// Columns of W_H that are all zero, as one lane (g, c) needs them: the bits
-// of the code word(s) it stores (word 4 p + q(g) of pass p), and its columns
-// 16 (p PT + k) + 4 g + i of pass p at bit 4 (PT - 1 - k) + i (the layout of
-// the band flags).
-template <int R>
-struct ZeroCols {
-    uint32_t word[R == 256 ? 2 : 1];
-    uint32_t flags[R == 256 ? 2 : 1];
 };
 
 __device__ __forceinline__ bool rows_append_ok(int64_t len, int n, int t_max, int64_t max_ctx) {
@@ -340,7 +341,7 @@ __device__ __forceinline__ void tile_mfma(const bf16x8 (&ah)[4], const bf16x8 (&
 template <int R>
 __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm, const float *W, int h,
                                              int64_t gi, const RGroup &e, uvec4 (&xa)[kRTiles][4],
-                                             const ZeroCols<R> &zc, int wv, int &n_list) {
+                                             int wv, int &n_list) {
     constexpr int NT = R / 16;          // column tiles
     constexpr int NW = R / 32;          // code words per row
     constexpr int PT = pass_tiles<R>();
@@ -528,6 +529,12 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
     // lane writes its own entries, at its place in the wave's prefix sum.
     const int list0 = n_list;  // this group's entries start here (uniform)
     constexpr uint32_t kFlagMask = PT == 8 ? 0xFFFFFFFFu : (1u << (4 * PT)) - 1u;
+    // (the zero-column masks are read from LDS here and before the stores,
+    // at an index the compiler takes as new per group: kept in registers
+    // across the loop they cost up to four more)
+    int gz = g;
+    asm volatile("" : "+v"(gz));
+    const ZeroCols<R> &zc = sm.zlane[gz];
 #pragma unroll
     for (int p = 0; p < NPASS; ++p)
 #pragma unroll
@@ -566,10 +573,11 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
         // (the lane's word offset is formed here from the lane number, per
         // group: hoisted out of the loop, base + offset would hold two more
         // registers throughout)
-        int lane;
-        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
-        const int gg = (lane >> 4) & 3;
+        int ln;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        const int gg = (ln >> 4) & 3;
         const int qq = ((gg & 1) << 1) | (gg >> 1);
+        const ZeroCols<R> &zs = sm.zlane[gg];
 #pragma unroll
         for (int t = 0; t < kRTiles; ++t) {
             const int row = 16 * t + c;
@@ -577,7 +585,7 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
             const bool live = row < e.nr;
 #pragma unroll
             for (int p = 0; p < NPASS; ++p) {
-                const uint32_t o = th[t] < 0.f ? 0u : ~(word[t][p] | zc.word[p]);
+                const uint32_t o = th[t] < 0.f ? 0u : ~(word[t][p] | zs.word[p]);
                 if (live && 4 * p + qq < NW) dst[4 * p + qq] = o;
             }
         }
@@ -693,24 +701,24 @@ __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
         }
     }
     __syncthreads();
-    ZeroCols<R> zc;
-    {
+    if (t < 4) {
         constexpr int PT = pass_tiles<R>();
-        const int q = ((g & 1) << 1) | (g >> 1);
+        const int gz = t, q = ((gz & 1) << 1) | (gz >> 1);
 #pragma unroll
         for (int p = 0; p < NT / PT; ++p) {
-            zc.word[p] = sm.zcol[4 * p + q < R / 32 ? 4 * p + q : 0];
+            sm.zlane[gz].word[p] = sm.zcol[4 * p + q < R / 32 ? 4 * p + q : 0];
             uint32_t f = 0u;
 #pragma unroll
             for (int k = 0; k < PT; ++k)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int col = 16 * (p * PT + k) + 4 * g + i;
+                    const int col = 16 * (p * PT + k) + 4 * gz + i;
                     f |= ((sm.zcol[col >> 5] >> (col & 31)) & 1u) << (4 * (PT - 1 - k) + i);
                 }
-            zc.flags[p] = f;
+            sm.zlane[gz].flags[p] = f;
         }
     }
+    __syncthreads();
 
     // ---- the wave's groups, two register buffers: the next group loads
     // while this one is computed
@@ -730,7 +738,7 @@ __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
         const int64_t gi1 = gi + stride;
         const RGroup e1 = gi1 < n_groups ? group_of<R>(a, sm, gi1) : none;
         load_group(a, h, e1, g, c, xa1);
-        if (e0.nr > 0) encode_group<R>(a, sm, W, h, gi, e0, xa0, zc, wv, n_list);
+        if (e0.nr > 0) encode_group<R>(a, sm, W, h, gi, e0, xa0, wv, n_list);
         if (n_list > kRList / 2) {
             flush_list<R>(a, sm, W, h, n_list);
             n_list = 0;
@@ -738,7 +746,7 @@ __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
         const int64_t gi2 = gi1 + stride;
         e0 = gi2 < n_groups ? group_of<R>(a, sm, gi2) : none;
         load_group(a, h, e0, g, c, xa0);
-        if (e1.nr > 0) encode_group<R>(a, sm, W, h, gi1, e1, xa1, zc, wv, n_list);
+        if (e1.nr > 0) encode_group<R>(a, sm, W, h, gi1, e1, xa1, wv, n_list);
         if (n_list > kRList / 2) {
             flush_list<R>(a, sm, W, h, n_list);
             n_list = 0;
