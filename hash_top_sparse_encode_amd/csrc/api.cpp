@@ -62,7 +62,8 @@ hata_status hata_encode_keys(const uint16_t *keys, int64_t n_rows, int32_t n_hea
     // Bulk calls on the matrix cores (16-byte row pieces), small ones exact;
     // both give the same bits.
     const bool mfma = n_rows >= kMfmaMinRows && aligned16(keys) && row_stride % 8 == 0 &&
-                      head_stride % 8 == 0 && aligned16(codes_out);
+                      head_stride % 8 == 0 && aligned16(codes_out) &&
+                      rows_shape_fits(n_rows, 1, row_stride);
     hipError_t e = mfma ? launch_encode_rows(keys, n_rows, n_heads, row_stride, head_stride, w_h,
                                              kBits, codes_out, static_cast<hipStream_t>(stream))
                         : launch_encode_exact(keys, n_rows, n_heads, row_stride, head_stride, w_h,
@@ -83,7 +84,8 @@ hata_status hata_encode_keys_nbits(const uint16_t *keys, int64_t n_rows, int32_t
     if (row_stride < 0 || head_stride < 0) return HATA_ERR_INVALID_ARG;
     if (n_heads > 1 && head_stride < kHeadDim && row_stride < kHeadDim) return HATA_ERR_INVALID_ARG;
     if (!aligned16(keys) || row_stride % 8 || head_stride % 8) return HATA_ERR_INVALID_ARG;
-    hipError_t e = n_rows >= kMfmaMinRows && aligned16(codes_out)
+    hipError_t e = n_rows >= kMfmaMinRows && aligned16(codes_out) &&
+                           rows_shape_fits(n_rows, 1, row_stride)
                        ? launch_encode_rows(keys, n_rows, n_heads, row_stride, head_stride, w_h,
                                             n_bits, codes_out, static_cast<hipStream_t>(stream))
                        : launch_encode_bits(keys, n_rows, n_heads, row_stride, head_stride, w_h,
@@ -100,7 +102,8 @@ hata_status hata_append(const hata_cache *c, const uint16_t *k_new, const uint16
     if (t_max == 0) return HATA_OK;
     if (c->n_bits != kBits) {
         if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return HATA_ERR_INVALID_ARG;
-        hipError_t e = t_max >= kMfmaMinRows
+        hipError_t e = t_max >= kMfmaMinRows &&
+                               rows_shape_fits(t_max, c->batch, k_new ? (int64_t)c->n_kv_heads * kHeadDim : kHeadDim)
                            ? launch_append_rows(c->k, c->v, c->codes, c->seq_len, c->ctrl, c->batch,
                                                 c->n_kv_heads, c->max_ctx, k_new, v_new, n_new,
                                                 t_max, w_h, c->n_bits, static_cast<hipStream_t>(stream))
@@ -109,7 +112,8 @@ hata_status hata_append(const hata_cache *c, const uint16_t *k_new, const uint16
                                                 t_max, w_h, c->n_bits, static_cast<hipStream_t>(stream));
         return e == hipSuccess ? HATA_OK : HATA_ERR_HIP;
     }
-    const bool mfma = t_max >= kMfmaMinRows && (k_new == nullptr || (aligned16(k_new) && aligned16(v_new)));
+    const bool mfma = t_max >= kMfmaMinRows && (k_new == nullptr || (aligned16(k_new) && aligned16(v_new))) &&
+                      rows_shape_fits(t_max, c->batch, k_new ? (int64_t)c->n_kv_heads * kHeadDim : kHeadDim);
     hipError_t e = mfma ? launch_append_rows(c->k, c->v, c->codes, c->seq_len, c->ctrl, c->batch,
                                              c->n_kv_heads, c->max_ctx, k_new, v_new, n_new, t_max,
                                              w_h, kBits, static_cast<hipStream_t>(stream))

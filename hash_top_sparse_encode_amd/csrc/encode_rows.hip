@@ -85,8 +85,13 @@ struct RowsArgs {
     const uint16_t *k_new, *v_new;
     int B, Hkv, t_max;
     int64_t max_ctx;
-    // both
-    uint32_t *codes_base;  // codes_out (mode 0) or codes (mode 1), chosen on the host
+    // both, chosen on the host (a choice between two pointer fields of the
+    // argument block would be made through a private copy of it: a scratch
+    // load before each use)
+    const uint16_t *src_base;  // keys (mode 0), k_new or k_cache (mode 1)
+    uint32_t *codes_base;      // codes_out (mode 0) or codes (mode 1)
+    int src_step;              // elements from one row of a group to the next
+    int code_step;             // code words from one row of a group to the next
     const float *w;  // [heads][128][R]
     int n_heads;
     int64_t groups_per_seg;
@@ -124,12 +129,13 @@ __device__ __forceinline__ bool rows_append_ok(int64_t len, int n, int t_max, in
     return n >= 0 && n <= t_max && len >= 0 && len + n <= max_ctx;
 }
 
-// A group: its batch entry s, first row r0, the entry's length l0 and the rows
-// nr of the group (0 when past the work or the entry is skipped).
+// A group: its rows nr (0 when past the work or the entry is skipped) and
+// where its first row is: src elements from src_base, code words from
+// codes_base (row r of the group is r src_step and r code_step further; in
+// mode 1 the first row's cache row is code / (R / 32)).
 struct RGroup {
-    int s;
-    int64_t r0, l0;
     int nr;
+    int64_t src, code;
 };
 
 // A value the whole wave reads at one address, through the scalar cache (a
@@ -140,61 +146,96 @@ __device__ __forceinline__ int32_t uniform_load(const int32_t *p) {
     return *(const __attribute__((address_space(4))) int32_t *)p;
 }
 
-template <int R>
-__device__ __forceinline__ RGroup group_of(const RowsArgs &a, const RowsSmem<R> &sm, int64_t gi) {
-    RGroup e{0, 0, 0, 0};
-    e.s = (int)(gi / a.groups_per_seg);
-    e.r0 = (gi - (int64_t)e.s * a.groups_per_seg) * kRGroup;
+// Group gs (rows 64 gs ..) of batch entry s (mode 0: s = 0), head h.  With
+// Uniform (the same group in every lane), the lengths read from LDS are
+// moved to scalar registers, so that the offsets are scalar arithmetic and
+// the loads take a scalar base.
+template <int R, bool Uniform>
+__device__ __forceinline__ RGroup group_at(const RowsArgs &a, const RowsSmem<R> &sm, int h, int s,
+                                           int64_t gs) {
+    RGroup e{0, 0, 0};
+    const int64_t r0 = gs * kRGroup;
     int64_t rows;
     if (a.mode == 0) {
         rows = a.n_rows;
-    } else if (e.s < kRSegLds) {
-        e.l0 = sm.seg_l0[e.s];
-        rows = sm.seg_rows[e.s];
+        e.src = r0 * a.row_stride + (int64_t)h * a.head_stride;
+        e.code = r0 * a.code_step + (int64_t)h * (R / 32);
     } else {
-        e.l0 = uniform_load(a.seq_len + e.s);
-        const int n = uniform_load(a.n_new + e.s);
-        rows = rows_append_ok(e.l0, n, a.t_max, a.max_ctx) ? n : 0;
+        int64_t l0;
+        if (s < kRSegLds) {
+            l0 = sm.seg_l0[s];
+            rows = sm.seg_rows[s];
+            if (Uniform) {
+                const uint64_t l = (uint64_t)l0;
+                l0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(l >> 32)) << 32) |
+                               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)l));
+                rows = __builtin_amdgcn_readfirstlane((int)rows);
+            }
+        } else {
+            l0 = uniform_load(a.seq_len + s);
+            const int n = uniform_load(a.n_new + s);
+            rows = rows_append_ok(l0, n, a.t_max, a.max_ctx) ? n : 0;
+        }
+        const int64_t row0 = ((int64_t)s * a.Hkv + h) * a.max_ctx + l0 + r0;  // cache row
+        e.src = a.k_new ? (((int64_t)s * a.t_max + r0) * a.Hkv + h) * kHeadDim : row0 * kHeadDim;
+        e.code = row0 * (R / 32);
     }
-    e.nr = e.r0 < rows ? (int)(rows - e.r0 < kRGroup ? rows - e.r0 : kRGroup) : 0;
+    e.nr = r0 < rows ? (int)(rows - r0 < kRGroup ? rows - r0 : kRGroup) : 0;
     return e;
 }
 
-// Source of row r (0 .. 63) of a group of head h; rows past the group's
-// count read its first row.
-__device__ __forceinline__ const uint16_t *src_row(const RowsArgs &a, int h, const RGroup &e, int r) {
-    const int64_t rr = e.r0 + (r < e.nr ? r : 0);
-    if (a.mode == 0) return a.keys + rr * a.row_stride + (int64_t)h * a.head_stride;
-    if (a.k_new) return a.k_new + (((int64_t)e.s * a.t_max + rr) * a.Hkv + h) * kHeadDim;
-    return a.k_cache + (((int64_t)e.s * a.Hkv + h) * a.max_ctx + e.l0 + rr) * kHeadDim;
+// A group without rows, whose loads read row 0 of the head (entry 0's row 0
+// in mode 1: a valid address whatever the entry's length).
+__device__ __forceinline__ RGroup no_group(const RowsArgs &a, int h) {
+    RGroup e{0, 0, 0};
+    e.src = a.mode == 0 ? (int64_t)h * a.head_stride
+                        : (a.k_new ? (int64_t)h * kHeadDim : (int64_t)h * a.max_ctx * kHeadDim);
+    return e;
 }
 
-// Cache row (mode 1) of row r of a group.
-__device__ __forceinline__ int64_t cache_row(const RowsArgs &a, int h, const RGroup &e, int r) {
-    return ((int64_t)e.s * a.Hkv + h) * a.max_ctx + e.l0 + e.r0 + r;
+// Source of row r (0 .. 63) of a group; rows past the group's count read its
+// first row.  The per-row part is 32-bit (the host keeps 63 src_step below
+// 2^31), so the loads take a uniform base and a 32-bit lane offset.
+__device__ __forceinline__ const uint16_t *src_row(const RowsArgs &a, const RGroup &e, int r) {
+    const uint32_t rr = (uint32_t)(r < e.nr ? r : 0);
+    return a.src_base + e.src + rr * (uint32_t)a.src_step;
 }
 
-// The code words of row r of a group.  One base pointer and a row index per
-// mode: a choice between two pointer fields of the argument block would be
-// made by the compiler through a private copy of it (a scratch load before
-// each store, and flat stores that also hold up the LDS waits).
+// Code word k of row r of a group (a uniform base and a 32-bit byte
+// offset: the store address form with the base in scalar registers).
 template <int R>
-__device__ __forceinline__ uint32_t *code_row(const RowsArgs &a, int h, const RGroup &e, int r) {
-    const int64_t row = a.mode == 0 ? (e.r0 + r) * a.n_heads + h : cache_row(a, h, e, r);
-    return a.codes_base + row * (R / 32);
+__device__ __forceinline__ uint32_t *code_word(const RowsArgs &a, const RGroup &e, int r, int k) {
+    char *base = reinterpret_cast<char *>(a.codes_base + e.code);
+    return reinterpret_cast<uint32_t *>(
+        base + (uint64_t)((uint32_t)r * (uint32_t)(4 * a.code_step) + 4u * (uint32_t)k));
+}
+
+// The lane number, as a value the compiler cannot move: what is formed from
+// it stays where it is used instead of being hoisted out of the group loop
+// and held in registers throughout.
+__device__ __forceinline__ int lane_here() {
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    return ln;
 }
 
 // The sixteen 16-byte B-operand loads of a group (lane (g, c): rows 16 t + c,
 // dims 32 j + 8 g .. + 8; each instruction reads 64 contiguous bytes of 16
-// rows).  A group without rows reads row 0 of the first entry instead.
-__device__ __forceinline__ void load_group(const RowsArgs &a, int h, const RGroup &e, int g, int c,
+// rows).  A group without rows comes as no_group: a valid address.
+__device__ __forceinline__ void load_group(const RowsArgs &a, const RGroup &e, int g, int c,
                                            uvec4 (&xa)[kRTiles][4]) {
-    const RGroup ee = e.nr > 0 ? e : RGroup{0, 0, 0, 0};
+    // a uniform base and one 32-bit element offset per load: the address
+    // form with the base in scalar registers
+    // (in bytes: an element offset doubled could pass 2^32 as far as the
+    // compiler knows)
+    const char *base = reinterpret_cast<const char *>(a.src_base + e.src);
 #pragma unroll
     for (int t = 0; t < kRTiles; ++t) {
-        const uint16_t *src = src_row(a, h, ee, 16 * t + c) + 8 * g;
+        const int r = 16 * t + c;
+        const uint32_t off = (uint32_t)(r < e.nr ? r : 0) * (uint32_t)(2 * a.src_step) + 16u * (uint32_t)g;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xa[t][j] = *reinterpret_cast<const uvec4 *>(src + 32 * j);
+        for (int j = 0; j < 4; ++j)
+            xa[t][j] = *reinterpret_cast<const uvec4 *>(base + (uint64_t)(off + 64u * j));
     }
 }
 
@@ -270,11 +311,13 @@ __device__ __forceinline__ void flush_list(const RowsArgs &a, RowsSmem<R> &sm, c
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll 1
     for (int b = lane; b < count; b += 64) {
-        const int64_t gi = sm.lgrp[wv][b];
+        // (a 32-bit division: the host keeps the group count below 2^32)
+        const uint32_t gi = sm.lgrp[wv][b], gps = (uint32_t)a.groups_per_seg;
+        const uint32_t es = gi / gps;
         const int rc = sm.lrc[wv][b], row = rc >> 8, col = rc & 255;
-        const RGroup e = group_of<R>(a, sm, gi);
-        const double y = exact_sum<R>(sm, W, src_row(a, h, e, row), col);
-        uint32_t *word = code_row<R>(a, h, e, row) + (col >> 5);
+        const RGroup e = group_at<R, false>(a, sm, h, (int)es, gi - es * gps);
+        const double y = exact_sum<R>(sm, W, src_row(a, e, row), col);
+        uint32_t *word = code_word<R>(a, e, row, col >> 5);
         const uint32_t bit = 1u << (col & 31);
         if (y > 0.0)
             atomicOr(word, bit);
@@ -294,12 +337,12 @@ __device__ __forceinline__ void exact_group(const RowsArgs &a, const RowsSmem<R>
 #pragma unroll 1
     for (int w = lane; w < e.nr * NW; w += 64) {
         const int row = w / NW, k = w % NW;
-        const uint16_t *xr = src_row(a, h, e, row);
+        const uint16_t *xr = src_row(a, e, row);
         uint32_t word = 0u;
 #pragma unroll 1
         for (int b = 0; b < 32; ++b)
             if (exact_sum<R>(sm, W, xr, 32 * k + b) > 0.0) word |= 1u << b;
-        code_row<R>(a, h, e, row)[k] = word;
+        *code_word<R>(a, e, row, k) = word;
     }
 }
 
@@ -570,35 +613,32 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
         // ---- store: lane (g, c) of row tile t writes word 4 p + q(g) of row
         // 16 t + c.  Codes are 1 for y' > 0: the complement of the sign bits,
         // with columns of zeros and rows of zeros at 0.
-        // (the lane's word offset is formed here from the lane number, per
-        // group: hoisted out of the loop, base + offset would hold two more
-        // registers throughout)
-        int ln;
-        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-        const int gg = (ln >> 4) & 3;
+        // (the addresses are formed here from lane_here(), per group)
+        const int ln = lane_here(), gg = (ln >> 4) & 3, cc = ln & 15;
         const int qq = ((gg & 1) << 1) | (gg >> 1);
         const ZeroCols<R> &zs = sm.zlane[gg];
 #pragma unroll
         for (int t = 0; t < kRTiles; ++t) {
-            const int row = 16 * t + c;
-            uint32_t *dst = code_row<R>(a, h, e, row);
+            const int row = 16 * t + cc;
             const bool live = row < e.nr;
 #pragma unroll
             for (int p = 0; p < NPASS; ++p) {
                 const uint32_t o = th[t] < 0.f ? 0u : ~(word[t][p] | zs.word[p]);
-                if (live && 4 * p + qq < NW) dst[4 * p + qq] = o;
+                if (live && 4 * p + qq < NW) *code_word<R>(a, e, row, 4 * p + qq) = o;
             }
         }
     }
     // ---- appended rows into the cache: K from the registers, V copied
     if (a.mode == 1 && a.k_new) {
+        const int ln = lane_here(), gk = (ln >> 4) & 3, ck = ln & 15;
 #pragma unroll
         for (int t = 0; t < kRTiles; ++t) {
-            const int r = 16 * t + c;
+            const int r = 16 * t + ck;
             if (r < e.nr) {
-                uint16_t *kd = a.k_cache + cache_row(a, h, e, r) * kHeadDim + 8 * g;
-                uint16_t *vd = a.v_cache + cache_row(a, h, e, r) * kHeadDim + 8 * g;
-                const uint16_t *vs = a.v_new + (((int64_t)e.s * a.t_max + e.r0 + r) * a.Hkv + h) * kHeadDim + 8 * g;
+                const int64_t crow = e.code / (R / 32) + r;   // cache row
+                uint16_t *kd = a.k_cache + crow * kHeadDim + 8 * gk;
+                uint16_t *vd = a.v_cache + crow * kHeadDim + 8 * gk;
+                const uint16_t *vs = a.v_new + e.src + (int64_t)r * a.src_step + 8 * gk;
                 uvec4 vv[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) vv[j] = *reinterpret_cast<const uvec4 *>(vs + 32 * j);
@@ -721,31 +761,48 @@ __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
     __syncthreads();
 
     // ---- the wave's groups, two register buffers: the next group loads
-    // while this one is computed
-    const int64_t n_groups = a.groups_per_seg * a.n_seg;
+    // while this one is computed.  Group gi of the head is group gi mod G of
+    // batch entry gi / G (G groups per entry); the wave takes every
+    // stride-th, from blockIdx.x * waves + wave, and steps the (entry, group)
+    // pair by (stride / G, stride mod G) with a carry (no division per step).
+    const int64_t gps = a.groups_per_seg;
     const int64_t stride = (int64_t)gridDim.x * kRWaves;
-    const RGroup none{0, 0, 0, 0};
+    const int64_t step_s = stride / gps, step_g = stride - step_s * gps;
+    const RGroup none = no_group(a, h);
     int64_t gi = (int64_t)blockIdx.x * kRWaves + wv;
+    int64_t cs = gi / gps, cg = gi - cs * gps;   // entry and group of gi
     uvec4 xa0[kRTiles][4], xa1[kRTiles][4];
     int n_list = 0;  // in-band bits listed by this wave, not yet resolved (uniform)
     // The loads are issued whether or not the group has rows (one past the
     // work, or skipped, reads row 0 of the head: a valid address), so that
     // the count of loads in flight is the same on every path and a group's
     // use waits only for its own loads.
-    RGroup e0 = gi < n_groups ? group_of<R>(a, sm, gi) : none;
-    load_group(a, h, e0, g, c, xa0);
-    while (gi < n_groups) {
+    RGroup e0 = cs < a.n_seg ? group_at<R, true>(a, sm, h, (int)cs, cg) : none;
+    load_group(a, e0.nr > 0 ? e0 : none, g, c, xa0);
+    while (cs < a.n_seg) {
+        cg += step_g;
+        cs += step_s;
+        if (cg >= gps) {
+            cg -= gps;
+            ++cs;
+        }
         const int64_t gi1 = gi + stride;
-        const RGroup e1 = gi1 < n_groups ? group_of<R>(a, sm, gi1) : none;
-        load_group(a, h, e1, g, c, xa1);
+        const RGroup e1 = cs < a.n_seg ? group_at<R, true>(a, sm, h, (int)cs, cg) : none;
+        load_group(a, e1.nr > 0 ? e1 : none, g, c, xa1);
         if (e0.nr > 0) encode_group<R>(a, sm, W, h, gi, e0, xa0, wv, n_list);
         if (n_list > kRList / 2) {
             flush_list<R>(a, sm, W, h, n_list);
             n_list = 0;
         }
+        cg += step_g;
+        cs += step_s;
+        if (cg >= gps) {
+            cg -= gps;
+            ++cs;
+        }
         const int64_t gi2 = gi1 + stride;
-        e0 = gi2 < n_groups ? group_of<R>(a, sm, gi2) : none;
-        load_group(a, h, e0, g, c, xa0);
+        e0 = cs < a.n_seg ? group_at<R, true>(a, sm, h, (int)cs, cg) : none;
+        load_group(a, e0.nr > 0 ? e0 : none, g, c, xa0);
         if (e1.nr > 0) encode_group<R>(a, sm, W, h, gi1, e1, xa1, wv, n_list);
         if (n_list > kRList / 2) {
             flush_list<R>(a, sm, W, h, n_list);
@@ -814,6 +871,7 @@ hipError_t dispatch_rows(RowsArgs &a, int n_bits, int heads, int64_t groups_per_
 hipError_t launch_encode_rows(const uint16_t *keys, int64_t n_rows, int n_heads, int64_t row_stride,
                               int64_t head_stride, const float *w, int n_bits, uint32_t *codes,
                               hipStream_t s) {
+    if (!rows_shape_fits(n_rows, 1, row_stride)) return hipErrorInvalidValue;
     RowsArgs a = {};
     a.mode = 0;
     a.keys = keys;
@@ -821,7 +879,10 @@ hipError_t launch_encode_rows(const uint16_t *keys, int64_t n_rows, int n_heads,
     a.head_stride = head_stride;
     a.n_rows = n_rows;
     a.codes_out = codes;
+    a.src_base = keys;
     a.codes_base = codes;
+    a.src_step = (int)row_stride;
+    a.code_step = n_heads * (n_bits / 32);
     a.w = w;
     a.n_heads = n_heads;
     a.n_seg = 1;
@@ -833,12 +894,16 @@ hipError_t launch_append_rows(uint16_t *k_cache, uint16_t *v_cache, uint32_t *co
                               int32_t *seq_len, int32_t *ctrl, int B, int Hkv, int64_t max_ctx,
                               const uint16_t *k_new, const uint16_t *v_new, const int32_t *n_new,
                               int t_max, const float *w, int n_bits, hipStream_t s) {
+    if (!rows_shape_fits(t_max, B, k_new ? (int64_t)Hkv * kHeadDim : kHeadDim)) return hipErrorInvalidValue;
     RowsArgs a = {};
     a.mode = 1;
     a.k_cache = k_cache;
     a.v_cache = v_cache;
     a.codes = codes;
+    a.src_base = k_new ? k_new : k_cache;
     a.codes_base = codes;
+    a.src_step = k_new ? Hkv * kHeadDim : kHeadDim;
+    a.code_step = n_bits / 32;
     a.seq_len = seq_len;
     a.ctrl = ctrl;
     a.n_new = n_new;

@@ -52,6 +52,14 @@ hipError_t launch_append_exact(uint16_t *k_cache, uint16_t *v_cache, uint32_t *c
 // multiples of 8 elements).
 constexpr int kMfmaMinRows = 64;
 
+// Shapes the bulk encoder indexes in 32 bits: fewer than 2^32 groups of 64
+// rows over all batch entries, and 63 row steps (elements) below 2^31.
+inline bool rows_shape_fits(int64_t rows_per_entry, int64_t n_entries, int64_t row_step) {
+    if (rows_per_entry < 0 || n_entries <= 0 || row_step < 0) return false;
+    const int64_t groups = (rows_per_entry + 63) / 64;
+    return groups <= (int64_t)0xFFFFFFFF / n_entries && row_step < ((int64_t)1 << 31) / 63;
+}
+
 // Bulk encoder on the matrix cores for every code length (encode_rows.hip):
 // flat rows, and cache appends (K / V rows copied when k_new is given, the
 // last workgroup publishes the lengths).  Same bits as the exact kernels.
