@@ -270,35 +270,63 @@ __device__ __forceinline__ uint32_t or_transpose4(uint32_t u0, uint32_t u1, uint
 // The defining sum of bit `col` of a row (sequential, d = 0 .. 127; every
 // product of a bf16 and an fp32 value is exact in double).  The row is read
 // in quarters of four 16-byte loads issued together.
-template <int R>
+// The defining sum of one bit: y = sum over d of x_d W_dj, sequentially in
+// double (each product of a bf16 and an fp32 is exact in double).  W comes
+// from the transposed copy in LDS (r <= 128) or from memory (r = 256).
+// Wide (the flush at r = 256, where W comes from memory and the group just
+// encoded has freed its registers): the row (16 pieces of 16 bytes) is
+// loaded at once, so that its latency is paid once, then W a quarter at a
+// time; otherwise a quarter of the row and of W at a time (at r <= 128 the
+// wide form measured slower).
+template <int R, bool Wide>
 __device__ __forceinline__ double exact_sum(const RowsSmem<R> &sm, const float *W, const uint16_t *xr,
                                             int col) {
-    double y = 0.0;
+    if constexpr (!Wide) {
+        double y = 0.0;
 #pragma unroll 1
-    for (int d0 = 0; d0 < kHeadDim; d0 += 32) {
-        uvec4 xv[4];
+        for (int d0 = 0; d0 < kHeadDim; d0 += 32) {
+            uvec4 xq[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) xv[k] = *reinterpret_cast<const uvec4 *>(xr + d0 + 8 * k);
+            for (int k = 0; k < 4; ++k) xq[k] = *reinterpret_cast<const uvec4 *>(xr + d0 + 8 * k);
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+            for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int d = d0 + 8 * k + 2 * q;
-                float w0, w1;
-                if constexpr (R <= 128) {
-                    w0 = sm.wt[col][d];
-                    w1 = sm.wt[col][d + 1];
-                } else {
-                    w0 = W[(int64_t)d * R + col];
-                    w1 = W[(int64_t)(d + 1) * R + col];
+                for (int q = 0; q < 4; ++q) {
+                    const int d = d0 + 8 * k + 2 * q;
+                    const float w0 = R <= 128 ? sm.wt[R <= 128 ? col : 0][d] : W[(int64_t)d * R + col];
+                    const float w1 = R <= 128 ? sm.wt[R <= 128 ? col : 0][d + 1] : W[(int64_t)(d + 1) * R + col];
+                    const uint32_t u = xq[k][q];
+                    y = fma((double)__uint_as_float(u << 16), (double)w0, y);
+                    y = fma((double)__uint_as_float(u & 0xFFFF0000u), (double)w1, y);
                 }
-                // the element goes through a scalar (see the row norms)
-                const uint32_t u = xv[k][q];
-                y = fma((double)__uint_as_float(u << 16), (double)w0, y);
-                y = fma((double)__uint_as_float(u & 0xFFFF0000u), (double)w1, y);
-            }
+        }
+        return y;
+    } else {
+        static_assert(R > 128, "the wide form is for W read from memory");
+        uvec4 xv[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) xv[k] = *reinterpret_cast<const uvec4 *>(xr + 8 * k);
+        double y = 0.0;
+        // (a quarter of W at a time: with two in flight the flush would
+        // not fit beside the prefetched group's registers)
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+            float wq[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) wq[i] = W[(int64_t)(32 * qt + i) * R + col];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int i = 8 * k + 2 * q;
+                    const uint32_t u = xv[4 * qt + k][q];
+                    y = fma((double)__uint_as_float(u << 16), (double)wq[i], y);
+                    y = fma((double)__uint_as_float(u & 0xFFFF0000u), (double)wq[i + 1], y);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return y;
     }
-    return y;
 }
 
 // Resolve a wave's listed in-band bits: one lane per bit runs the defining
@@ -316,7 +344,7 @@ __device__ __forceinline__ void flush_list(const RowsArgs &a, RowsSmem<R> &sm, c
         const uint32_t es = gi / gps;
         const int rc = sm.lrc[wv][b], row = rc >> 8, col = rc & 255;
         const RGroup e = group_at<R, false>(a, sm, h, (int)es, gi - es * gps);
-        const double y = exact_sum<R>(sm, W, src_row(a, e, row), col);
+        const double y = exact_sum<R, (R > 128)>(sm, W, src_row(a, e, row), col);
         uint32_t *word = code_word<R>(a, e, row, col >> 5);
         const uint32_t bit = 1u << (col & 31);
         if (y > 0.0)
@@ -341,7 +369,7 @@ __device__ __forceinline__ void exact_group(const RowsArgs &a, const RowsSmem<R>
         uint32_t word = 0u;
 #pragma unroll 1
         for (int b = 0; b < 32; ++b)
-            if (exact_sum<R>(sm, W, xr, 32 * k + b) > 0.0) word |= 1u << b;
+            if (exact_sum<R, false>(sm, W, xr, 32 * k + b) > 0.0) word |= 1u << b;
         *code_word<R>(a, e, row, k) = word;
     }
 }
@@ -569,7 +597,8 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
     // ---- list the in-band bits: band flag 0, columns of zeros excepted
     // (their bit is 0), rows past the group's count skipped.  Flag bit
     // 4 (PT - 1 - k) + i of pass p is column 16 (p PT + k) + 4 g + i.  Each
-    // lane writes its own entries, at its place in the wave's prefix sum.
+    // lane writes its own entries, at its place in one prefix sum over the
+    // wave of the lanes' counts.
     const int list0 = n_list;  // this group's entries start here (uniform)
     constexpr uint32_t kFlagMask = PT == 8 ? 0xFFFFFFFFu : (1u << (4 * PT)) - 1u;
     // (the zero-column masks are read from LDS here and before the stores,
@@ -578,31 +607,39 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
     int gz = g;
     asm volatile("" : "+v"(gz));
     const ZeroCols<R> &zc = sm.zlane[gz];
+    uint32_t inb[NPASS][kRTiles];
+    int cnt = 0;
 #pragma unroll
     for (int p = 0; p < NPASS; ++p)
 #pragma unroll
         for (int t = 0; t < kRTiles; ++t) {
-            const int row = 16 * t + c;
-            uint32_t inb = row < e.nr ? ~dec[t][p] & kFlagMask & ~zc.flags[p] : 0u;
-            if (__builtin_amdgcn_ballot_w64(inb != 0u) == 0) continue;
-            const int cnt = __builtin_popcount(inb);
-            const int incl = wave_incl_scan(cnt);
-            const int total = __builtin_amdgcn_readlane(incl, 63);
-            if (n_list + total > kRList) {
-                overflow = true;
-                continue;
-            }
+            inb[p][t] = 16 * t + c < e.nr ? ~dec[t][p] & kFlagMask & ~zc.flags[p] : 0u;
+            cnt += __builtin_popcount(inb[p][t]);
+        }
+    if (__builtin_amdgcn_ballot_w64(cnt != 0) != 0) {
+        const int incl = wave_incl_scan(cnt);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (n_list + total > kRList) {
+            overflow = true;
+        } else {
             int pos = n_list + incl - cnt;
-            while (inb) {
-                const int b = __builtin_ctz(inb);
-                inb &= inb - 1;
-                const int col = 16 * (p * PT + PT - 1 - (b >> 2)) + 4 * g + (b & 3);
-                sm.lgrp[wv][pos] = (uint32_t)gi;
-                sm.lrc[wv][pos] = (uint16_t)((row << 8) | col);
-                ++pos;
-            }
+#pragma unroll
+            for (int p = 0; p < NPASS; ++p)
+#pragma unroll
+                for (int t = 0; t < kRTiles; ++t) {
+                    uint32_t m = inb[p][t];
+                    while (m) {
+                        const int b = __builtin_ctz(m);
+                        m &= m - 1;
+                        const int col = 16 * (p * PT + PT - 1 - (b >> 2)) + 4 * g + (b & 3);
+                        sm.lgrp[wv][pos] = (uint32_t)gi;
+                        sm.lrc[wv][pos] = (uint16_t)(((16 * t + c) << 8) | col);
+                        ++pos;
+                    }
+                }
             n_list += total;
         }
+    }
 
     if (overflow) {
         // too many in-band bits, or a non-finite row: every word of the group
