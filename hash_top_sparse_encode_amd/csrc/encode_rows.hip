@@ -354,6 +354,32 @@ __device__ __forceinline__ void flush_list(const RowsArgs &a, RowsSmem<R> &sm, c
     }
 }
 
+// Resolve the listed bits in whole rounds of 64, one per lane (a round
+// costs the latency of its loads however few lanes it has), or all of them
+// when `all`; the entries left over move to the front of the wave's list.
+// Returns how many are left.
+template <int R>
+__device__ __forceinline__ int flush_rounds(const RowsArgs &a, RowsSmem<R> &sm, const float *W, int h,
+                                            int count, bool all) {
+    const int done = all ? count : (count & ~63);
+    if (done > 0) flush_list<R>(a, sm, W, h, done);
+    const int rest = count - done;   // below 64
+    if (rest > 0) {
+        const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        uint32_t gq = 0u;
+        uint16_t rc = 0;
+        if (lane < rest) {
+            gq = sm.lgrp[wv][done + lane];
+            rc = sm.lrc[wv][done + lane];
+        }
+        if (lane < rest) {
+            sm.lgrp[wv][lane] = gq;
+            sm.lrc[wv][lane] = rc;
+        }
+    }
+    return rest;
+}
+
 // Every code word of a group by the defining sums (a group with more in-band
 // bits than the list holds: rows with a non-finite value, degenerate rows):
 // one lane per word.
@@ -827,10 +853,7 @@ __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
         const RGroup e1 = cs < a.n_seg ? group_at<R, true>(a, sm, h, (int)cs, cg) : none;
         load_group(a, e1.nr > 0 ? e1 : none, g, c, xa1);
         if (e0.nr > 0) encode_group<R>(a, sm, W, h, gi, e0, xa0, wv, n_list);
-        if (n_list > kRList / 2) {
-            flush_list<R>(a, sm, W, h, n_list);
-            n_list = 0;
-        }
+        if (n_list >= 64) n_list = flush_rounds<R>(a, sm, W, h, n_list, false);
         cg += step_g;
         cs += step_s;
         if (cg >= gps) {
@@ -841,13 +864,10 @@ __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
         e0 = cs < a.n_seg ? group_at<R, true>(a, sm, h, (int)cs, cg) : none;
         load_group(a, e0.nr > 0 ? e0 : none, g, c, xa0);
         if (e1.nr > 0) encode_group<R>(a, sm, W, h, gi1, e1, xa1, wv, n_list);
-        if (n_list > kRList / 2) {
-            flush_list<R>(a, sm, W, h, n_list);
-            n_list = 0;
-        }
+        if (n_list >= 64) n_list = flush_rounds<R>(a, sm, W, h, n_list, false);
         gi = gi2;
     }
-    if (n_list > 0) flush_list<R>(a, sm, W, h, n_list);
+    if (n_list > 0) flush_rounds<R>(a, sm, W, h, n_list, true);
 
     if (a.mode == 1) {
         // The last workgroup to finish publishes the new lengths (every
