@@ -233,9 +233,11 @@ __device__ __forceinline__ void load_group(const RowsArgs &a, const RGroup &e, i
     for (int t = 0; t < kRTiles; ++t) {
         const int r = 16 * t + c;
         const uint32_t off = (uint32_t)(r < e.nr ? r : 0) * (uint32_t)(2 * a.src_step) + 16u * (uint32_t)g;
+        // (the 64 j bytes added after the extension go into the
+        // instructions' immediate offsets)
+        const uvec4 *src = reinterpret_cast<const uvec4 *>(base + (uint64_t)off);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            xa[t][j] = *reinterpret_cast<const uvec4 *>(base + (uint64_t)(off + 64u * j));
+        for (int j = 0; j < 4; ++j) xa[t][j] = src[4 * j];
     }
 }
 
@@ -679,14 +681,18 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
         // (the addresses are formed here from lane_here(), per group)
         const int ln = lane_here(), gg = (ln >> 4) & 3, cc = ln & 15;
         const int qq = ((gg & 1) << 1) | (gg >> 1);
-        const ZeroCols<R> &zs = sm.zlane[gg];
+        // (the masks read once, ahead of the selects below: read inside them
+        // they would take one LDS round trip per row tile)
+        uint32_t zw[NPASS];
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) zw[p] = sm.zlane[gg].word[p];
 #pragma unroll
         for (int t = 0; t < kRTiles; ++t) {
             const int row = 16 * t + cc;
             const bool live = row < e.nr;
 #pragma unroll
             for (int p = 0; p < NPASS; ++p) {
-                const uint32_t o = th[t] < 0.f ? 0u : ~(word[t][p] | zs.word[p]);
+                const uint32_t o = th[t] < 0.f ? 0u : ~(word[t][p] | zw[p]);
                 if (live && 4 * p + qq < NW) *code_word<R>(a, e, row, 4 * p + qq) = o;
             }
         }
