@@ -175,19 +175,22 @@ def measured_traffic_bytes():
         return None
 
 
-def encode_intervals(call, n, stream):
-    """ms of each of n calls of `call` queued behind one untimed call, with an
-    event recorded between consecutive calls; the host issues each call while
-    the device still runs the one before, so the intervals are device time."""
+def encode_intervals(prep, call, n, stream):
+    """ms of each of n calls of `call`, each after `prep` (the reset that lets
+    the same rows be encoded again), queued behind one untimed round, with an
+    event pair around each call only; the host issues each round while the
+    device still runs the one before, so the intervals are device time."""
     import torch
+    prep()
     call()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-    for i in range(n):
-        ev[i].record(stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in ev:
+        prep()
+        e0.record(stream)
         call()
-    ev[n].record(stream)
+        e1.record(stream)
     torch.cuda.synchronize()
-    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+    return [e0.elapsed_time(e1) for e0, e1 in ev]
 
 
 def cpu_baseline(spec, reps):
@@ -318,16 +321,9 @@ def measure_config(cfg, args, dev, cores):
           flush=True)
     base = GpuWorkload(spec, dev, extra_ctx=per_layer)
     stream = torch.cuda.current_stream()
-    enc = []
-    for _ in range(2):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        base.encode_prefill()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        enc.append(e0.elapsed_time(e1))
+    enc = encode_intervals(base.cache.seq_len.zero_, base.append_prefill, 3, stream)
     enc_rows = Hkv * sum(n - 1 for n in spec.lengths)
-    enc_s = enc[-1] * 1e-3
+    enc_s = statistics.mean(enc) * 1e-3
     caches = [(base.cache, base.ws)]
     for i in range(1, L):
         c = hata.HataCache(B, Hq, Hkv, base.max_ctx, device=dev, k=base.cache.k.clone(),
@@ -625,10 +621,11 @@ def main():
 
     # The prefill encode of the same workload (hata_append over the N - 1
     # prefilled rows of every sequence, codes computed in place): calls queued
-    # back to back behind an untimed one, an event between each pair, so that
-    # each interval is the device's time for one call (its seq_len fill and
-    # the encode) and not the host's time to issue it.
-    enc_ms = encode_intervals(base.encode_prefill, 3, stream)
+    # back to back behind an untimed one, each after the seq_len reset that
+    # lets the same rows be encoded again, an event pair around each call
+    # only, so that each interval is the device's time for the encode and not
+    # the host's time to issue it.
+    enc_ms = encode_intervals(base.cache.seq_len.zero_, base.append_prefill, 3, stream)
     enc_rows = Hkv * sum(n - 1 for n in spec.lengths)
     enc_s = statistics.mean(enc_ms) * 1e-3
     prefill = {
@@ -735,10 +732,9 @@ def main():
         c_r = hata.HataCache(B, Hq, Hkv, base.max_ctx, device=dev, k=base.cache.k.clone(),
                              v=base.cache.v.clone(), n_bits=r)
         def encode_r():
-            c_r.seq_len.zero_()
             hata.hata_append(c_r, None, None, base.n_pre, spec.max_len - 1, w_r)
 
-        enc_t = encode_intervals(encode_r, 2, stream)
+        enc_t = encode_intervals(c_r.seq_len.zero_, encode_r, 3, stream)
         rot = [(c_r, hata.alloc_workspace(c_r, base.k_max))]
         for i in range(1, L_r):
             c = hata.HataCache(B, Hq, Hkv, base.max_ctx, device=dev, k=base.cache.k.clone(),
@@ -770,7 +766,8 @@ def main():
         code_lengths.append({"n_bits": r, "us_per_step": us, "steps_per_s": 1e6 / us,
                              "alg_bytes": alg_r, "alg_GBps": alg_r / us / 1e3,
                              "hbm_frac": alg_r / us / 1e3 / HBM_PEAK_GBS,
-                             "layer_caches": L_r, "prefill_encode_ms": enc_t[-1]})
+                             "layer_caches": L_r, "prefill_encode_ms": statistics.mean(enc_t),
+                             "prefill_encode_vs_128": statistics.mean(enc_t) / (enc_s * 1e3)})
         del rot, c_r
         torch.cuda.empty_cache()
     base.cache.seq_len.copy_(base.n_pre)

@@ -28,24 +28,27 @@
 // eight waves work independently, with no barrier after the set-up: wave w
 // takes 64-row groups w, w + 8 P, ... of the head (P workgroups per head),
 // and while it computes one group the next group's rows are already loading
-// into a second set of registers.  The product is taken transposed,
-// y'^T = W'^T x^T: the A operand is a 16-column tile of W'^T (its bf16 high
-// and low parts, laid out per lane in LDS at the set-up and read once per
-// tile for all 64 rows), the B operand the rows: lane (g, c) of row tile t
-// holds row 16 t + c, dims 32 j + 8 g .. + 8 for k step j.  The result then
-// gives lane (g, c) the values of row 16 t + c at columns 16 n + 4 g + i,
-// i < 4, so the threshold is one per lane and row tile.  Per column tile,
-// the band test is one min over the lane's four |y'| per row tile; the sign
-// bits are shifted into a per-lane word (v_alignbit), two column tiles per
-// code word; after the last tile, lane swaps across the four lanes of a row
-// (v_permlane32_swap, v_permlane16_swap) OR the pieces so that lane (g, c)
-// holds code word g (r <= 128) or words 2 g, 2 g + 1 (r = 256) of its row,
-// which it stores.  In-band bits get the provisional sign of y' and are
-// listed in LDS (group, row, column); between groups, once the list is half
-// full, and at the end, the wave resolves them (one lane per bit runs the
-// defining sequential double sum, with W_H's column from LDS for r <= 128 or
-// from memory for r = 256) and sets or clears the bit.  A group with more
-// in-band bits than the list holds is computed entirely by the exact sum.
+// into a second set of registers.  A group's offsets are scalar, its loads
+// and stores a scalar base and a 32-bit lane offset.  The product is taken
+// transposed, y'^T = W'^T x^T: the A operand is a 16-column tile of W'^T
+// (its bf16 high and low parts, laid out per lane in LDS at the set-up and
+// read once per tile for all 64 rows), the B operand the rows: lane (g, c)
+// of row tile t holds row 16 t + c, dims 32 j + 8 g .. + 8 for k step j.
+// The result then gives lane (g, c) the values of row 16 t + c at columns
+// 16 n + 4 g + i, i < 4, so the threshold is one per lane and row tile.  Per
+// column tile and element, the sign bit and the band flag (the sign of
+// th - |y'|) are shifted into per-lane words (v_alignbit), while the next
+// tile's products issue; after the tiles of a pass (128 columns, or r),
+// lane swaps across the four lanes of a row (v_permlane32_swap,
+// v_permlane16_swap) OR the sign pieces so that lane (g, c) holds code word
+// 4 p + q(g) of its row, q(g) = {0, 2, 1, 3}[g], which it stores.  In-band
+// bits get the provisional sign of y' and are listed in LDS (group, row,
+// column) at each lane's place in one prefix sum over the wave; once the
+// list holds 64, and at the end, the wave resolves them in whole rounds of
+// 64 (one lane per bit runs the defining sequential double sum, with W_H's
+// column from LDS for r <= 128 or from memory for r = 256) and sets or
+// clears the bit.  A group with more in-band bits than the list holds is
+// computed entirely by the exact sums.
 #include "device_util.h"
 #include "hata_internal.h"
 #include "../../include/hata.h"
@@ -693,7 +696,16 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
 #pragma unroll
             for (int p = 0; p < NPASS; ++p) {
                 const uint32_t o = th[t] < 0.f ? 0u : ~(word[t][p] | zw[p]);
-                if (live && 4 * p + qq < NW) *code_word<R>(a, e, row, 4 * p + qq) = o;
+                if (live && 4 * p + qq < NW) {
+                    // streaming stores (the kernel touches a stored word
+                    // again only for an in-band bit, by an atomic after its
+                    // stores have completed); measured faster at r <= 128,
+                    // not at 256
+                    if constexpr (R <= 128)
+                        __builtin_nontemporal_store(o, code_word<R>(a, e, row, 4 * p + qq));
+                    else
+                        *code_word<R>(a, e, row, 4 * p + qq) = o;
+                }
             }
         }
     }

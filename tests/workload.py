@@ -75,6 +75,10 @@ class GpuWorkload:
     def encode_prefill(self):
         """Codes of the prefilled rows through hata_append (encode in place)."""
         self.cache.seq_len.zero_()
+        self.append_prefill()
+
+    def append_prefill(self):
+        """The hata_append call of encode_prefill, with seq_len already zero."""
         hata.hata_append(self.cache, None, None, self.n_pre, max(self.spec.max_len - 1, 0),
                          self.w)
 
