@@ -542,6 +542,11 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
 #pragma unroll
     for (int t = 0; t < kRTiles; ++t) asm volatile("" : "+v"(acc[t]));
     __builtin_amdgcn_sched_barrier(0);
+    // The tiles at a raised wave priority: of the two waves of a SIMD, the
+    // one feeding the matrix core issues first, and the other's vector work
+    // (listing, stores, norms) fills the gaps (measured 1 % faster at 128
+    // bits, 2-4 % at 256).
+    __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
         uint32_t cur[kRTiles], held[kRTiles], pair[kRTiles][NPAIR];
@@ -625,6 +630,7 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
         }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // ---- list the in-band bits: band flag 0, columns of zeros excepted
     // (their bit is 0), rows past the group's count skipped.  Flag bit
     // 4 (PT - 1 - k) + i of pass p is column 16 (p PT + k) + 4 g + i.  Each
