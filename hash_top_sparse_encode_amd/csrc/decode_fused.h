@@ -159,9 +159,22 @@ enum Phase {
         if ((a).trace && threadIdx.x == 0 && (int)blockIdx.x < (a).trace_items)                 \
             (a).trace[(int64_t)blockIdx.x * 16 + (k)] = __builtin_amdgcn_s_memrealtime();        \
     } while (0)
+// A diagnostic word of the workgroup's item in a trace slot of its own: 12
+// the earlier spans' counts (bit 0 window hit, bit 1 read again, T from bit
+// 8, tc from bit 20, the candidate count from bit 32), 13 the selected count
+// (bit 30: taken from all scores), 14 the polls until the unit histogram was
+// complete.
+#define HATA_TRACE_WORD(a, k, v)                                                                \
+    do {                                                                                        \
+        if ((a).trace && threadIdx.x == 0 && (int)blockIdx.x < (a).trace_items)                 \
+            (a).trace[(int64_t)blockIdx.x * 16 + (k)] = (uint64_t)(v);                          \
+    } while (0)
 #else
 #define HATA_PHASE(a, k) \
     do {                 \
+    } while (0)
+#define HATA_TRACE_WORD(a, k, v) \
+    do {                         \
     } while (0)
 #endif
 
@@ -299,7 +312,7 @@ struct SmemSel {
     int scan[8];
     int weq[4], wlt[4];  // per-wave counts of score-T and below-T keys in a batch
     int red[8];
-    int T, below, last;
+    int T, below, cntT, last;
 };
 
 template <int G>
@@ -1402,6 +1415,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
         int tot;
         int run = block_excl_scan_256(tsum, sm.sel.scan, &tot);
         if ((int64_t)tot >= len) {
+            HATA_TRACE_WORD(a, 14, spins);
             // T: first bin whose cumulative count reaches k_eff; below: the
             // count under T
 #pragma unroll
@@ -1410,6 +1424,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
                 if ((int64_t)run < k_eff && (int64_t)nxt >= k_eff) {
                     sm.sel.T = t * PER + e;
                     sm.sel.below = run;
+                    sm.sel.cntT = (int)loc[e];
                 }
                 run = nxt;
             }
@@ -1433,8 +1448,16 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     // window when it holds bins T - 1 and T, else read (again) until every
     // entry carries this launch's tag
     long long tie = 0, lo = 0;
-    const bool in_win = T <= tc && (T == 0 ? wlo <= 0 : T - 1 >= wlo);
+    // The unit's last span: the items before it are all the others, so its
+    // counts come from the unit histogram less its own (still in LDS: the
+    // selection has not written that part of the shared memory yet).
+    const bool last_span = s == n_splits_u - 1;
+    const bool in_win = !last_span && T <= tc && (T == 0 ? wlo <= 0 : T - 1 >= wlo);
     int bad = 0;
+    if (last_span && t == 0) {
+        tie = (long long)sm.sel.cntT - (long long)sm.scan.hist[0][T];
+        lo = (long long)sm.sel.below - (T > 0 ? (long long)sm.scan.hist[1][T - 1] : 0ll);
+    }
     if (in_win) {
 #pragma unroll
         for (int k = 0; k < WPT; ++k) {
@@ -1450,7 +1473,10 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
             }
         }
     }
-    if (!in_win || __syncthreads_or(bad)) {
+    const bool reread = !last_span && (!in_win || __syncthreads_or(bad));
+    HATA_TRACE_WORD(a, 12, (uint64_t)in_win | ((uint64_t)reread << 1) | ((uint64_t)T << 8) |
+                               ((uint64_t)tc << 20) | ((uint64_t)(n_cand < 0 ? 0xFFFF : n_cand) << 32));
+    if (reread) {
         for (int spins = 0;; ++spins) {
             tie = lo = 0;
             bad = 0;
@@ -1537,6 +1563,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
             }
         }
         HATA_PHASE(a, kPhSelected);
+        HATA_TRACE_WORD(a, 13, n_sel);
         const int app_off = (app_row >= s0 && app_row < s1) ? (int)(app_row - s0) : -1;
         attend_mfma<G>(Ku + s0 * kHeadDim, Vu + s0 * kHeadDim, kapp, vapp, app_off, sm.sel.list,
                        n_sel, qa, sm.sel.vst[wv], sm.sel.pb[wv], m, l, o);
@@ -1563,6 +1590,7 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
             ties_acc += batch_eq;
             // the batch's selections through the attention
             if (rb == s0) HATA_PHASE(a, kPhSelected);
+            if (rb == s0) HATA_TRACE_WORD(a, 13, (1u << 30) | batch_sel);
             const int app_off = (app_row >= rb && app_row < rb + kListCap) ? (int)(app_row - rb) : -1;
             attend_mfma<G>(Ku + rb * kHeadDim, Vu + rb * kHeadDim, kapp, vapp, app_off, sm.sel.list,
                            batch_sel, qa, sm.sel.vst[wv], sm.sel.pb[wv], m, l, o);
