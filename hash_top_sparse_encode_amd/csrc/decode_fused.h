@@ -315,6 +315,17 @@ struct SmemSel {
     int T, below, cntT, last;
 };
 
+// Whether an item's own summed and cumulative histograms (scan.hist[0] and
+// [1]) are still intact when its earlier spans' counts are needed: the
+// selection phase writes its list (and the attention its staging rows) over
+// the rest of the scan state first.
+template <int G, int R>
+constexpr bool own_hist_kept() {
+    using Scan = SmemScan<G, R>;
+    using Sel = SmemSel<G>;
+    return __builtin_offsetof(Scan, hist) + 2 * sizeof(uint32_t) * (G * R + 1) <= __builtin_offsetof(Sel, list);
+}
+
 template <int G>
 struct SmemPro {
     float x[G + 1][kHeadDim];                   // query heads, then the appended key or zeros
@@ -1449,9 +1460,9 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
     // entry carries this launch's tag
     long long tie = 0, lo = 0;
     // The unit's last span: the items before it are all the others, so its
-    // counts come from the unit histogram less its own (still in LDS: the
-    // selection has not written that part of the shared memory yet).
-    const bool last_span = s == n_splits_u - 1;
+    // counts come from the unit histogram less its own (still in LDS where
+    // own_hist_kept holds: every code length but 256 bits at G = 8).
+    const bool last_span = own_hist_kept<G, R>() && s == n_splits_u - 1;
     const bool in_win = !last_span && T <= tc && (T == 0 ? wlo <= 0 : T - 1 >= wlo);
     int bad = 0;
     if (last_span && t == 0) {

@@ -168,3 +168,36 @@ def test_full_cache_other_length(gpu):
     torch.cuda.synchronize()
     assert wl.cache.status() & hata.HATA_DEV_APPEND_OVERFLOW
     assert wl.cache.seq_len.cpu().tolist() == [3000, 500]
+
+
+def test_cut_at_the_top_bin_r256_g8(gpu):
+    # All eight query heads of the group equal, and one key of the unit's
+    # last span set to their negation: its code differs from theirs in every
+    # bit, so its summed score is 8 x 256 = 2048, the top bin.  With the
+    # token budget equal to the context the cut T is that bin, and the last
+    # span's counts below it are those of bin 2047 of its histograms (the
+    # bins nearest the end of the scan state in shared memory).
+    spec = synth.custom("g8 top bin", 1, 8, 1, [9000], [9000], [0], seed=77)
+    wl = GpuWorkload(spec, gpu, extra_ctx=2, n_bits=256, encode_prefill=False)
+    q = wl.q_host.copy()
+    q[0, :] = q[0, 0]
+    wl.q_host = q
+    wl.q = bf16_dev(q, gpu)
+    pos = 8192 + 100
+    anti = (q[0, 0] ^ 0x8000).astype(np.uint16)
+    wl.cache.k[0, 0, pos] = bf16_dev(anti[None], gpu)[0]
+    wl.encode_prefill()
+    _say("[bits] r=256 g8 top bin: step")
+    out, sel, sc = wl.step(debug=True)
+    torch.cuda.synchronize()
+    assert wl.cache.status() == 0
+    K, V = synth.unit_context(spec, 0, 0, wl.q_host, wl.new_host)
+    K[pos] = anti
+    ref = oracle.decode_unit(q[0], wl.w_host[0], K, V, 9000, threads=16)
+    assert ref["scores"][pos] == 8 * 256 and ref["scores"].max() == 8 * 256
+    codes = wl.cache.codes[0, 0, :9000].cpu().numpy().view(np.uint32)
+    assert np.array_equal(codes, ref["kcodes"])
+    assert np.array_equal(sc[0, 0, :9000].cpu().numpy().view(np.uint16).astype(np.int32), ref["scores"])
+    assert np.array_equal(sel[0, 0].cpu().numpy()[:9000], ref["idx"])
+    err = np.abs(out[0].float().cpu().numpy().astype(np.float64) - ref["out"]).max()
+    assert err <= OUT_TOL
