@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--phases-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--phases-raw", default=None, help="with --phases: also save the raw "
                     "timestamps (steps x workgroups x 16, uint64) to this .npy file")
+    ap.add_argument("--phases-bits", type=int, default=128, choices=[32, 64, 128, 256],
+                    help="with --phases: the code length of the traced workload")
     return ap.parse_args()
 
 
@@ -420,12 +422,12 @@ def phases_child(args):
     B, Hkv = spec.B, spec.Hkv
     L = max(1, args.layers)
     n = args.steps
-    base = GpuWorkload(spec, dev, extra_ctx=(args.warmup + n) // L + 2)
+    base = GpuWorkload(spec, dev, extra_ctx=(args.warmup + n) // L + 2, n_bits=args.phases_bits)
     caches = [(base.cache, base.ws)]
     for i in range(1, L):
         c = hata.HataCache(B, spec.Hq, Hkv, base.max_ctx, device=dev, k=base.cache.k.clone(),
                            v=base.cache.v.clone(), codes=base.cache.codes.clone(),
-                           seq_len=base.n_pre.clone())
+                           seq_len=base.n_pre.clone(), n_bits=args.phases_bits)
         caches.append((c, hata.alloc_workspace(c, base.k_max)))
     base.cache.seq_len.copy_(base.n_pre)
     k_new, v_new = base.k_new.view(B, Hkv, 128), base.v_new.view(B, Hkv, 128)
@@ -472,7 +474,7 @@ def phases_child(args):
     rows = [("first workgroup starts", "0.00", "0.00", int(len(kind))),
             ("PRO: query and new-key codes published", m(prod), m(pros), int(pro.sum()))]
     rows += [(f"WORK: {name}", m(med[k]), m(last[k]), int(np.median(cnt[k]))) for k, name in PHASES]
-    print(f"Decode-step phases, {spec.name} (r = 128, {L} layer caches, {n} steps traced "
+    print(f"Decode-step phases, {spec.name} (r = {args.phases_bits}, {L} layer caches, {n} steps traced "
           f"after {args.warmup}); microseconds from the launch's first workgroup start, "
           "median over the steps.\n")
     print("| phase | median work item | last work item | items with the mark |")
@@ -491,7 +493,8 @@ def phases_parent(args):
     env = dict(os.environ, HATA_LIB_PATH=_build.TRACE_LIB_PATH)
     cmd = [sys.executable, os.path.abspath(__file__), "--phases-child", "--config",
            str(args.config), "--steps", str(args.steps), "--warmup", str(args.warmup),
-           "--layers", str(args.layers)] + (["--phases-raw", args.phases_raw] if args.phases_raw else [])
+           "--layers", str(args.layers), "--phases-bits", str(args.phases_bits)] + \
+        (["--phases-raw", args.phases_raw] if args.phases_raw else [])
     sys.exit(subprocess.run(cmd, env=env).returncode)
 
 

@@ -42,7 +42,7 @@ bool make_decode_plan(int B, int Hq, int Hkv, int64_t max_ctx, int n_bits, Decod
     const int64_t per = (ctx + (int64_t)kMaxSplits * kSpanUnit - 1) / ((int64_t)kMaxSplits * kSpanUnit);
     d.span = per * kSpanUnit;
     const int64_t C = (ctx + d.span - 1) / d.span;
-    const int64_t items = units * (n_bits / 32 + C);
+    const int64_t items = units * (pro_parts(n_bits) + C);
     if (items > INT32_MAX / 2) return false;
     d.n_chunks = (int)C;
     d.n_items = (int)items;

@@ -327,10 +327,17 @@ constexpr bool own_hist_kept() {
     return __builtin_offsetof(Scan, hist) + 2 * sizeof(uint32_t) * (G * R + 1) <= __builtin_offsetof(Sel, list);
 }
 
-template <int G>
+// PRO parts per unit: one per 32 code bits up to 128 bits; at 256 bits four
+// parts of 64 bits each, so that the step's grid (with 17 spans a unit at
+// 128K context) still fits on the chip at once.
+__host__ __device__ constexpr int pro_parts(int r) { return r >= 256 ? 4 : r / 32; }
+template <int R>
+constexpr int pro_groups() { return R / 32 / pro_parts(R); }  // 32-column groups per part
+
+template <int G, int R>
 struct SmemPro {
     float x[G + 1][kHeadDim];                   // query heads, then the appended key or zeros
-    float w[kHeadDim][32];                      // this part's 32 columns of W_H
+    float w[pro_groups<R>()][kHeadDim][32];     // this part's columns of W_H, 32 per group
     float py[4][G + 1][32];                     // per-wave partial sums
     float pa[4][G + 1][32];                     // per-wave partial sums of |products|
 };
@@ -339,14 +346,15 @@ template <int G, int R>
 union Smem {
     SmemScan<G, R> scan;
     SmemSel<G> sel;
-    SmemPro<G> pro;
+    SmemPro<G, R> pro;
 };
 
 // ---------------------------------------------------------------- PRO(u)
 
-// Part p of unit u computes code bits [32 p, 32 p + 32) of the G query heads
-// and of the appended key; part 0 also copies the appended K/V rows and
-// writes the outputs of an empty selection.
+// Part p of unit u computes code bits [32 NG p, 32 NG (p + 1)) of the G
+// query heads and of the appended key (NG = pro_groups: one group of 32, two
+// at 256 bits, one after the other); part 0 also copies the appended K/V
+// rows and writes the outputs of an empty selection.
 //
 // Each bit is sign(y) with y = sum_t x[t] W[t][j] evaluated as a sequential
 // double sum in ascending t (bf16 x fp32 products are exact in double).
@@ -363,22 +371,25 @@ union Smem {
 template <int G, int R>
 __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Smem<G, R> &sm) {
     constexpr int COLS = 32;
+    constexpr int NG = pro_groups<R>();
     constexpr int W = R / 32;
     constexpr int NV = G + 1;                // query heads + appended key
     const int b = u / a.Hkv, kv = u % a.Hkv, Hq = a.Hkv * G;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     // Every load the part needs is issued before any is used, so they share
-    // one round trip: its 128 x 32 slice of W_H (16 bytes per load), the x
+    // one round trip: its 128 x 32 NG slice of W_H (16 bytes per load), the x
     // rows (query heads, then the token's key: one 16-byte load per thread,
     // 16 threads per row), the unit's generation and the entry's length, and
     // for part 0 the top-k and the token's K/V words to append.
-    fvec4 wq[kHeadDim * COLS / 4 / kThreads];  // 4
-    {
-        const float *wk = a.w + (int64_t)kv * kHeadDim * R + part * COLS;
+    constexpr int WQ = kHeadDim * COLS / 4 / kThreads;  // 4 per group
+    fvec4 wq[NG][WQ];
 #pragma unroll
-        for (int r = 0; r < kHeadDim * COLS / 4 / kThreads; ++r) {
+    for (int g = 0; g < NG; ++g) {
+        const float *wk = a.w + (int64_t)kv * kHeadDim * R + (part * NG + g) * COLS;
+#pragma unroll
+        for (int r = 0; r < WQ; ++r) {
             const int f = r * kThreads + t;  // row f / 8, four columns at 4 (f % 8)
-            wq[r] = *reinterpret_cast<const fvec4 *>(wk + (f >> 3) * R + 4 * (f & 7));
+            wq[g][r] = *reinterpret_cast<const fvec4 *>(wk + (f >> 3) * R + 4 * (f & 7));
         }
     }
     // (Loads are issued by every lane, those with nothing to load reading the
@@ -408,9 +419,12 @@ __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Sm
             sm.pro.x[xv][d0 + 2 * e + 1] = __uint_as_float(wds[e] & 0xFFFF0000u);
         }
     }
-    fvec4 *wl = reinterpret_cast<fvec4 *>(&sm.pro.w[0][0]);
 #pragma unroll
-    for (int r = 0; r < kHeadDim * COLS / 4 / kThreads; ++r) wl[r * kThreads + t] = wq[r];
+    for (int g = 0; g < NG; ++g) {
+        fvec4 *wl = reinterpret_cast<fvec4 *>(&sm.pro.w[g][0][0]);
+#pragma unroll
+        for (int r = 0; r < WQ; ++r) wl[r * kThreads + t] = wq[g][r];
+    }
     // Part 0's stores: nothing in this launch waits for them (the unit's
     // attention reads the token's K/V from k_new / v_new, and its code word
     // from the published words), so they are issued and left in flight.
@@ -437,64 +451,69 @@ __device__ __forceinline__ void item_pro(const FusedArgs &a, int u, int part, Sm
                 a.out[((int64_t)b * Hq + kv * G) * kHeadDim + i] = 0;
         }
     }
-    __syncthreads();
-    // Segment sums: lane col = lane & 31 of wave w covers rows
-    // [16 seg, 16 seg + 16) with seg = 2 w + (lane >> 5).
-    {
-        const int col = lane & 31, seg = 2 * wv + (lane >> 5);
-        float ys[NV], as[NV];
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            ys[v] = 0.f;
-            as[v] = 0.f;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = 16 * seg + r;
-            const float wf = sm.pro.w[row][col];
+#pragma unroll 1
+    for (int g = 0; g < NG; ++g) {
+        // the staged rows (and, after the first group, every read of the
+        // previous group's partials)
+        __syncthreads();
+        // Segment sums: lane col = lane & 31 of wave w covers rows
+        // [16 seg, 16 seg + 16) with seg = 2 w + (lane >> 5).
+        {
+            const int col = lane & 31, seg = 2 * wv + (lane >> 5);
+            float ys[NV], as[NV];
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                const float xf = sm.pro.x[v][row];
-                ys[v] = fmaf(xf, wf, ys[v]);
-                as[v] = fmaf(fabsf(xf), fabsf(wf), as[v]);
+                ys[v] = 0.f;
+                as[v] = 0.f;
             }
-        }
-        // pair the wave's two segments, then park the wave's partials
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const float yo = __shfl_xor(ys[v], 32, 64), ao = __shfl_xor(as[v], 32, 64);
-            if (lane < 32) {
-                sm.pro.py[wv][v][col] = ys[v] + yo;  // lower segment first
-                sm.pro.pa[wv][v][col] = as[v] + ao;
-            }
-        }
-    }
-    __syncthreads();
-    // Decide bit (v, col) for v = t >> 5 (and v = 8 + (t >> 5) on a second
-    // pass for G = 8): tree over the four waves, then the sign test.
+            for (int r = 0; r < 16; ++r) {
+                const int row = 16 * seg + r;
+                const float wf = sm.pro.w[g][row][col];
 #pragma unroll
-    for (int pass = 0; pass < (NV + 7) / 8; ++pass) {
-        const int v = pass * 8 + (t >> 5), col = t & 31;
-        bool bit = false;
-        if (v < NV) {
-            const float y = (sm.pro.py[0][v][col] + sm.pro.py[1][v][col]) +
-                            (sm.pro.py[2][v][col] + sm.pro.py[3][v][col]);
-            const float A = (sm.pro.pa[0][v][col] + sm.pro.pa[1][v][col]) +
-                            (sm.pro.pa[2][v][col] + sm.pro.pa[3][v][col]);
-            if (fabsf(y) > fmaf(0x1p-16f, A, 0x1p-100f)) {
-                bit = y > 0.f;
-            } else {
-                double ysq = 0.0;  // the defining sequential sum
-                for (int row = 0; row < kHeadDim; ++row)
-                    ysq = fma((double)sm.pro.x[v][row], (double)sm.pro.w[row][col], ysq);
-                bit = ysq > 0.0;
+                for (int v = 0; v < NV; ++v) {
+                    const float xf = sm.pro.x[v][row];
+                    ys[v] = fmaf(xf, wf, ys[v]);
+                    as[v] = fmaf(fabsf(xf), fabsf(wf), as[v]);
+                }
+            }
+            // pair the wave's two segments, then park the wave's partials
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const float yo = __shfl_xor(ys[v], 32, 64), ao = __shfl_xor(as[v], 32, 64);
+                if (lane < 32) {
+                    sm.pro.py[wv][v][col] = ys[v] + yo;  // lower segment first
+                    sm.pro.pa[wv][v][col] = as[v] + ao;
+                }
             }
         }
-        const uint64_t mb = __ballot(bit);
-        if ((t & 31) == 0 && v < NV && sl.len > 0) {
-            const uint32_t word = v < nvec ? (uint32_t)(((t >> 5) & 1) ? (mb >> 32) : mb) : 0u;
-            st_dev(a.qtag + ((int64_t)u * NV + v) * W + part, ((uint64_t)tag << 32) | word);
-            if (v == G && sl.app) st_dev(a.codes + ((int64_t)u * a.max_ctx + sl.l0) * W + part, word);
+        __syncthreads();
+        // Decide bit (v, col) for v = t >> 5 (and v = 8 + (t >> 5) on a second
+        // pass for G = 8): tree over the four waves, then the sign test.
+#pragma unroll
+        for (int pass = 0; pass < (NV + 7) / 8; ++pass) {
+            const int v = pass * 8 + (t >> 5), col = t & 31;
+            bool bit = false;
+            if (v < NV) {
+                const float y = (sm.pro.py[0][v][col] + sm.pro.py[1][v][col]) +
+                                (sm.pro.py[2][v][col] + sm.pro.py[3][v][col]);
+                const float A = (sm.pro.pa[0][v][col] + sm.pro.pa[1][v][col]) +
+                                (sm.pro.pa[2][v][col] + sm.pro.pa[3][v][col]);
+                if (fabsf(y) > fmaf(0x1p-16f, A, 0x1p-100f)) {
+                    bit = y > 0.f;
+                } else {
+                    double ysq = 0.0;  // the defining sequential sum
+                    for (int row = 0; row < kHeadDim; ++row)
+                        ysq = fma((double)sm.pro.x[v][row], (double)sm.pro.w[g][row][col], ysq);
+                    bit = ysq > 0.0;
+                }
+            }
+            const uint64_t mb = __ballot(bit);
+            if ((t & 31) == 0 && v < NV && sl.len > 0) {
+                const uint32_t word = v < nvec ? (uint32_t)(((t >> 5) & 1) ? (mb >> 32) : mb) : 0u;
+                st_dev(a.qtag + ((int64_t)u * NV + v) * W + part * NG + g, ((uint64_t)tag << 32) | word);
+                if (v == G && sl.app) st_dev(a.codes + ((int64_t)u * a.max_ctx + sl.l0) * W + part * NG + g, word);
+            }
         }
     }
     HATA_PHASE(a, kPhCodes);
@@ -1767,7 +1786,7 @@ struct Item {
 // PRO(u, p) then WORK(u, c).
 template <int R>
 __device__ __forceinline__ Item item_in(const FusedArgs &a, int U, int tk) {
-    constexpr int P = R / 32;  // PRO parts per unit
+    constexpr int P = pro_parts(R);  // PRO parts per unit
     Item it;
     if (!a.resident) {
         // unit by unit, each unit's PRO parts just before its WORK items, so
