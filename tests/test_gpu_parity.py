@@ -190,7 +190,8 @@ def _bf16_bits_of(x: np.ndarray) -> np.ndarray:
     return (u >> 16).astype(np.uint16)
 
 
-def test_query_codes_in_band(gpu):
+@pytest.mark.parametrize("n_bits", [128, 256, 32])
+def test_query_codes_in_band(gpu, n_bits):
     # Code bits whose sum x . W_j is zero or tiny next to A = sum_t |x_t W_tj|
     # cannot be decided by the kernel's fp32 sum and go to the defining
     # sequential double sum.  W's rows 2i and 2i + 1 agree in every even
@@ -200,7 +201,9 @@ def test_query_codes_in_band(gpu):
     # batch entry's new keys, carry one imbalance, x_1 = -(1 - 2^-8) against
     # x_0 = 1, which leaves a sum of 2^-8 W_1j against an A near 2^10 |W|.
     spec = synth.custom("in band", 2, 8, 2, [5000, 1200], [64, 16], [5, 2], seed=13)
-    wl = GpuWorkload(spec, gpu, extra_ctx=2, encode_prefill=False)
+    # (at 256 bits each query-code part decides two groups of 32 columns,
+    # the second after the first)
+    wl = GpuWorkload(spec, gpu, extra_ctx=2, encode_prefill=False, n_bits=n_bits)
     q_keys = wl.q_host.copy()  # the keys of the context were planted from these
     w = wl.w_host.copy()
     w[:, 1::2, 0::2] = w[:, 0::2, 0::2]
