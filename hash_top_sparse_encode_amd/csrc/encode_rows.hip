@@ -125,6 +125,8 @@ struct RowsSmem {
     uint16_t lrc[kRWaves][kRList];   // ... and row << 8 | column
     int64_t seg_l0[kRSegLds];      // mode 1: each entry's length ...
     int32_t seg_rows[kRSegLds];    // ... and the rows it appends
+    int32_t seg_pre[kRSegLds + 1]; // ... and its first group among the head's non-empty ones
+    int32_t wsum[kRWaves];
     int last;
 };
 
@@ -739,6 +741,107 @@ __device__ __forceinline__ void encode_group(const RowsArgs &a, RowsSmem<R> &sm,
     }
 }
 
+// The entry and group of non-empty group gq of a head (prefix sums in
+// seg_pre; entries from s_from on): n_seg past the last one.
+template <int R>
+__device__ __forceinline__ int2 dense_at(const RowsSmem<R> &sm, int n_seg, int s_from, int64_t gq,
+                                         int64_t n_dense) {
+    if (gq >= n_dense) return int2{n_seg, 0};
+    const int q = (int)gq;
+    int s0 = s_from;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (q >= sm.seg_pre[s0 + 1]) ++s0;
+    if (q >= sm.seg_pre[s0 + 1]) {  // binary search over (s0, n_seg)
+        int lo = s0 + 1, hi = n_seg - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sm.seg_pre[mid] <= q) lo = mid;
+            else hi = mid - 1;
+        }
+        s0 = lo;
+    }
+    s0 = __builtin_amdgcn_readfirstlane(s0);
+    return int2{s0, q - sm.seg_pre[s0]};
+}
+
+// ---- the wave's groups, two register buffers: the next group loads
+// while this one is computed.  Group gi of the head is group gi mod G of
+// batch entry gi / G (G groups per entry); the wave takes every stride-th,
+// from blockIdx.x * waves + wave, and steps the (entry, group) pair by
+// (stride / G, stride mod G) with a carry (no division per step).  With the
+// prefix sums (dense), group gi of the head is the non-empty group
+// gi - seg_pre[s] of the entry s with seg_pre[s] <= gi < seg_pre[s + 1],
+// found by stepping s forward (a binary search when the stride spans more
+// than a few entries).  Returns the wave's in-band bits not yet resolved.
+template <int R>
+__device__ __forceinline__ int wave_groups(const RowsArgs &a, RowsSmem<R> &sm, const float *W, int h,
+                                           int wv, int g, int c, bool dense) {
+    const int64_t gps = a.groups_per_seg;
+    const int64_t stride = (int64_t)gridDim.x * kRWaves;
+    const int64_t step_s = stride / gps, step_g = stride - step_s * gps;
+    const RGroup none = no_group(a, h);
+    int64_t gi = (int64_t)blockIdx.x * kRWaves + wv;
+    int64_t cs = gi / gps, cg = gi - cs * gps;   // entry and group of gi
+    const int64_t n_dense = dense ? (int64_t)sm.seg_pre[a.n_seg] : 0;
+    if (dense) {
+        const int2 l = dense_at<R>(sm, a.n_seg, 0, gi, n_dense);
+        cs = l.x;
+        cg = l.y;
+    }
+    uvec4 xa0[kRTiles][4], xa1[kRTiles][4];
+    int n_list = 0;  // in-band bits listed by this wave, not yet resolved (uniform)
+    // The loads are issued whether or not the group has rows (one past the
+    // work, or skipped, reads row 0 of the head: a valid address), so that
+    // the count of loads in flight is the same on every path and a group's
+    // use waits only for its own loads.  A group is listed for the exact
+    // sums under its index among all of the head's group slots, entry *
+    // groups_per_seg + group, which flush_list decodes.
+    RGroup e0 = cs < a.n_seg ? group_at<R, true>(a, sm, h, (int)cs, cg) : none;
+    int64_t sp0 = cs * gps + cg;
+    load_group(a, e0.nr > 0 ? e0 : none, g, c, xa0);
+    while (cs < a.n_seg) {
+        const int64_t gi1 = gi + stride;
+        if (dense) {
+            const int2 l = dense_at<R>(sm, a.n_seg, (int)cs, gi1, n_dense);
+            cs = l.x;
+            cg = l.y;
+        } else {
+            cg += step_g;
+            cs += step_s;
+            if (cg >= gps) {
+                cg -= gps;
+                ++cs;
+            }
+        }
+        const RGroup e1 = cs < a.n_seg ? group_at<R, true>(a, sm, h, (int)cs, cg) : none;
+        const int64_t sp1 = cs * gps + cg;
+        load_group(a, e1.nr > 0 ? e1 : none, g, c, xa1);
+        if (e0.nr > 0) encode_group<R>(a, sm, W, h, sp0, e0, xa0, wv, n_list);
+        if (n_list >= 64) n_list = flush_rounds<R>(a, sm, W, h, n_list, false);
+        const int64_t gi2 = gi1 + stride;
+        if (dense) {
+            const int2 l = dense_at<R>(sm, a.n_seg, (int)cs, gi2, n_dense);
+            cs = l.x;
+            cg = l.y;
+        } else {
+            cg += step_g;
+            cs += step_s;
+            if (cg >= gps) {
+                cg -= gps;
+                ++cs;
+            }
+        }
+        e0 = cs < a.n_seg ? group_at<R, true>(a, sm, h, (int)cs, cg) : none;
+        sp0 = cs * gps + cg;
+        load_group(a, e0.nr > 0 ? e0 : none, g, c, xa0);
+        if (e1.nr > 0) encode_group<R>(a, sm, W, h, sp1, e1, xa1, wv, n_list);
+        if (n_list >= 64) n_list = flush_rounds<R>(a, sm, W, h, n_list, false);
+        gi = gi2;
+    }
+    return n_list;
+}
+
 template <int R>
 __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
     constexpr int NT = R / 16;   // column tiles
@@ -819,12 +922,53 @@ __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
             for (int q = 0; q < 8; ++q) sm.wt[col][d0 + q] = wf[q];
         }
     }
+    // Batches of 16 to kRSegLds entries (lengths in LDS) also get the prefix
+    // sum of their group counts, and when a quarter or more of
+    // the head's group slots are empty (a ragged batch sets the group count
+    // of every entry by its longest append) the waves step over the
+    // non-empty groups only (64 ragged sequences of up to 64K keys: 1.40 ->
+    // 1.31 ms; with few empty slots the search costs more than it saves).
+    const bool scan_groups = a.mode == 1 && a.n_seg >= 16 && a.n_seg <= kRSegLds;
+    int groups0 = 0, groups1 = 0;  // group counts of this thread's entries t and t + 512
     if (a.mode == 1) {
         for (int s = t; s < a.n_seg && s < kRSegLds; s += kRThreads) {
             const int64_t l0 = a.seq_len[s];
             const int n = a.n_new[s];
+            const int rows = rows_append_ok(l0, n, a.t_max, a.max_ctx) ? n : 0;
             sm.seg_l0[s] = l0;
-            sm.seg_rows[s] = rows_append_ok(l0, n, a.t_max, a.max_ctx) ? n : 0;
+            sm.seg_rows[s] = rows;
+            if (s < kRThreads) groups0 = (rows + kRGroup - 1) / kRGroup;
+            else groups1 = (rows + kRGroup - 1) / kRGroup;
+        }
+    }
+    if (scan_groups) {
+        // exclusive prefix sum over entries 0 .. n_seg - 1: entry s is
+        // thread s % 512's, pass s / 512
+        int base = 0;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int v = pass == 0 ? groups0 : groups1;
+            int incl = v;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int u = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += u;
+            }
+            if (lane == 63) sm.wsum[wv] = incl;
+            __syncthreads();
+            int before = base, total = base;
+#pragma unroll
+            for (int w2 = 0; w2 < kRWaves; ++w2) {
+                const int ws = sm.wsum[w2];
+                before += w2 < wv ? ws : 0;
+                total += ws;
+            }
+            const int s = pass * kRThreads + t;
+            if (s < a.n_seg) sm.seg_pre[s] = before + incl - v;
+            if (s == a.n_seg - 1) sm.seg_pre[a.n_seg] = before + incl;
+            if (t == 0 && a.n_seg == 0) sm.seg_pre[0] = 0;
+            base = total;
+            __syncthreads();
         }
     }
     __syncthreads();
@@ -847,50 +991,8 @@ __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
     }
     __syncthreads();
 
-    // ---- the wave's groups, two register buffers: the next group loads
-    // while this one is computed.  Group gi of the head is group gi mod G of
-    // batch entry gi / G (G groups per entry); the wave takes every
-    // stride-th, from blockIdx.x * waves + wave, and steps the (entry, group)
-    // pair by (stride / G, stride mod G) with a carry (no division per step).
-    const int64_t gps = a.groups_per_seg;
-    const int64_t stride = (int64_t)gridDim.x * kRWaves;
-    const int64_t step_s = stride / gps, step_g = stride - step_s * gps;
-    const RGroup none = no_group(a, h);
-    int64_t gi = (int64_t)blockIdx.x * kRWaves + wv;
-    int64_t cs = gi / gps, cg = gi - cs * gps;   // entry and group of gi
-    uvec4 xa0[kRTiles][4], xa1[kRTiles][4];
-    int n_list = 0;  // in-band bits listed by this wave, not yet resolved (uniform)
-    // The loads are issued whether or not the group has rows (one past the
-    // work, or skipped, reads row 0 of the head: a valid address), so that
-    // the count of loads in flight is the same on every path and a group's
-    // use waits only for its own loads.
-    RGroup e0 = cs < a.n_seg ? group_at<R, true>(a, sm, h, (int)cs, cg) : none;
-    load_group(a, e0.nr > 0 ? e0 : none, g, c, xa0);
-    while (cs < a.n_seg) {
-        cg += step_g;
-        cs += step_s;
-        if (cg >= gps) {
-            cg -= gps;
-            ++cs;
-        }
-        const int64_t gi1 = gi + stride;
-        const RGroup e1 = cs < a.n_seg ? group_at<R, true>(a, sm, h, (int)cs, cg) : none;
-        load_group(a, e1.nr > 0 ? e1 : none, g, c, xa1);
-        if (e0.nr > 0) encode_group<R>(a, sm, W, h, gi, e0, xa0, wv, n_list);
-        if (n_list >= 64) n_list = flush_rounds<R>(a, sm, W, h, n_list, false);
-        cg += step_g;
-        cs += step_s;
-        if (cg >= gps) {
-            cg -= gps;
-            ++cs;
-        }
-        const int64_t gi2 = gi1 + stride;
-        e0 = cs < a.n_seg ? group_at<R, true>(a, sm, h, (int)cs, cg) : none;
-        load_group(a, e0.nr > 0 ? e0 : none, g, c, xa0);
-        if (e1.nr > 0) encode_group<R>(a, sm, W, h, gi1, e1, xa1, wv, n_list);
-        if (n_list >= 64) n_list = flush_rounds<R>(a, sm, W, h, n_list, false);
-        gi = gi2;
-    }
+    const bool dense = scan_groups && 4 * (int64_t)sm.seg_pre[a.n_seg] <= 3 * a.n_seg * a.groups_per_seg;
+    const int n_list = wave_groups<R>(a, sm, W, h, wv, g, c, dense);
     if (n_list > 0) flush_rounds<R>(a, sm, W, h, n_list, true);
 
     if (a.mode == 1) {
