@@ -926,8 +926,8 @@ __global__ __launch_bounds__(kRThreads, 1) void k_encode_rows(RowsArgs a) {
     // sum of their group counts, and when a quarter or more of
     // the head's group slots are empty (a ragged batch sets the group count
     // of every entry by its longest append) the waves step over the
-    // non-empty groups only (64 ragged sequences of up to 64K keys: 1.40 ->
-    // 1.31 ms; with few empty slots the search costs more than it saves).
+    // non-empty groups only (64 ragged sequences of up to 64K keys: 1.41 ->
+    // 1.32 ms; with few empty slots the search costs more than it saves).
     const bool scan_groups = a.mode == 1 && a.n_seg >= 16 && a.n_seg <= kRSegLds;
     int groups0 = 0, groups1 = 0;  // group counts of this thread's entries t and t + 512
     if (a.mode == 1) {
