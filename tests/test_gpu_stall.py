@@ -18,8 +18,17 @@ from workload import GpuWorkload
 pytestmark = pytest.mark.gpu
 
 
-def test_forced_stall_sets_status_and_recovers(gpu, monkeypatch):
-    spec = synth.custom("stall", 2, 8, 2, [20000, 9000], [300, 140], [20, 9], seed=13)
+STALL_SPECS = [
+    synth.custom("stall", 2, 8, 2, [20000, 9000], [300, 140], [20, 9], seed=13),
+    # 256 units of two or three items each: more workgroups than the chip
+    # holds at once, so the grid runs in the unit-by-unit order
+    synth.custom("stall, grid larger than the chip", 32, 32, 8, [9000 if b % 2 else 13000 for b in range(32)],
+                 [140 if b % 2 else 200 for b in range(32)], [9 if b % 2 else 13 for b in range(32)], seed=17),
+]
+
+
+@pytest.mark.parametrize("spec", STALL_SPECS, ids=[s.name for s in STALL_SPECS])
+def test_forced_stall_sets_status_and_recovers(gpu, monkeypatch, spec):
     clean = GpuWorkload(spec, gpu, extra_ctx=2)
     out_c, sel_c, sc_c = clean.step(debug=True)
     torch.cuda.synchronize()
