@@ -866,7 +866,10 @@ __device__ __forceinline__ int slot_publish(const FusedArgs &a, const Slot &s, u
     }
     const int tc = sm.scan.tc;
     __syncthreads();
-    if (t >= 3 * 64) {
+    // a unit of one span: its histogram is the unit's, read from LDS by the
+    // selection (nothing to publish)
+    const bool single = s.sl.len <= a.span;
+    if (t >= 3 * 64 && !single) {
         uint64_t *ch = a.chunk_hist + ((int64_t)s.u * a.n_chunks + s.c) * NB;
         const uint64_t tag = (uint64_t)gen << 32;
 #pragma unroll
@@ -1428,7 +1431,18 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
         const int i = t + k * kPoll;
         return t < kPoll && i / kWin < s && wlo + i % kWin >= 0;
     };
-    read_state();
+    // A unit of one span takes its own counts (still in LDS) as the unit
+    // histogram, so its first pass below finds them complete.
+    const bool single = n_splits_u == 1;
+    if (single) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int bin = t * PER + e;
+            loc[e] = (t < kPoll && bin < NB) ? sm.scan.hist[0][bin] : 0u;
+        }
+    } else {
+        read_state();
+    }
     // ---- meanwhile the span's candidates: every key up to the candidate
     // cut tc, in index order (spans kept in LDS)
     const int n_cand = in_lds ? uni(list_candidates<G, R>(pf, tc, woff, sm)) : -1;
@@ -1672,11 +1686,26 @@ __device__ __forceinline__ bool sel_phase(const FusedArgs &a, const Slot &cur, i
             O0 = fmaf(ow.x, aw, O0);
             O1 = fmaf(ow.y, aw, O1);
         }
+        if (single) {
+            // the unit's only split: its state is the output (as the merge
+            // below would compute it, with weight exp2(0) = 1)
+            uint16_t *op = a.out + ((int64_t)b * Hq + kv * G) * kHeadDim + 2 * pr;
+            op[0] = L > 0.f ? f32_to_bf16(O0 / L) : (uint16_t)0;
+            op[1] = L > 0.f ? f32_to_bf16(O1 / L) : (uint16_t)0;
+            continue;
+        }
         st_dev(po + pr, (uint64_t)__float_as_uint(O0) | ((uint64_t)__float_as_uint(O1) << 32));
         if (e == 0) {
             st_dev(pml + 2 * h, M);
             st_dev(pml + 2 * h + 1, L);
         }
+    }
+    if (single) {
+        // no partial, no count; the unit histogram received nothing, so it
+        // is still clear for the next launch
+        HATA_PHASE(a, kPhPartial);
+        if (t == 0) entry_done(a, b, sl, unit_done(a, u));
+        return true;
     }
 
     // ---- the last split of the unit merges all partials in split order
