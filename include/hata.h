@@ -85,7 +85,7 @@ typedef enum {
  * codes of its (sequence, KV head) unit and, before it selects, for the
  * histogram counts of every other work item of that unit.  This needs those
  * other items to be running: workgroups start in block order and a unit's
- * items (at most 72: up to 8 query-code parts and 64 spans) fit on the GPU
+ * items (at most 68: up to 4 query-code parts and 64 spans) fit on the GPU
  * together.  When the whole launch fits on
  * the GPU with 64 workgroup slots to spare, the items are also reordered for
  * balance, which needs every workgroup of the launch resident at once.  Both
